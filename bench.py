@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Throughput of packed draft-token verification on one MI355X.
+
+One step is one pass of the whole verification path over one batch of
+synthetic input: every verify row streamed once from HBM and reduced or
+sampled, the per-request prefix-accept scan, compaction of emitted tokens by
+device offsets, and (where the workload has draft logits) the draft
+confidence of every draft row. The default workload is the EAGLE-shaped
+greedy batch the headline metric is quoted on (B=128 requests, K=4 drafts,
+V=152064, bf16 logits). Inputs are resident in HBM before timing starts and
+rotate over enough copies (>= 1 GiB) that no step reads from the 256 MB
+Infinity Cache.
+
+Prints one JSON line on stdout. `roofline` rates the dominant kernel's
+algorithmic bytes per launch against the 8 TB/s HBM peak, with the
+per-launch duration from HIP events around each launch in the timed region;
+`cpu_baseline` times the float64 CPU oracle on the same kind of input.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+ROTATE_BYTES = 1 << 30
+KERNEL_SOURCES = ("csrc/device.hpp", "csrc/row_stream.hpp", "csrc/sampled_row.hpp", "csrc/verify.hip",
+                  "csrc/confidence.hip", "csrc/kernels.hpp")
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    pkg = os.path.join(ROOT, "draft_token_verification_packed_amd")
+    for rel in KERNEL_SOURCES:
+        p = os.path.join(pkg, rel)
+        if os.path.exists(p):
+            h.update(rel.encode())
+            h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload_tag):
+    """HBM bytes per launch from committed rocprofv3 PMC runs, if still valid."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        entries = json.load(open(p))
+    except ValueError:
+        return None
+    e = entries.get("%s/%s" % (kernel, workload_tag))
+    if not e or e.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def upload(torch, arr):
+    import numpy as np
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def build_steps(vsv, torch, wl):
+    """One list of prepared calls per rotating copy of the inputs.
+
+    Returns (steps, kernels): steps[c] is the call list for copy c, kernels
+    names each call's kernel and its algorithmic bytes per launch.
+    """
+    es = 2 if wl.dtype == 1 else 4
+    verify_bytes = wl.R * wl.V * es
+    conf_bytes = wl.D * wl.V * es
+    step_bytes = verify_bytes + conf_bytes
+    ncopy = max(1, math.ceil(ROTATE_BYTES / step_bytes))
+    off, own, dr = upload(torch, wl.offsets), upload(torch, wl.owner), upload(torch, wl.drafts)
+    base = upload(torch, wl.logits)
+    dbase = upload(torch, wl.draft_logits) if wl.D else None
+    sel = upload(torch, wl.selected) if wl.D else None
+    if wl.sampled:
+        params = [upload(torch, a) for a in (wl.temperature, wl.top_k, wl.top_p, wl.min_p)]
+    steps = []
+    for c in range(ncopy):
+        logits = base if c == 0 else base.clone()
+        calls = []
+        if wl.sampled:
+            call, _ = vsv.prepare_sampled(logits, off, own, dr, *params, wl.seed, wl.offset)
+        else:
+            call, _ = vsv.prepare_greedy(logits, off, own, dr, relaxed_topk=wl.relaxed_topk)
+        calls.append(call)
+        if wl.D:
+            dl = dbase if c == 0 else dbase.clone()
+            ccall, _ = vsv.prepare_confidence(dl, sel)
+            calls.append(ccall)
+        steps.append(calls)
+    kernels = [("verify_sampled_kernel" if wl.sampled else "verify_greedy_kernel", verify_bytes)]
+    if wl.D:
+        kernels.append(("confidence_kernel", conf_bytes))
+    return steps, kernels, ncopy, step_bytes
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """Oracle (float64 NumPy, one process) on whole requests of the workload."""
+    import numpy as np
+    import oracle
+    t0 = time.perf_counter()
+    rows = 0
+    passes = 0
+    # one pass over the whole batch is seconds; repeat within the budget
+    while True:
+        if wl.sampled:
+            oracle.verify_sampled(wl.logits, wl.dtype, wl.V, wl.offsets, wl.owner, wl.drafts,
+                                  wl.temperature, wl.top_k, wl.top_p, wl.min_p, wl.seed, wl.offset)
+        else:
+            oracle.verify_greedy(wl.logits, wl.dtype, wl.V, wl.offsets, wl.owner, wl.drafts,
+                                 relaxed_topk=wl.relaxed_topk)
+        if wl.D:
+            oracle.draft_confidence(wl.draft_logits, wl.dtype, wl.V, wl.selected)
+        rows += wl.R
+        passes += 1
+        if time.perf_counter() - t0 >= budget_s or passes >= 20:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=rows / dt, unit="rows/s", cores=1, kind="oracle",
+                sample="%d full pass(es) over the %d-row batch (%s), %.1f s, single process"
+                       % (passes, wl.R, "plus its draft rows" if wl.D else "verify rows only", dt))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
+                    help="workload (default: EAGLE greedy B=128 K=4 V=152064)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this library verifies on one GPU; --gpus %d is not supported "
+              "(requests shard across GPUs without collectives, see the design notes)" % max(args.gpus, world),
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import synth
+    import draft_token_verification_packed_amd as vsv
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    vsv.lib()
+    print("[bench] generating workload %d" % args.config, file=sys.stderr, flush=True)
+    wl = synth.make(args.config)
+    steps, kernels, ncopy, step_bytes = build_steps(vsv, torch, wl)
+    torch.cuda.synchronize()
+    print("[bench] %d input copies, %.1f MB per step" % (ncopy, step_bytes / 1e6), file=sys.stderr, flush=True)
+
+    for k in range(args.warmup):
+        for call in steps[k % ncopy]:
+            call.run()
+    torch.cuda.synchronize()
+
+    ncall = len(steps[0])
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ncall + 1)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(args.steps):
+        e = evs[k]
+        for c, call in enumerate(steps[k % ncopy]):
+            e[c].record()
+            call.run()
+        e[ncall].record()
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    per_kernel_ms = [sum(evs[k][c].elapsed_time(evs[k][c + 1]) for k in range(args.steps)) / args.steps
+                     for c in range(ncall)]
+    ms = total_ms / args.steps
+    print("[bench] %.2f us/step; per kernel %s us" % (ms * 1e3, ["%.2f" % (t * 1e3) for t in per_kernel_ms]),
+          file=sys.stderr, flush=True)
+
+    dom = max(range(ncall), key=lambda c: kernels[c][1])
+    kname, kbytes = kernels[dom]
+    kms = per_kernel_ms[dom]
+    achieved = kbytes / (kms * 1e-3) / 1e9
+    tag = "config%d" % args.config
+    traffic = measured_traffic(kname, tag)
+    line = dict(
+        metric="verified rows/sec and achieved HBM GB/s (% of peak), B=128 K=4 V=152064",
+        value=wl.R / (ms * 1e-3), unit="rows/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=ms, higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="bf16" if wl.dtype == 1 else "f32", data="synthetic",
+        hbm_gbps=step_bytes / (ms * 1e-3) / 1e9, hbm_frac=step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        config=dict(workload=wl.name, config=args.config, B=wl.B, R=wl.R, D=wl.D, V=wl.V,
+                    K=None if wl.config == 3 else int((wl.R - wl.B) // wl.B),
+                    relaxed_topk=wl.relaxed_topk, sampled=bool(wl.sampled), input_copies=ncopy,
+                    bytes_per_step=step_bytes, data_seed=1000 + args.config, philox_seed=wl.seed),
+        roofline=dict(bound="hbm", kernel=kname, achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s",
+                      frac=achieved / HBM_PEAK_GBPS, traffic=traffic, bytes_per_launch=kbytes,
+                      launch_us=kms * 1e3),
+    )
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

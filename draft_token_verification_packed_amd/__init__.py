@@ -1,0 +1,269 @@
+"""Packed draft-token verification on MI355X: Python binding of libvspec_verify.
+
+Argument marshalling only. Every step of verification runs in the HIP
+kernels of `libvspec_verify.so` (built in-tree by `build.py`); PyTorch is used
+for device memory and the current stream. There is no CPU fallback: if the
+library is missing or cannot be loaded, every call raises.
+
+Entry points mirror the C ABI in include/vspec_verify.h:
+    verify_greedy(logits, row_offsets, row_owner, draft_tokens, relaxed_topk=1)
+    verify_sampled(logits, row_offsets, row_owner, draft_tokens,
+                   temperature, top_k, top_p, min_p, seed, offset=0)
+    draft_confidence(draft_logits, selected=None)
+"""
+import ctypes
+import os
+
+import torch  # load torch's HIP runtime first so the library binds to it
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvspec_verify.so")
+
+VSV_F32 = 0
+VSV_BF16 = 1
+FLAG_LAYOUT = 1
+FLAG_TOKEN = 2
+FLAG_LOGITS = 4
+FLAG_PARAMS = 8
+
+_STATUS = {0: "VSV_OK", 1: "VSV_EINVAL", 2: "VSV_EUNSUPPORTED", 3: "VSV_EWORKSPACE", 4: "VSV_EHIP"}
+
+
+class VSVError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("%s (%s): %s" % (_STATUS.get(status, status), status, msg))
+        self.status = status
+
+
+class Batch(ctypes.Structure):
+    _fields_ = [("logits", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("ld", ctypes.c_int64), ("num_requests", ctypes.c_int32), ("num_rows", ctypes.c_int32),
+                ("row_offsets", ctypes.c_void_p), ("row_owner", ctypes.c_void_p),
+                ("draft_tokens", ctypes.c_void_p)]
+
+
+class Outputs(ctypes.Structure):
+    _fields_ = [("accepted_len", ctypes.c_void_p), ("next_token", ctypes.c_void_p),
+                ("out_offsets", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p),
+                ("row_token", ctypes.c_void_p), ("row_lse", ctypes.c_void_p),
+                ("error_flag", ctypes.c_void_p)]
+
+
+SYMBOLS = ("vsv_workspace_bytes", "vsv_workspace_init", "vsv_verify_greedy", "vsv_verify_sampled",
+           "vsv_draft_confidence", "vsv_status_string", "vsv_version")
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libvspec_verify.so is not built; run "
+                           "`python -m draft_token_verification_packed_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, u64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t
+    L.vsv_workspace_bytes.argtypes = [i32, i32, i32]
+    L.vsv_workspace_bytes.restype = sz
+    L.vsv_workspace_init.argtypes = [vp, sz, vp]
+    L.vsv_workspace_init.restype = ctypes.c_int
+    L.vsv_verify_greedy.argtypes = [ctypes.POINTER(Batch), i32, ctypes.POINTER(Outputs), vp, sz, vp]
+    L.vsv_verify_greedy.restype = ctypes.c_int
+    L.vsv_verify_sampled.argtypes = [ctypes.POINTER(Batch), vp, vp, vp, vp, u64, u64,
+                                     ctypes.POINTER(Outputs), vp, sz, vp]
+    L.vsv_verify_sampled.restype = ctypes.c_int
+    L.vsv_draft_confidence.argtypes = [vp, i32, i32, i64, i32, vp, vp, vp, vp, vp]
+    L.vsv_draft_confidence.restype = ctypes.c_int
+    L.vsv_status_string.argtypes = [ctypes.c_int]
+    L.vsv_status_string.restype = ctypes.c_char_p
+    L.vsv_version.argtypes = []
+    L.vsv_version.restype = i32
+    _lib = L
+    return L
+
+
+def _check(status):
+    if status != 0:
+        raise VSVError(status, lib().vsv_status_string(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return VSV_BF16
+    if t.dtype == torch.float32:
+        return VSV_F32
+    raise TypeError("logits must be bfloat16 or float32")
+
+
+def _vec(t, n, dtype, name):
+    if t is None or not t.is_cuda or t.dtype != dtype or t.dim() != 1 or t.numel() != n or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous %s CUDA vector of length %d" % (name, dtype, n))
+    return t
+
+
+def _logits(t, vocab):
+    if not t.is_cuda or t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("logits must be a 2-D CUDA tensor with unit column stride")
+    v = t.shape[1] if vocab is None else int(vocab)
+    if v > t.shape[1]:
+        raise ValueError("vocab exceeds the logits width")
+    return _dtype_code(t), v, t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
+
+
+def workspace_bytes(num_requests, num_rows, sampled=False):
+    return int(lib().vsv_workspace_bytes(int(num_requests), int(num_rows), int(bool(sampled))))
+
+
+_ws_cache = {}
+
+
+def workspace(num_requests, num_rows, sampled=False, device=None, stream=None):
+    """A zeroed workspace tensor, cached per (device, stream) and grown on demand.
+
+    Calls on one stream run in order and each leaves the workspace zeroed, so
+    the cached buffer is safe to reuse for later calls on that stream.
+    """
+    need = workspace_bytes(num_requests, num_rows, sampled)
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    key = (dev.index, _stream(stream).value)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(max(need, 4096), dtype=torch.uint8, device=dev)
+        _ws_cache[key] = ws
+    return ws
+
+
+def _prepare(logits, row_offsets, row_owner, draft_tokens, vocab):
+    dtype, V, ld = _logits(logits, vocab)
+    R = logits.shape[0]
+    B = row_offsets.numel() - 1
+    _vec(row_offsets, B + 1, torch.int32, "row_offsets")
+    _vec(row_owner, R, torch.int32, "row_owner")
+    if R - B > 0:
+        _vec(draft_tokens, R - B, torch.int32, "draft_tokens")
+    dev = logits.device
+    out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
+               next_token=torch.empty(B, dtype=torch.int32, device=dev),
+               out_offsets=torch.empty(B + 1, dtype=torch.int32, device=dev),
+               out_tokens=torch.full((max(R, 1),), -1, dtype=torch.int32, device=dev),
+               row_token=torch.empty(R, dtype=torch.int32, device=dev),
+               row_lse=torch.empty(R, dtype=torch.float32, device=dev),
+               error_flag=torch.zeros(1, dtype=torch.int32, device=dev))
+    batch = Batch(_ptr(logits), dtype, V, ld, B, R, _ptr(row_offsets), _ptr(row_owner),
+                  _ptr(draft_tokens) if R - B > 0 else None)
+    outs = Outputs(*[_ptr(out[k]) for k in ("accepted_len", "next_token", "out_offsets", "out_tokens",
+                                            "row_token", "row_lse", "error_flag")])
+    return batch, outs, out, B, R
+
+
+def verify_greedy(logits, row_offsets, row_owner, draft_tokens, relaxed_topk=1, vocab=None,
+                  ws=None, stream=None):
+    """Greedy verification of a packed batch; returns a dict of device tensors."""
+    batch, outs, out, B, R = _prepare(logits, row_offsets, row_owner, draft_tokens, vocab)
+    ws = workspace(B, R, False, logits.device, stream) if ws is None else ws
+    _check(lib().vsv_verify_greedy(ctypes.byref(batch), int(relaxed_topk), ctypes.byref(outs),
+                                   _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def verify_sampled(logits, row_offsets, row_owner, draft_tokens, temperature, top_k, top_p, min_p,
+                   seed, offset=0, vocab=None, ws=None, stream=None):
+    """Sampled / mixed verification of a packed batch; returns a dict of device tensors."""
+    batch, outs, out, B, R = _prepare(logits, row_offsets, row_owner, draft_tokens, vocab)
+    _vec(temperature, B, torch.float32, "temperature")
+    _vec(top_k, B, torch.int32, "top_k")
+    _vec(top_p, B, torch.float32, "top_p")
+    _vec(min_p, B, torch.float32, "min_p")
+    ws = workspace(B, R, True, logits.device, stream) if ws is None else ws
+    _check(lib().vsv_verify_sampled(ctypes.byref(batch), _ptr(temperature), _ptr(top_k), _ptr(top_p),
+                                    _ptr(min_p), int(seed) & (2**64 - 1), int(offset) & (2**64 - 1),
+                                    ctypes.byref(outs), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def draft_confidence(draft_logits, selected=None, vocab=None, stream=None):
+    """(confidence, lse, error_flag) device tensors for every draft row."""
+    dtype, V, ld = _logits(draft_logits, vocab)
+    D = draft_logits.shape[0]
+    if selected is not None:
+        _vec(selected, D, torch.int32, "selected")
+    dev = draft_logits.device
+    conf = torch.empty(D, dtype=torch.float32, device=dev)
+    lse = torch.empty(D, dtype=torch.float32, device=dev)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    _check(lib().vsv_draft_confidence(_ptr(draft_logits), dtype, V, ld, D, _ptr(selected), _ptr(conf),
+                                      _ptr(lse), _ptr(flag), _stream(stream)))
+    return conf, lse, flag
+
+
+class PreparedCall:
+    """One entry-point call with every argument marshalled once.
+
+    `run()` issues the C call on the stream captured at construction; the
+    tensors passed in must stay alive (they are referenced here). Used where
+    per-call Python overhead would otherwise show next to a ~30 us kernel.
+    """
+
+    def __init__(self, fn, args, keep):
+        self._fn = fn
+        self._args = args
+        self._keep = keep
+
+    def run(self):
+        _check(self._fn(*self._args))
+
+
+def prepare_greedy(logits, row_offsets, row_owner, draft_tokens, relaxed_topk=1, vocab=None,
+                   out=None, ws=None, stream=None):
+    batch, outs, res, B, R = _prepare(logits, row_offsets, row_owner, draft_tokens, vocab)
+    if out is not None:
+        res = out
+        outs = Outputs(*[_ptr(res[k]) for k in ("accepted_len", "next_token", "out_offsets", "out_tokens",
+                                                "row_token", "row_lse", "error_flag")])
+    ws = workspace(B, R, False, logits.device, stream) if ws is None else ws
+    args = (ctypes.byref(batch), int(relaxed_topk), ctypes.byref(outs), _ptr(ws), ws.numel(), _stream(stream))
+    return PreparedCall(lib().vsv_verify_greedy, args, (batch, outs, res, ws, logits)), res
+
+
+def prepare_sampled(logits, row_offsets, row_owner, draft_tokens, temperature, top_k, top_p, min_p,
+                    seed, offset=0, vocab=None, out=None, ws=None, stream=None):
+    batch, outs, res, B, R = _prepare(logits, row_offsets, row_owner, draft_tokens, vocab)
+    if out is not None:
+        res = out
+        outs = Outputs(*[_ptr(res[k]) for k in ("accepted_len", "next_token", "out_offsets", "out_tokens",
+                                                "row_token", "row_lse", "error_flag")])
+    for t, dt, name in ((temperature, torch.float32, "temperature"), (top_k, torch.int32, "top_k"),
+                        (top_p, torch.float32, "top_p"), (min_p, torch.float32, "min_p")):
+        _vec(t, B, dt, name)
+    ws = workspace(B, R, True, logits.device, stream) if ws is None else ws
+    args = (ctypes.byref(batch), _ptr(temperature), _ptr(top_k), _ptr(top_p), _ptr(min_p),
+            int(seed) & (2**64 - 1), int(offset) & (2**64 - 1), ctypes.byref(outs), _ptr(ws), ws.numel(),
+            _stream(stream))
+    return PreparedCall(lib().vsv_verify_sampled, args,
+                        (batch, outs, res, ws, logits, temperature, top_k, top_p, min_p)), res
+
+
+def prepare_confidence(draft_logits, selected=None, vocab=None, out=None, stream=None):
+    dtype, V, ld = _logits(draft_logits, vocab)
+    D = draft_logits.shape[0]
+    if selected is not None:
+        _vec(selected, D, torch.int32, "selected")
+    dev = draft_logits.device
+    if out is None:
+        out = (torch.empty(D, dtype=torch.float32, device=dev), torch.empty(D, dtype=torch.float32, device=dev),
+               torch.zeros(1, dtype=torch.int32, device=dev))
+    conf, lse, flag = out
+    args = (_ptr(draft_logits), dtype, V, ld, D, _ptr(selected), _ptr(conf), _ptr(lse), _ptr(flag),
+            _stream(stream))
+    return PreparedCall(lib().vsv_draft_confidence, args, (draft_logits, selected, out)), out

@@ -1,0 +1,138 @@
+// C ABI entry points: host-side validation, workspace carving and launch.
+// Nothing here synchronises, allocates or reads device memory.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.hpp"
+
+using vsv::VerifyArgs;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elem_size(int32_t dtype) { return dtype == VSV_BF16 ? 2 : 4; }
+
+bool dtype_ok(int32_t dtype) { return dtype == VSV_F32 || dtype == VSV_BF16; }
+
+// Common checks of a batch and its outputs; fills the shared launch args.
+vsv_status prepare(const vsv_batch* b, const vsv_outputs* o, void* ws, size_t ws_bytes, int32_t sampled,
+                   VerifyArgs* a, bool* empty) {
+  *empty = false;
+  if (!b || !o) return VSV_EINVAL;
+  if (b->num_requests < 0 || b->num_rows < b->num_requests) return VSV_EINVAL;
+  if (b->num_requests == 0) {
+    if (b->num_rows != 0) return VSV_EINVAL;
+    *empty = true;
+    return VSV_OK;
+  }
+  if (!dtype_ok(b->dtype) || b->vocab < 1 || b->ld < b->vocab) return VSV_EINVAL;
+  if (!b->logits || !aligned(b->logits, elem_size(b->dtype))) return VSV_EINVAL;
+  if (!b->row_offsets || !b->row_owner) return VSV_EINVAL;
+  if (b->num_rows > b->num_requests && !b->draft_tokens) return VSV_EINVAL;
+  if (!o->accepted_len || !o->next_token || !o->out_offsets || !o->out_tokens) return VSV_EINVAL;
+  // the last row must be addressable with 64-bit element offsets
+  if (b->ld > (INT64_MAX / 4) / (b->num_rows > 0 ? b->num_rows : 1)) return VSV_EINVAL;
+  if (!ws || !aligned(ws, vsv::kWsAlign)) return VSV_EWORKSPACE;
+  if (ws_bytes < vsv::ws_bytes(b->num_requests, b->num_rows, sampled)) return VSV_EWORKSPACE;
+
+  VerifyArgs& v = *a;
+  v = VerifyArgs{};
+  v.logits = b->logits;
+  v.ld = b->ld;
+  v.V = b->vocab;
+  v.B = b->num_requests;
+  v.R = b->num_rows;
+  v.dtype = b->dtype;
+  v.offsets = b->row_offsets;
+  v.owner = b->row_owner;
+  v.drafts = b->draft_tokens;
+  v.relaxed_k = 1;
+  v.accepted_len = o->accepted_len;
+  v.next_token = o->next_token;
+  v.out_offsets = o->out_offsets;
+  v.out_tokens = o->out_tokens;
+  v.row_token = o->row_token;
+  v.row_lse = o->row_lse;
+  v.error_flag = o->error_flag;
+  char* w = static_cast<char*>(ws);
+  v.ws_ticket = reinterpret_cast<int32_t*>(w);
+  v.ws_stats = reinterpret_cast<int32_t*>(w) + 16;
+  w += vsv::kWsAlign;
+  v.ws_row_token = reinterpret_cast<int32_t*>(w);
+  w += vsv::ws_align(static_cast<size_t>(b->num_rows) * 4);
+  v.ws_row_acc = reinterpret_cast<int32_t*>(w);
+  return VSV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t vsv_workspace_bytes(int32_t num_requests, int32_t num_rows, int32_t sampled) {
+  if (num_requests < 0 || num_rows < 0) return 0;
+  return vsv::ws_bytes(num_requests, num_rows, sampled);
+}
+
+vsv_status vsv_workspace_init(void* workspace, size_t bytes, hipStream_t stream) {
+  if (!workspace || !aligned(workspace, 4) || bytes % 4) return VSV_EINVAL;
+  return vsv::launch_zero(workspace, bytes, stream) == hipSuccess ? VSV_OK : VSV_EHIP;
+}
+
+vsv_status vsv_verify_greedy(const vsv_batch* batch, int32_t relaxed_topk, const vsv_outputs* out,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  VerifyArgs a;
+  bool empty = false;
+  const vsv_status st = prepare(batch, out, workspace, workspace_bytes, 0, &a, &empty);
+  if (st != VSV_OK || empty) return st;
+  if (relaxed_topk < 1 || relaxed_topk > batch->vocab) return VSV_EINVAL;
+  a.relaxed_k = relaxed_topk;
+  return vsv::launch_verify_greedy(a, stream) == hipSuccess ? VSV_OK : VSV_EHIP;
+}
+
+vsv_status vsv_verify_sampled(const vsv_batch* batch, const float* temperature, const int32_t* top_k,
+                              const float* top_p, const float* min_p, uint64_t seed, uint64_t offset,
+                              const vsv_outputs* out, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  VerifyArgs a;
+  bool empty = false;
+  const vsv_status st = prepare(batch, out, workspace, workspace_bytes, 1, &a, &empty);
+  if (st != VSV_OK || empty) return st;
+  if (!temperature || !top_k || !top_p || !min_p) return VSV_EINVAL;
+  a.temperature = temperature;
+  a.top_k = top_k;
+  a.top_p = top_p;
+  a.min_p = min_p;
+  a.seed = seed;
+  a.offset = offset;
+  const hipError_t e = vsv::launch_verify_sampled(a, stream);
+  if (e == hipErrorNotSupported) return VSV_EUNSUPPORTED;
+  return e == hipSuccess ? VSV_OK : VSV_EHIP;
+}
+
+vsv_status vsv_draft_confidence(const void* draft_logits, int32_t dtype, int32_t vocab, int64_t ld,
+                                int32_t num_draft_rows, const int32_t* selected, float* confidence,
+                                float* lse, int32_t* error_flag, hipStream_t stream) {
+  if (num_draft_rows < 0) return VSV_EINVAL;
+  if (num_draft_rows == 0) return VSV_OK;
+  if (!dtype_ok(dtype) || vocab < 1 || ld < vocab) return VSV_EINVAL;
+  if (!draft_logits || !aligned(draft_logits, elem_size(dtype)) || !confidence) return VSV_EINVAL;
+  if (ld > (INT64_MAX / 4) / num_draft_rows) return VSV_EINVAL;
+  vsv::ConfidenceArgs a{draft_logits, ld, vocab, num_draft_rows, dtype, selected, confidence, lse, error_flag};
+  return vsv::launch_confidence(a, stream) == hipSuccess ? VSV_OK : VSV_EHIP;
+}
+
+const char* vsv_status_string(vsv_status status) {
+  switch (status) {
+    case VSV_OK: return "ok";
+    case VSV_EINVAL: return "invalid argument";
+    case VSV_EUNSUPPORTED: return "unsupported option";
+    case VSV_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case VSV_EHIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t vsv_version(void) { return 100; }
+
+}  // extern "C"

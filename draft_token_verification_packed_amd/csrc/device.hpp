@@ -1,0 +1,155 @@
+// Device helpers shared by the verification kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+
+namespace vsv {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- elements
+// A row is streamed in 16-byte vectors: 4 float32 or 8 bfloat16 logits.
+
+template <typename E> struct Elem;
+
+template <> struct Elem<float> {
+  static constexpr int kVec = 4;
+  __device__ static __forceinline__ float at(const float* p, int64_t i) { return p[i]; }
+  __device__ static __forceinline__ void decode(const u32x4& w, float* f) {
+    f[0] = __uint_as_float(w.x);
+    f[1] = __uint_as_float(w.y);
+    f[2] = __uint_as_float(w.z);
+    f[3] = __uint_as_float(w.w);
+  }
+};
+
+// bfloat16 is the top half of a float32: the low element of a 32-bit word
+// is widened by a shift, the high one by masking.
+template <> struct Elem<uint16_t> {
+  static constexpr int kVec = 8;
+  __device__ static __forceinline__ float at(const uint16_t* p, int64_t i) {
+    return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+  }
+  __device__ static __forceinline__ void decode(const u32x4& w, float* f) {
+    f[0] = __uint_as_float(w.x << 16);
+    f[1] = __uint_as_float(w.x & 0xFFFF0000u);
+    f[2] = __uint_as_float(w.y << 16);
+    f[3] = __uint_as_float(w.y & 0xFFFF0000u);
+    f[4] = __uint_as_float(w.z << 16);
+    f[5] = __uint_as_float(w.z & 0xFFFF0000u);
+    f[6] = __uint_as_float(w.w << 16);
+    f[7] = __uint_as_float(w.w & 0xFFFF0000u);
+  }
+};
+
+// Streaming load: the logits are read exactly once, so keep them out of
+// the caches' way (nt bit).
+__device__ __forceinline__ u32x4 load_stream(const u32x4* p) {
+  return __builtin_nontemporal_load(p);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------- reductions
+
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = op(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Every thread receives the reduction of `v` over the block. `scratch` holds
+// NT / 64 values; the leading barrier makes back-to-back calls safe.
+template <int NT, typename T, typename Op>
+__device__ __forceinline__ T block_reduce(T v, Op op, T* scratch) {
+  v = wave_reduce(v, op);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) scratch[threadIdx.x / kWave] = v;
+  __syncthreads();
+  T r = scratch[0];
+#pragma unroll
+  for (int w = 1; w < NT / kWave; ++w) r = op(r, scratch[w]);
+  return r;
+}
+
+struct MaxOp {
+  template <typename T> __device__ __forceinline__ T operator()(T a, T b) const { return a > b ? a : b; }
+};
+struct MinOp {
+  template <typename T> __device__ __forceinline__ T operator()(T a, T b) const { return a < b ? a : b; }
+};
+struct SumOp {
+  template <typename T> __device__ __forceinline__ T operator()(T a, T b) const { return a + b; }
+};
+
+// Inclusive prefix sum over a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int n = __shfl_up(v, o, kWave);
+    if (lane >= o) v += n;
+  }
+  return v;
+}
+
+// Exclusive prefix sum over the block; `total` receives the block sum.
+// `scratch` holds NT / 64 ints.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int& total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const int incl = wave_inclusive_scan(v);
+  __syncthreads();
+  if (lane == kWave - 1) scratch[w] = incl;
+  __syncthreads();
+  int before = 0, sum = 0;
+#pragma unroll
+  for (int k = 0; k < NT / kWave; ++k) {
+    const int s = scratch[k];
+    before += (k < w) ? s : 0;
+    sum += s;
+  }
+  total = sum;
+  return before + incl - v;
+}
+
+// ---------------------------------------------------------------- Philox
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
+// 32x32->64 multiplies whose halves are XOR-mixed with the other counter
+// words and the key; the key is bumped by two Weyl constants between rounds.
+
+struct Philox4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ Philox4 philox4x32_10(Philox4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = 0xD2511F53u * c.x;
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c.x);
+    const uint32_t lo1 = 0xCD9E8D57u * c.z;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z);
+    c = Philox4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+  }
+  return c;
+}
+
+// Uniform on the 2^-24 grid in [0, 1) for (request, local row).
+__device__ __forceinline__ double row_uniform(uint64_t seed, uint64_t offset, int request, int row) {
+  const Philox4 o = philox4x32_10(
+      Philox4{static_cast<uint32_t>(row), static_cast<uint32_t>(request),
+              static_cast<uint32_t>(offset), static_cast<uint32_t>(offset >> 32)},
+      static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
+  return static_cast<double>(o.x >> 8) * (1.0 / 16777216.0);
+}
+
+}  // namespace vsv

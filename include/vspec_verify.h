@@ -1,0 +1,159 @@
+/*
+ * vspec_verify.h -- C ABI of the packed draft-token verification library
+ * (MI355X / gfx950).
+ *
+ * One call verifies a whole ragged batch of speculative-decoding requests
+ * whose target logits rows are packed into one matrix. Request i owns the
+ * consecutive rows row_offsets[i] .. row_offsets[i+1]-1: its K_i draft-verify
+ * rows first, then its bonus row (K_i = row_offsets[i+1] - row_offsets[i] - 1
+ * may be 0). Per-request data is reached from a row through the row-owner
+ * map, as the xLLM documentation describes its ragged verifier ("Adaptive
+ * speculative inference", DSpark section "Launch example": per-request
+ * sampling parameters are mapped through device-side packed-row owners, and
+ * packing boundaries are never read back to the host).
+ *
+ * Conventions shared by every entry point:
+ *  - Every data pointer is a caller-owned DEVICE pointer unless stated. The
+ *    library allocates nothing and keeps no state between calls; calls are
+ *    reentrant and may run concurrently on different streams as long as they
+ *    use different workspaces and outputs.
+ *  - All work is enqueued on `stream` (0 = the null stream). Nothing is
+ *    synchronised and nothing is read back to the host; results are valid
+ *    once the stream reaches them.
+ *  - Host-side argument errors return a status before anything is enqueued.
+ *    Conditions that only the device can see (layout, token range, logits,
+ *    sampling parameters) set bits in the optional sticky `error_flag` word;
+ *    outputs are then unspecified but every write stays inside the buffers.
+ *  - bfloat16 logits are raw 16-bit patterns; float32 logits are IEEE single.
+ *    Row r starts at element r * ld; only its first `vocab` entries are read.
+ *    The logits pointer must be aligned to the element size.
+ *  - Token ties are broken by lowest index; values compare as IEEE numbers
+ *    (so -0 == +0).
+ */
+#ifndef VSPEC_VERIFY_H
+#define VSPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VSV_OK = 0,
+  VSV_EINVAL = 1,        /* NULL required pointer, bad size, dtype or option  */
+  VSV_EUNSUPPORTED = 2,  /* option not built into this library                */
+  VSV_EWORKSPACE = 3,    /* workspace NULL, misaligned or smaller than needed */
+  VSV_EHIP = 4           /* the HIP runtime refused the launch                */
+} vsv_status;
+
+typedef enum { VSV_F32 = 0, VSV_BF16 = 1 } vsv_dtype;
+
+/* Bits of the sticky device error word (OR-ed in, never cleared). */
+#define VSV_FLAG_LAYOUT 1  /* offsets not 0 .. R strictly increasing, or owner map inconsistent */
+#define VSV_FLAG_TOKEN 2   /* a draft / selected token outside [0, vocab): treated as a mismatch */
+#define VSV_FLAG_LOGITS 4  /* NaN or +inf logit, or a row with no finite logit                  */
+#define VSV_FLAG_PARAMS 8  /* temperature < 0, top_p outside (0, 1], min_p outside [0, 1]       */
+
+typedef struct {
+  const void* logits;          /* [num_rows, ld] vocab-wide target logits             */
+  int32_t dtype;               /* vsv_dtype                                           */
+  int32_t vocab;               /* V >= 1                                              */
+  int64_t ld;                  /* row stride in elements, >= vocab                    */
+  int32_t num_requests;        /* B >= 0                                              */
+  int32_t num_rows;            /* R = sum_i (K_i + 1) >= B                            */
+  const int32_t* row_offsets;  /* [B + 1]: 0 = off[0] < off[1] < ... < off[B] = R     */
+  const int32_t* row_owner;    /* [R]: owner[r] = i for off[i] <= r < off[i+1]        */
+  const int32_t* draft_tokens; /* [R - B]: draft j of request i at off[i] - i + j;     */
+                               /* may be NULL when R == B                             */
+} vsv_batch;
+
+typedef struct {
+  int32_t* accepted_len; /* [B] a_i = number of leading accepted drafts              */
+  int32_t* next_token;   /* [B] replacement token (a_i < K_i) or bonus (a_i = K_i)   */
+  int32_t* out_offsets;  /* [B + 1] exclusive scan of (a_i + 1); out_offsets[B] = total */
+  int32_t* out_tokens;   /* [R] capacity; request i writes its a_i accepted drafts   */
+                         /* and then next_token[i] at out_offsets[i]                 */
+  int32_t* row_token;    /* [R] or NULL: the target token chosen for every row       */
+  float* row_lse;        /* [R] or NULL: log-sum-exp of the logits the row uses:     */
+                         /* x for greedy rows, x / T for sampled rows                */
+  int32_t* error_flag;   /* [1] or NULL: sticky VSV_FLAG_* bits                      */
+} vsv_outputs;
+
+/* Bytes of device workspace a verify call needs (B requests, R rows).
+ * The workspace must be zero-filled before its first use (vsv_workspace_init
+ * or any zeroed allocation); every call leaves it zeroed again when it
+ * completes, so one workspace can serve any later call on the same stream.
+ * Two calls that may overlap in time need two workspaces. */
+size_t vsv_workspace_bytes(int32_t num_requests, int32_t num_rows, int32_t sampled);
+
+/* Zero-fill `bytes` of workspace on `stream` with a kernel (no memset node,
+ * so it can be captured into a HIP graph). */
+vsv_status vsv_workspace_init(void* workspace, size_t bytes, hipStream_t stream);
+
+/* Greedy target verification.
+ * Every row's target token is its arg-max (vllm-hust-vspec 0.13.0 README,
+ * "EAGLE features": strict greedy top-1 acceptance on a linear, D2H-free
+ * acceptance path). relaxed_topk = 1 accepts a draft iff it equals that
+ * token; relaxed_topk = K > 1 accepts a draft whose rank in the order
+ * (value desc, index asc) is below K, and then emits the draft token itself
+ * (same README, "Scope of support": relaxed top-K acceptance is an explicit
+ * quality trade-off whose output may differ from strict greedy). The scan
+ * accepts the longest run of leading accepted drafts; the next token is the
+ * target token of the first rejected row, or of the bonus row if all pass.
+ * Errors: VSV_EINVAL (NULL logits/offsets/owner/required output, vocab < 1,
+ * ld < vocab, num_rows < num_requests, relaxed_topk outside [1, vocab],
+ * misaligned logits, unknown dtype), VSV_EWORKSPACE, VSV_EHIP. */
+vsv_status vsv_verify_greedy(const vsv_batch* batch, int32_t relaxed_topk,
+                             const vsv_outputs* out, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/* Sampled (or mixed) target verification with point-mass drafts.
+ * Per-request device arrays [B]: temperature (0 = greedy arg-max for that
+ * request), top_k (<= 0 or >= vocab: off), top_p (>= 1: off), min_p
+ * (<= 0: off). For T > 0 every row draws its own token from the
+ * temperature-scaled distribution filtered in this order: top-k, then top-p
+ * renormalised over the top-k survivors (shortest prefix of the rank order
+ * whose mass reaches top_p, crossing token kept), then min-p (keep
+ * (x - max)/T >= ln(min_p)); the draw is the inverse CDF in rank order at
+ * u = (w0 >> 8) * 2^-24, w0 = word 0 of Philox4x32-10 with counter
+ * (local row j, request i, offset lo, offset hi) and key (seed lo, seed hi).
+ * With deterministic drafts this equals rejection sampling against a point
+ * mass: the leading matches are accepted, the first mismatching sample is
+ * the replacement and the last row's sample is the bonus (xLLM docs,
+ * "Adaptive speculative inference", DSpark section "Launch example").
+ * Acceptance is strict (draft == sampled token).
+ * Errors: as vsv_verify_greedy, plus VSV_EINVAL for NULL parameter arrays. */
+vsv_status vsv_verify_sampled(const vsv_batch* batch, const float* temperature,
+                              const int32_t* top_k, const float* top_p,
+                              const float* min_p, uint64_t seed, uint64_t offset,
+                              const vsv_outputs* out, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/* Draft confidence c_q = exp(y[s_q] - logsumexp(y)) for every draft row q of
+ * raw draft logits y (no temperature): the draft probability of the selected
+ * token, the score adaptive verification budgets consume (xLLM docs,
+ * "Adaptive speculative inference", section "Adaptive target verification
+ * from MTP logits"). selected = NULL uses each row's arg-max; an out-of-range
+ * selected token gives c_q = 0 and sets VSV_FLAG_TOKEN. lse may be NULL.
+ * Errors: VSV_EINVAL (NULL logits/confidence, vocab < 1, ld < vocab,
+ * num_draft_rows < 0, misaligned logits, unknown dtype), VSV_EHIP. */
+vsv_status vsv_draft_confidence(const void* draft_logits, int32_t dtype,
+                                int32_t vocab, int64_t ld, int32_t num_draft_rows,
+                                const int32_t* selected, float* confidence,
+                                float* lse, int32_t* error_flag,
+                                hipStream_t stream);
+
+/* Static description of a status code. */
+const char* vsv_status_string(vsv_status status);
+
+/* Library ABI version (major * 100 + minor). */
+int32_t vsv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VSPEC_VERIFY_H */

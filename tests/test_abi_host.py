@@ -1,0 +1,128 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point the header declares, and rejects bad arguments with a
+status before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import draft_token_verification_packed_amd as vsv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vspec_verify.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(vsv.LIB_PATH):
+        pytest.skip("library not built (run the package build first)")
+    return vsv.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(vsv_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    assert set(vsv.SYMBOLS) <= set(names)
+    assert {"vsv_verify_greedy", "vsv_verify_sampled", "vsv_draft_confidence"} <= set(names)
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings_and_version(L):
+    assert L.vsv_status_string(0) == b"ok"
+    for s in range(1, 5):
+        assert len(L.vsv_status_string(s)) > 3
+    assert L.vsv_version() >= 100
+
+
+def test_workspace_bytes(L):
+    assert L.vsv_workspace_bytes(0, 0, 0) >= 256
+    b = L.vsv_workspace_bytes(128, 640, 0)
+    assert b % 256 == 0 and b >= 640 * 8
+    assert L.vsv_workspace_bytes(-1, 5, 0) == 0
+    assert L.vsv_workspace_bytes(128, 640, 1) >= b
+
+
+def _batch(**kw):
+    b = dict(logits=0x10000, dtype=1, vocab=1024, ld=1024, num_requests=4, num_rows=20,
+             row_offsets=0x20000, row_owner=0x30000, draft_tokens=0x40000)
+    b.update(kw)
+    return vsv.Batch(**b)
+
+
+def _outs(**kw):
+    o = dict(accepted_len=0x50000, next_token=0x60000, out_offsets=0x70000, out_tokens=0x80000,
+             row_token=None, row_lse=None, error_flag=None)
+    o.update(kw)
+    return vsv.Outputs(**o)
+
+
+def _greedy(L, batch, outs, ws=0x100000, ws_bytes=1 << 20, k=1):
+    return L.vsv_verify_greedy(ctypes.byref(batch) if batch is not None else None, k,
+                               ctypes.byref(outs) if outs is not None else None,
+                               ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(logits=None), dict(dtype=7), dict(vocab=0), dict(ld=1000), dict(num_rows=3),
+    dict(num_requests=-1), dict(row_offsets=None), dict(row_owner=None), dict(draft_tokens=None),
+    dict(logits=0x10001), dict(dtype=0, logits=0x10002), dict(num_requests=0, num_rows=5),
+])
+def test_invalid_batch_is_rejected_before_launch(L, bad):
+    assert _greedy(L, _batch(**bad), _outs()) == 1
+
+
+@pytest.mark.parametrize("bad", [dict(accepted_len=None), dict(next_token=None), dict(out_offsets=None),
+                                 dict(out_tokens=None)])
+def test_missing_required_output_is_rejected(L, bad):
+    assert _greedy(L, _batch(), _outs(**bad)) == 1
+
+
+def test_null_structs_and_workspace_errors(L):
+    assert _greedy(L, None, _outs()) == 1
+    assert _greedy(L, _batch(), None) == 1
+    assert _greedy(L, _batch(), _outs(), ws=0) == 3
+    assert _greedy(L, _batch(), _outs(), ws=0x100010) == 3       # misaligned
+    assert _greedy(L, _batch(), _outs(), ws_bytes=64) == 3       # too small
+
+
+def test_relaxed_topk_range(L):
+    assert _greedy(L, _batch(), _outs(), k=0) == 1
+    assert _greedy(L, _batch(), _outs(), k=1025) == 1
+
+
+def test_empty_batch_is_a_noop(L):
+    assert _greedy(L, _batch(num_requests=0, num_rows=0), _outs(), ws=0, ws_bytes=0) == 0 or \
+        _greedy(L, _batch(num_requests=0, num_rows=0), _outs()) == 0
+    assert _greedy(L, _batch(num_requests=0, num_rows=0, logits=None), _outs()) == 0
+
+
+def test_sampled_rejects_missing_parameters(L):
+    b, o = _batch(), _outs()
+    st = L.vsv_verify_sampled(ctypes.byref(b), None, ctypes.c_void_p(8), ctypes.c_void_p(8),
+                              ctypes.c_void_p(8), 1, 0, ctypes.byref(o), ctypes.c_void_p(0x100000), 1 << 20, None)
+    assert st == 1
+
+
+def test_confidence_validation(L):
+    f = L.vsv_draft_confidence
+    assert f(ctypes.c_void_p(0x10000), 1, 100, 100, 0, None, None, None, None, None) == 0   # D = 0: no-op
+    assert f(ctypes.c_void_p(0x10000), 1, 100, 100, -1, None, ctypes.c_void_p(8), None, None, None) == 1
+    assert f(None, 1, 100, 100, 4, None, ctypes.c_void_p(8), None, None, None) == 1
+    assert f(ctypes.c_void_p(0x10000), 1, 100, 99, 4, None, ctypes.c_void_p(8), None, None, None) == 1
+    assert f(ctypes.c_void_p(0x10000), 1, 100, 100, 4, None, None, None, None, None) == 1
+    assert f(ctypes.c_void_p(0x10000), 3, 100, 100, 4, None, ctypes.c_void_p(8), None, None, None) == 1
+    assert f(ctypes.c_void_p(0x10001), 1, 100, 100, 4, None, ctypes.c_void_p(8), None, None, None) == 1
+
+
+def test_workspace_init_validation(L):
+    assert L.vsv_workspace_init(None, 256, None) == 1
+    assert L.vsv_workspace_init(ctypes.c_void_p(0x1000), 6, None) == 1
