@@ -10,6 +10,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 LIB = os.path.join(PKG, "libvspec_verify.so")
 SOURCES = ["abi.cpp", "verify.hip", "confidence.hip"]
 ARCH = "gfx950"
@@ -29,7 +30,7 @@ def hipcc():
 
 def build(extra_flags=(), out=LIB, verbose=False):
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    cmd = [hipcc()] + FLAGS + list(extra_flags) + ["-I", CSRC] + srcs + ["-o", out + ".tmp"]
+    cmd = [hipcc()] + FLAGS + list(extra_flags) + ["-I", CSRC, "-I", INCLUDE] + srcs + ["-o", out + ".tmp"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)

@@ -59,9 +59,7 @@ vsv_status prepare(const vsv_batch* b, const vsv_outputs* o, void* ws, size_t ws
   v.ws_ticket = reinterpret_cast<int32_t*>(w);
   v.ws_stats = reinterpret_cast<int32_t*>(w) + 16;
   w += vsv::kWsAlign;
-  v.ws_row_token = reinterpret_cast<int32_t*>(w);
-  w += vsv::ws_align(static_cast<size_t>(b->num_rows) * 4);
-  v.ws_row_acc = reinterpret_cast<int32_t*>(w);
+  v.ws_row = reinterpret_cast<uint32_t*>(w);
   return VSV_OK;
 }
 

@@ -9,9 +9,7 @@ namespace vsv {
 
 template <typename E, int NT, int U>
 __global__ __launch_bounds__(NT) void confidence_kernel(ConfidenceArgs a) {
-  __shared__ float scr_f[NT / kWave];
-  __shared__ int scr_i[NT / kWave];
-  __shared__ double scr_d[NT / kWave];
+  __shared__ RowScratch<NT> scr;
   const int q = blockIdx.x;
   const E* __restrict__ row = static_cast<const E*>(a.logits) + static_cast<int64_t>(q) * a.ld;
   int sel = -1;
@@ -24,7 +22,7 @@ __global__ __launch_bounds__(NT) void confidence_kernel(ConfidenceArgs a) {
   partial_init(p);
   constexpr float kLog2e = 1.4426950408889634f;
   stream_row<E, NT, U, false>(row, a.V, kLog2e, INFINITY, 0, p);
-  const RowResult res = finish_row<E, NT>(row, p, scr_f, scr_i, scr_d);
+  const RowResult res = finish_row<E, NT, U, false>(p, scr, row);
   if (threadIdx.x == 0) {
     int bits = 0;
     if (!(res.max < INFINITY) || res.argmax == INT32_MAX || !isfinite(res.lse)) bits |= VSV_FLAG_LOGITS;

@@ -55,6 +55,30 @@ __device__ __forceinline__ u32x4 load_stream(const u32x4* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------- cross-workgroup data
+// Data one workgroup hands to another inside a launch moves only through
+// agent-scope relaxed atomics: on gfx950 these are sc1 accesses, coherent
+// across the XCDs' separate L2 caches, so no device-wide fence (an L2
+// write-back plus invalidate per workgroup) is needed. A writer waits for
+// its stores to be acknowledged before it bumps the ticket that publishes
+// them.
+
+__device__ __forceinline__ void store_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ticket_agent(int* p) {
+  return __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_int_agent(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory access this wave issued has completed (stores
+// acknowledged).
+__device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
 // ---------------------------------------------------------------- reductions
 
 template <typename T, typename Op>

@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/vspec_verify.h"
+#include "vspec_verify.h"
 
 namespace vsv {
 
@@ -13,7 +13,7 @@ namespace vsv {
 #define VSV_VERIFY_THREADS 512
 #endif
 #ifndef VSV_UNROLL
-#define VSV_UNROLL 4
+#define VSV_UNROLL 2
 #endif
 constexpr int kVerifyThreads = VSV_VERIFY_THREADS;
 constexpr int kUnroll = VSV_UNROLL;
@@ -42,10 +42,9 @@ struct VerifyArgs {
   float* row_lse;
   int32_t* error_flag;
   // workspace
-  int32_t* ws_ticket;     // finished-row counter
-  int32_t* ws_row_token;  // [R] chosen token per row
-  int32_t* ws_row_acc;    // [R] 1 if the row's draft was accepted
-  int32_t* ws_stats;      // [4] diagnostics (rows that took the slow path)
+  int32_t* ws_ticket;   // finished-row counter
+  uint32_t* ws_row;     // [R] emitted token of the row | 0x80000000 if its draft was accepted
+  int32_t* ws_stats;    // [4] diagnostics (rows that took the slow path)
 };
 
 struct ConfidenceArgs {
@@ -63,7 +62,7 @@ constexpr size_t kWsAlign = 256;
 inline size_t ws_align(size_t b) { return (b + kWsAlign - 1) / kWsAlign * kWsAlign; }
 inline size_t ws_bytes(int32_t B, int32_t R, int32_t /*sampled*/) {
   (void)B;
-  return kWsAlign + 2 * ws_align(static_cast<size_t>(R) * 4);
+  return kWsAlign + ws_align(static_cast<size_t>(R) * 4);
 }
 
 hipError_t launch_verify_greedy(const VerifyArgs& a, hipStream_t s);

@@ -1,14 +1,15 @@
 // One-pass streaming statistics of a vocab-wide logits row, computed by one
-// workgroup: maximum, lowest arg-max, log-sum-exp of x * scale and (for
-// relaxed acceptance) the rank of one token.
+// workgroup: maximum, lowest arg-max, log-sum-exp of x * c and (for relaxed
+// acceptance) the rank of one token.
 //
 // Each thread walks 16-byte vectors tid, tid + NT, ... (a wave reads 1 KiB
 // contiguous per load instruction), so its own elements arrive in increasing
-// index order. Per vector it takes the vector max (v_max3 chain), keeps the
-// first vector whose max beats its running best (the exact lane is resolved
-// once at the end by re-reading that vector), and adds exp2(x*c - mc) to two
-// partial sums. mc is a per-thread exponent reference that is only moved
-// when a value would exceed it by 2^24, so the rescale branch is rare.
+// index order. Per group of U vectors it takes the group max (v_max3 chains)
+// and remembers the first group whose max beats its running best; only the
+// thread holding the row maximum re-reads that group at the end to find the
+// exact lane. Every element adds exp2(x*c - mc) to one of two partial sums;
+// mc is a per-thread exponent reference that only moves when a value would
+// exceed it by 2^24, so the rescale branch is rare.
 #pragma once
 
 #include "device.hpp"
@@ -17,8 +18,10 @@ namespace vsv {
 
 struct RowPartial {
   float best;   // largest value seen (-inf if none)
-  int bpos;     // element index of that value, or start of its vector
-  int bvec;     // 1: bpos is a vector start still to be resolved
+  int bpos;     // where it was first seen: see bvec
+  int bvec;     // 0: bpos is its element index; 1: bpos is the element index
+                // of the 16-byte vector holding it; 2: bpos is the vector
+                // index of the first vector of the thread's group holding it
   float mc;     // exponent reference (log2 domain)
   float s0, s1; // sum of exp2(x*c - mc)
   int rank;     // elements ordered before token d (relaxed acceptance)
@@ -27,8 +30,15 @@ struct RowPartial {
 struct RowResult {
   float max;     // row maximum
   int argmax;    // lowest index attaining it (INT32_MAX if no finite value)
-  double lse;    // log(sum exp(x / T)) in natural units
+  double lse;    // log(sum exp(x * c * ln2)) in natural units
   int rank;      // number of elements ordered before d
+};
+
+// LDS for finish_row: one slot per wave per reduced quantity.
+template <int NT> struct RowScratch {
+  float f[NT / kWave][2];
+  int i[NT / kWave][2];
+  double d[NT / kWave];
 };
 
 __device__ __forceinline__ void partial_init(RowPartial& p) {
@@ -61,14 +71,23 @@ __device__ __forceinline__ void take_scalar(RowPartial& p, float x, int e, float
   if (kRank) p.rank += (x > xd || (x == xd && e < d)) ? 1 : 0;
 }
 
-template <typename E, bool kRank>
-__device__ __forceinline__ void take_vector(RowPartial& p, const u32x4& w, int e0, float c, float xd, int d) {
+// Decode one 16-byte vector into f and return its maximum.
+template <typename E>
+__device__ __forceinline__ float vec_max(const u32x4& w, float* f) {
   constexpr int N = Elem<E>::kVec;
-  float f[N];
   Elem<E>::decode(w, f);
   float vmax = f[0];
 #pragma unroll
   for (int k = 1; k < N; ++k) vmax = fmaxf(vmax, f[k]);
+  return vmax;
+}
+
+// A single vector (the predicated last group).
+template <typename E, bool kRank>
+__device__ __forceinline__ void take_vector(RowPartial& p, const u32x4& w, int e0, float c, float xd, int d) {
+  constexpr int N = Elem<E>::kVec;
+  float f[N];
+  const float vmax = vec_max<E>(w, f);
   const bool gt = vmax > p.best;
   p.best = gt ? vmax : p.best;
   p.bpos = gt ? e0 : p.bpos;
@@ -88,10 +107,51 @@ __device__ __forceinline__ void take_vector(RowPartial& p, const u32x4& w, int e
   }
 }
 
-// Stream row[0 .. V) into this thread's partial. c = log2(e) / T.
-template <typename E, int NT, int U, bool kRank>
+// A group of U vectors of one thread: one best/rescale update for the group.
+template <typename E, int U, int NT, bool kRank>
+__device__ __forceinline__ void take_group(RowPartial& p, const u32x4* w, int v, int head, float c, float xd, int d) {
+  constexpr int N = Elem<E>::kVec;
+  float f[U][N];
+  float vmx[U];
+  float gmax = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    vmx[u] = vec_max<E>(w[u], f[u]);
+    gmax = fmaxf(gmax, vmx[u]);
+  }
+  const bool gt = gmax > p.best;
+  p.best = gt ? gmax : p.best;
+  p.bpos = gt ? v : p.bpos;      // group: first vector index
+  p.bvec = gt ? 2 : p.bvec;
+  if (fmaf(gmax, c, -p.mc) > 24.0f) partial_rescale(p, gmax, c);
+  const float nmc = -p.mc;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+#pragma unroll
+    for (int k = 0; k < N; k += 2) {
+      p.s0 += fast_exp2(fmaf(f[u][k], c, nmc));
+      p.s1 += fast_exp2(fmaf(f[u][k + 1], c, nmc));
+    }
+    if (kRank) {
+      const int e0 = head + (v + u * NT) * N;
+      if (vmx[u] >= xd) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) p.rank += (f[u][k] > xd || (f[u][k] == xd && e0 + k < d)) ? 1 : 0;
+      }
+    }
+  }
+}
+
+struct NoHook {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+// Stream row[0 .. V) into this thread's partial. c = log2(e) / T. `hook` runs
+// once, right after the first group's loads are issued, so loads it issues
+// overlap the stream instead of trailing it.
+template <typename E, int NT, int U, bool kRank, typename Hook = NoHook>
 __device__ __forceinline__ void stream_row(const E* __restrict__ row, int V, float c, float xd, int d,
-                                           RowPartial& p) {
+                                           RowPartial& p, Hook hook = Hook()) {
   constexpr int N = Elem<E>::kVec;
   const int tid = threadIdx.x;
   const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
@@ -100,32 +160,81 @@ __device__ __forceinline__ void stream_row(const E* __restrict__ row, int V, flo
   const int nvec = (V - head) / N;
   const int body_end = head + nvec * N;
 
-  if (tid < head) take_scalar<kRank>(p, Elem<E>::at(row, tid), tid, c, xd, d);
-
   const u32x4* __restrict__ vp = reinterpret_cast<const u32x4*>(row + head);
+  // Groups of U vectors per thread, software-pipelined: the loads of group
+  // g + 1 are in flight while group g is reduced. Only the last group can be
+  // partial; its loads and updates are predicated on the vector index.
+  constexpr int G = U * NT;
+  const int ngroups = (nvec + G - 1) / G;
   int v = tid;
-  for (; v + (U - 1) * NT < nvec; v += U * NT) {
-    u32x4 w[U];
+  u32x4 cur[U];
+  if (ngroups > 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) w[u] = load_stream(vp + v + u * NT);
-#pragma unroll
-    for (int u = 0; u < U; ++u) take_vector<E, kRank>(p, w[u], head + (v + u * NT) * N, c, xd, d);
+    for (int u = 0; u < U; ++u)
+      if (ngroups > 1 || v + u * NT < nvec) cur[u] = load_stream(vp + v + u * NT);
   }
-  for (; v < nvec; v += NT) take_vector<E, kRank>(p, load_stream(vp + v), head + v * N, c, xd, d);
+  hook();
+  if (tid < head) take_scalar<kRank>(p, Elem<E>::at(row, tid), tid, c, xd, d);
+  if (ngroups > 0) {
+    for (int g = 1; g < ngroups; ++g) {
+      u32x4 nxt[U];
+      const int vn = v + G;
+      const bool full = g + 1 < ngroups;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (full || vn + u * NT < nvec) nxt[u] = load_stream(vp + vn + u * NT);
+      take_group<E, U, NT, kRank>(p, cur, v, head, c, xd, d);
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+      v = vn;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (v + u * NT < nvec) take_vector<E, kRank>(p, cur[u], head + (v + u * NT) * N, c, xd, d);
+  }
 
   const int tail = V - body_end;
   if (tid < tail) take_scalar<kRank>(p, Elem<E>::at(row, body_end + tid), body_end + tid, c, xd, d);
 }
 
-// Combine the block's partials. Every thread receives the result.
-// `scr_f`, `scr_i` and `scr_d` each hold NT / 64 entries.
-template <typename E, int NT>
-__device__ __forceinline__ RowResult finish_row(const E* __restrict__ row, RowPartial& p, float* scr_f,
-                                                int* scr_i, double* scr_d) {
+// Combine the block's partials in two rounds (max and exponent reference;
+// then arg-max index, sum and rank). Every thread receives the result. `row`
+// is the streamed row: the thread holding the maximum re-reads its group.
+template <typename E, int NT, int U, bool kRank>
+__device__ __forceinline__ RowResult finish_row(RowPartial& p, RowScratch<NT>& s, const E* __restrict__ row) {
   constexpr int N = Elem<E>::kVec;
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+
+  const float m1 = wave_reduce(p.best, MaxOp());
+  const float m2 = wave_reduce(p.mc, MaxOp());
+  if (lane == 0) {
+    s.f[w][0] = m1;
+    s.f[w][1] = m2;
+  }
+  __syncthreads();
+  float mx = s.f[0][0], mref = s.f[0][1];
+#pragma unroll
+  for (int k = 1; k < NW; ++k) {
+    mx = fmaxf(mx, s.f[k][0]);
+    mref = fmaxf(mref, s.f[k][1]);
+  }
+
   int idx = INT32_MAX;
-  if (p.best > -INFINITY) {
-    if (p.bvec) {
+  if (p.best == mx && mx > -INFINITY) {
+    if (p.bvec == 2) {
+      const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
+      const int head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(E));
+      const u32x4* vp = reinterpret_cast<const u32x4*>(row + head);
+#pragma unroll
+      for (int u = U - 1; u >= 0; --u) {
+        float f[N];
+        Elem<E>::decode(vp[p.bpos + u * NT], f);
+#pragma unroll
+        for (int k = N - 1; k >= 0; --k) idx = (f[k] == p.best) ? head + (p.bpos + u * NT) * N + k : idx;
+      }
+    } else if (p.bvec) {
       float f[N];
       Elem<E>::decode(*reinterpret_cast<const u32x4*>(row + p.bpos), f);
 #pragma unroll
@@ -134,15 +243,29 @@ __device__ __forceinline__ RowResult finish_row(const E* __restrict__ row, RowPa
       idx = p.bpos;
     }
   }
-  RowResult r;
-  r.max = block_reduce<NT>(p.best, MaxOp(), scr_f);
-  r.argmax = block_reduce<NT>(p.best == r.max ? idx : INT32_MAX, MinOp(), scr_i);
-  const float mref = block_reduce<NT>(p.mc, MaxOp(), scr_f);
   const double term = static_cast<double>(p.s0 + p.s1) *
                       exp2(static_cast<double>(p.mc) - static_cast<double>(mref));
-  const double s = block_reduce<NT>(term, SumOp(), scr_d);
-  r.lse = 0.69314718055994530942 * (static_cast<double>(mref) + log2(s));
-  r.rank = block_reduce<NT>(p.rank, SumOp(), scr_i);
+  idx = wave_reduce(idx, MinOp());
+  const double sw = wave_reduce(term, SumOp());
+  const int rk = kRank ? wave_reduce(p.rank, SumOp()) : 0;
+  if (lane == 0) {
+    s.i[w][0] = idx;
+    s.i[w][1] = rk;
+    s.d[w] = sw;
+  }
+  __syncthreads();
+  RowResult r;
+  r.max = mx;
+  r.argmax = s.i[0][0];
+  r.rank = s.i[0][1];
+  double sum = s.d[0];
+#pragma unroll
+  for (int k = 1; k < NW; ++k) {
+    r.argmax = min(r.argmax, s.i[k][0]);
+    r.rank += s.i[k][1];
+    sum += s.d[k];
+  }
+  r.lse = 0.69314718055994530942 * (static_cast<double>(mref) + log2(sum));
   return r;
 }
 

@@ -46,7 +46,7 @@ def test_status_strings_and_version(L):
 def test_workspace_bytes(L):
     assert L.vsv_workspace_bytes(0, 0, 0) >= 256
     b = L.vsv_workspace_bytes(128, 640, 0)
-    assert b % 256 == 0 and b >= 640 * 8
+    assert b % 256 == 0 and b >= 640 * 4
     assert L.vsv_workspace_bytes(-1, 5, 0) == 0
     assert L.vsv_workspace_bytes(128, 640, 1) >= b
 
