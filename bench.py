@@ -188,6 +188,9 @@ def main():
     print("[bench] %.2f us/step; per kernel %s us" % (ms * 1e3, ["%.2f" % (t * 1e3) for t in per_kernel_ms]),
           file=sys.stderr, flush=True)
 
+    slow = None
+    if wl.sampled:
+        slow = int(steps[0][0]._keep[2]["slow_rows"].item())  # rows sent to the exact path, summed over calls
     dom = max(range(ncall), key=lambda c: kernels[c][1])
     kname, kbytes = kernels[dom]
     kms = per_kernel_ms[dom]
@@ -203,7 +206,8 @@ def main():
         config=dict(workload=wl.name, config=args.config, B=wl.B, R=wl.R, D=wl.D, V=wl.V,
                     K=None if wl.config == 3 else int((wl.R - wl.B) // wl.B),
                     relaxed_topk=wl.relaxed_topk, sampled=bool(wl.sampled), input_copies=ncopy,
-                    bytes_per_step=step_bytes, data_seed=1000 + args.config, philox_seed=wl.seed),
+                    bytes_per_step=step_bytes, data_seed=1000 + args.config, philox_seed=wl.seed,
+                    slow_rows_first_copy=slow),
         roofline=dict(bound="hbm", kernel=kname, achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s",
                       frac=achieved / HBM_PEAK_GBPS, traffic=traffic, bytes_per_launch=kbytes,
                       launch_us=kms * 1e3),

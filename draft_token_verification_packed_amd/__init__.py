@@ -46,7 +46,7 @@ class Outputs(ctypes.Structure):
     _fields_ = [("accepted_len", ctypes.c_void_p), ("next_token", ctypes.c_void_p),
                 ("out_offsets", ctypes.c_void_p), ("out_tokens", ctypes.c_void_p),
                 ("row_token", ctypes.c_void_p), ("row_lse", ctypes.c_void_p),
-                ("error_flag", ctypes.c_void_p)]
+                ("error_flag", ctypes.c_void_p), ("slow_rows", ctypes.c_void_p)]
 
 
 SYMBOLS = ("vsv_workspace_bytes", "vsv_workspace_init", "vsv_verify_greedy", "vsv_verify_sampled",
@@ -159,11 +159,12 @@ def _prepare(logits, row_offsets, row_owner, draft_tokens, vocab):
                out_tokens=torch.full((max(R, 1),), -1, dtype=torch.int32, device=dev),
                row_token=torch.empty(R, dtype=torch.int32, device=dev),
                row_lse=torch.empty(R, dtype=torch.float32, device=dev),
-               error_flag=torch.zeros(1, dtype=torch.int32, device=dev))
+               error_flag=torch.zeros(1, dtype=torch.int32, device=dev),
+               slow_rows=torch.zeros(1, dtype=torch.int32, device=dev))
     batch = Batch(_ptr(logits), dtype, V, ld, B, R, _ptr(row_offsets), _ptr(row_owner),
                   _ptr(draft_tokens) if R - B > 0 else None)
     outs = Outputs(*[_ptr(out[k]) for k in ("accepted_len", "next_token", "out_offsets", "out_tokens",
-                                            "row_token", "row_lse", "error_flag")])
+                                            "row_token", "row_lse", "error_flag", "slow_rows")])
     return batch, outs, out, B, R
 
 
@@ -230,7 +231,7 @@ def prepare_greedy(logits, row_offsets, row_owner, draft_tokens, relaxed_topk=1,
     if out is not None:
         res = out
         outs = Outputs(*[_ptr(res[k]) for k in ("accepted_len", "next_token", "out_offsets", "out_tokens",
-                                                "row_token", "row_lse", "error_flag")])
+                                                "row_token", "row_lse", "error_flag", "slow_rows")])
     ws = workspace(B, R, False, logits.device, stream) if ws is None else ws
     args = (ctypes.byref(batch), int(relaxed_topk), ctypes.byref(outs), _ptr(ws), ws.numel(), _stream(stream))
     return PreparedCall(lib().vsv_verify_greedy, args, (batch, outs, res, ws, logits)), res
@@ -242,7 +243,7 @@ def prepare_sampled(logits, row_offsets, row_owner, draft_tokens, temperature, t
     if out is not None:
         res = out
         outs = Outputs(*[_ptr(res[k]) for k in ("accepted_len", "next_token", "out_offsets", "out_tokens",
-                                                "row_token", "row_lse", "error_flag")])
+                                                "row_token", "row_lse", "error_flag", "slow_rows")])
     for t, dt, name in ((temperature, torch.float32, "temperature"), (top_k, torch.int32, "top_k"),
                         (top_p, torch.float32, "top_p"), (min_p, torch.float32, "min_p")):
         _vec(t, B, dt, name)

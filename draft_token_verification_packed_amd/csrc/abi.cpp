@@ -55,9 +55,9 @@ vsv_status prepare(const vsv_batch* b, const vsv_outputs* o, void* ws, size_t ws
   v.row_token = o->row_token;
   v.row_lse = o->row_lse;
   v.error_flag = o->error_flag;
+  v.slow_rows = o->slow_rows;
   char* w = static_cast<char*>(ws);
   v.ws_ticket = reinterpret_cast<int32_t*>(w);
-  v.ws_stats = reinterpret_cast<int32_t*>(w) + 16;
   w += vsv::kWsAlign;
   v.ws_row = reinterpret_cast<uint32_t*>(w);
   return VSV_OK;
@@ -103,9 +103,7 @@ vsv_status vsv_verify_sampled(const vsv_batch* batch, const float* temperature, 
   a.min_p = min_p;
   a.seed = seed;
   a.offset = offset;
-  const hipError_t e = vsv::launch_verify_sampled(a, stream);
-  if (e == hipErrorNotSupported) return VSV_EUNSUPPORTED;
-  return e == hipSuccess ? VSV_OK : VSV_EHIP;
+  return vsv::launch_verify_sampled(a, stream) == hipSuccess ? VSV_OK : VSV_EHIP;
 }
 
 vsv_status vsv_draft_confidence(const void* draft_logits, int32_t dtype, int32_t vocab, int64_t ld,

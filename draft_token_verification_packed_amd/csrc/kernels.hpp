@@ -41,10 +41,10 @@ struct VerifyArgs {
   int32_t* row_token;
   float* row_lse;
   int32_t* error_flag;
+  int32_t* slow_rows;
   // workspace
   int32_t* ws_ticket;   // finished-row counter
   uint32_t* ws_row;     // [R] emitted token of the row | 0x80000000 if its draft was accepted
-  int32_t* ws_stats;    // [4] diagnostics (rows that took the slow path)
 };
 
 struct ConfidenceArgs {

@@ -7,9 +7,11 @@
 // index order. Per group of U vectors it takes the group max (v_max3 chains)
 // and remembers the first group whose max beats its running best; only the
 // thread holding the row maximum re-reads that group at the end to find the
-// exact lane. Every element adds exp2(x*c - mc) to one of two partial sums;
-// mc is a per-thread exponent reference that only moves when a value would
-// exceed it by 2^24, so the rescale branch is rare.
+// exact lane. Every element's exp2(x*c - mc) is summed in float32 within its
+// group (a short tree) and the group sums accumulate in float64; mc is a
+// per-thread exponent reference held at an integer (log2 units) just above
+// the thread's running max, so every rescale is an exact power of two and
+// the largest terms carry the smallest rounding.
 #pragma once
 
 #include "device.hpp"
@@ -22,8 +24,8 @@ struct RowPartial {
   int bvec;     // 0: bpos is its element index; 1: bpos is the element index
                 // of the 16-byte vector holding it; 2: bpos is the vector
                 // index of the first vector of the thread's group holding it
-  float mc;     // exponent reference (log2 domain)
-  float s0, s1; // sum of exp2(x*c - mc)
+  float mc;     // exponent reference (log2 domain, integer-valued once set)
+  double s;     // sum of exp2(x*c - mc)
   int rank;     // elements ordered before token d (relaxed acceptance)
 };
 
@@ -32,6 +34,8 @@ struct RowResult {
   int argmax;    // lowest index attaining it (INT32_MAX if no finite value)
   double lse;    // log(sum exp(x * c * ln2)) in natural units
   int rank;      // number of elements ordered before d
+  double sum;    // sum of exp2(x * c - mref)
+  float mref;    // exponent reference of `sum`
 };
 
 // LDS for finish_row: one slot per wave per reduced quantity.
@@ -46,17 +50,30 @@ __device__ __forceinline__ void partial_init(RowPartial& p) {
   p.bpos = INT32_MAX;
   p.bvec = 0;
   p.mc = -FLT_MAX;
-  p.s0 = 0.f;
-  p.s1 = 0.f;
+  p.s = 0.0;
   p.rank = 0;
 }
 
-__device__ __forceinline__ void partial_rescale(RowPartial& p, float vmax, float c) {
-  const float nm = vmax * c;
-  const float sc = fast_exp2(p.mc - nm);
-  p.s0 *= sc;
-  p.s1 *= sc;
-  p.mc = nm;
+// Raise the reference to ceil(vmax * c) if vmax * c exceeds it; the sum is
+// rescaled by an exact power of two. Non-finite maxima leave it alone (such
+// rows are flagged).
+__device__ __forceinline__ void partial_rebase(RowPartial& p, float vmax, float c) {
+  const float y = vmax * c;
+  if (y > p.mc && y < FLT_MAX) {
+    const float nm = ceilf(y);
+    p.s = (p.mc > -FLT_MAX) ? ldexp(p.s, static_cast<int>(fmaxf(p.mc - nm, -2000.f))) : 0.0;
+    p.mc = nm;
+  }
+}
+
+// Pairwise sum of n (a power of two) floats.
+template <int n>
+__device__ __forceinline__ float tree_sum(float* e) {
+#pragma unroll
+  for (int w = n / 2; w >= 1; w /= 2)
+#pragma unroll
+    for (int k = 0; k < w; ++k) e[k] = e[k] + e[k + w];
+  return e[0];
 }
 
 template <bool kRank>
@@ -66,8 +83,8 @@ __device__ __forceinline__ void take_scalar(RowPartial& p, float x, int e, float
     p.bpos = e;
     p.bvec = 0;
   }
-  if (fmaf(x, c, -p.mc) > 24.0f) partial_rescale(p, x, c);
-  p.s0 += fast_exp2(fmaf(x, c, -p.mc));
+  partial_rebase(p, x, c);
+  p.s += static_cast<double>(fast_exp2(fmaf(x, c, -p.mc)));
   if (kRank) p.rank += (x > xd || (x == xd && e < d)) ? 1 : 0;
 }
 
@@ -92,13 +109,12 @@ __device__ __forceinline__ void take_vector(RowPartial& p, const u32x4& w, int e
   p.best = gt ? vmax : p.best;
   p.bpos = gt ? e0 : p.bpos;
   p.bvec = gt ? 1 : p.bvec;
-  if (fmaf(vmax, c, -p.mc) > 24.0f) partial_rescale(p, vmax, c);
+  partial_rebase(p, vmax, c);
   const float nmc = -p.mc;
+  float e[N];
 #pragma unroll
-  for (int k = 0; k < N; k += 2) {
-    p.s0 += fast_exp2(fmaf(f[k], c, nmc));
-    p.s1 += fast_exp2(fmaf(f[k + 1], c, nmc));
-  }
+  for (int k = 0; k < N; ++k) e[k] = fast_exp2(fmaf(f[k], c, nmc));
+  p.s += static_cast<double>(tree_sum<N>(e));
   if (kRank) {
     if (vmax >= xd) {
 #pragma unroll
@@ -107,9 +123,15 @@ __device__ __forceinline__ void take_vector(RowPartial& p, const u32x4& w, int e
   }
 }
 
+struct NoCapture {
+  __device__ __forceinline__ void operator()(int, float) const {}
+};
+
 // A group of U vectors of one thread: one best/rescale update for the group.
-template <typename E, int U, int NT, bool kRank>
-__device__ __forceinline__ void take_group(RowPartial& p, const u32x4* w, int v, int head, float c, float xd, int d) {
+// `cap(u, vmax)` sees each vector's max before the exponentials are summed.
+template <typename E, int U, int NT, bool kRank, typename Cap = NoCapture>
+__device__ __forceinline__ void take_group(RowPartial& p, const u32x4* w, int v, int head, float c, float xd, int d,
+                                           Cap cap = Cap()) {
   constexpr int N = Elem<E>::kVec;
   float f[U][N];
   float vmx[U];
@@ -119,19 +141,22 @@ __device__ __forceinline__ void take_group(RowPartial& p, const u32x4* w, int v,
     vmx[u] = vec_max<E>(w[u], f[u]);
     gmax = fmaxf(gmax, vmx[u]);
   }
+#pragma unroll
+  for (int u = 0; u < U; ++u) cap(u, vmx[u]);
   const bool gt = gmax > p.best;
   p.best = gt ? gmax : p.best;
   p.bpos = gt ? v : p.bpos;      // group: first vector index
   p.bvec = gt ? 2 : p.bvec;
-  if (fmaf(gmax, c, -p.mc) > 24.0f) partial_rescale(p, gmax, c);
+  partial_rebase(p, gmax, c);
   const float nmc = -p.mc;
+  float e[U * N];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int k = 0; k < N; ++k) e[u * N + k] = fast_exp2(fmaf(f[u][k], c, nmc));
+  p.s += static_cast<double>(tree_sum<U * N>(e));
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-#pragma unroll
-    for (int k = 0; k < N; k += 2) {
-      p.s0 += fast_exp2(fmaf(f[u][k], c, nmc));
-      p.s1 += fast_exp2(fmaf(f[u][k + 1], c, nmc));
-    }
     if (kRank) {
       const int e0 = head + (v + u * NT) * N;
       if (vmx[u] >= xd) {
@@ -200,7 +225,7 @@ __device__ __forceinline__ void stream_row(const E* __restrict__ row, int V, flo
 // Combine the block's partials in two rounds (max and exponent reference;
 // then arg-max index, sum and rank). Every thread receives the result. `row`
 // is the streamed row: the thread holding the maximum re-reads its group.
-template <typename E, int NT, int U, bool kRank>
+template <typename E, int NT, int U, bool kRank, bool kArgmax = true>
 __device__ __forceinline__ RowResult finish_row(RowPartial& p, RowScratch<NT>& s, const E* __restrict__ row) {
   constexpr int N = Elem<E>::kVec;
   constexpr int NW = NT / kWave;
@@ -222,7 +247,7 @@ __device__ __forceinline__ RowResult finish_row(RowPartial& p, RowScratch<NT>& s
   }
 
   int idx = INT32_MAX;
-  if (p.best == mx && mx > -INFINITY) {
+  if (kArgmax && p.best == mx && mx > -INFINITY) {
     if (p.bvec == 2) {
       const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
       const int head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(E));
@@ -243,8 +268,8 @@ __device__ __forceinline__ RowResult finish_row(RowPartial& p, RowScratch<NT>& s
       idx = p.bpos;
     }
   }
-  const double term = static_cast<double>(p.s0 + p.s1) *
-                      exp2(static_cast<double>(p.mc) - static_cast<double>(mref));
+  // both references are integers (or -FLT_MAX for a thread that saw nothing)
+  const double term = (p.mc > -FLT_MAX) ? ldexp(p.s, static_cast<int>(fmaxf(p.mc - mref, -2000.f))) : 0.0;
   idx = wave_reduce(idx, MinOp());
   const double sw = wave_reduce(term, SumOp());
   const int rk = kRank ? wave_reduce(p.rank, SumOp()) : 0;
@@ -266,6 +291,8 @@ __device__ __forceinline__ RowResult finish_row(RowPartial& p, RowScratch<NT>& s
     sum += s.d[k];
   }
   r.lse = 0.69314718055994530942 * (static_cast<double>(mref) + log2(sum));
+  r.sum = sum;
+  r.mref = mref;
   return r;
 }
 

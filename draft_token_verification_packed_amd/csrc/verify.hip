@@ -11,9 +11,7 @@
 // speculative inference", DSpark section "Launch example").
 #include "kernels.hpp"
 #include "row_stream.hpp"
-#if VSV_HAVE_SAMPLED
 #include "sampled_row.hpp"
-#endif
 
 namespace vsv {
 
@@ -107,9 +105,8 @@ __device__ void batch_tail(const VerifyArgs& a, TailScratch& t) {
 
 // Publish this row's word and, if this is the last row, run the tail.
 template <int NT>
-__device__ __forceinline__ void publish_and_maybe_tail(const VerifyArgs& a, int r, uint32_t word) {
+__device__ __forceinline__ void publish_and_maybe_tail(const VerifyArgs& a, int r, uint32_t word, TailScratch& tail) {
   __shared__ int s_last;
-  __shared__ TailScratch tail;
   if (threadIdx.x == 0) {
     store_agent(a.ws_row + r, word);
     wait_memory();
@@ -139,6 +136,7 @@ __device__ __forceinline__ uint32_t row_word(const VerifyArgs& a, const RowMeta&
 template <typename E, int NT, int U, bool kRelaxed>
 __global__ __launch_bounds__(NT) void verify_greedy_kernel(VerifyArgs a) {
   __shared__ RowScratch<NT> scr;
+  __shared__ TailScratch tail;
   const int r = blockIdx.x;
   const E* __restrict__ row = static_cast<const E*>(a.logits) + static_cast<int64_t>(r) * a.ld;
   const int owner = a.owner[r];
@@ -172,7 +170,7 @@ __global__ __launch_bounds__(NT) void verify_greedy_kernel(VerifyArgs a) {
     if (a.row_token) a.row_token[r] = token;
     if (a.row_lse) a.row_lse[r] = static_cast<float>(res.lse);
   }
-  publish_and_maybe_tail<NT>(a, r, word);
+  publish_and_maybe_tail<NT>(a, r, word, tail);
 }
 
 template <typename E>
@@ -190,11 +188,58 @@ hipError_t launch_verify_greedy(const VerifyArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------- sampled
-#if VSV_HAVE_SAMPLED
-#include "verify_sampled.inc"
-#else
-hipError_t launch_verify_sampled(const VerifyArgs&, hipStream_t) { return hipErrorNotSupported; }
-#endif
+
+// Rows of requests with temperature > 0 draw their token (sampled_row.hpp);
+// rows of greedy requests take the arg-max exactly as verify_greedy does.
+// Acceptance is strict: the draft must equal the row's token.
+template <typename E, int NT, int U>
+__global__ __launch_bounds__(NT) void verify_sampled_kernel(VerifyArgs a) {
+  __shared__ SampledLds<NT> L;
+  static_assert(sizeof(TailScratch) <= sizeof(L.elem), "tail staging aliases the candidate buffers");
+  const int r = blockIdx.x;
+  const E* __restrict__ row = static_cast<const E*>(a.logits) + static_cast<int64_t>(r) * a.ld;
+  const RowMeta m = load_meta(a, r, a.owner[r]);
+  const float T = a.temperature[m.req < 0 ? 0 : m.req];
+  int token = 0, bits = 0, slow = 0;
+  double lse = 0.0;
+  if (m.req >= 0 && T > 0.f) {
+    const SampledOut o = sampled_row<E, NT, U>(a, row, m.req, m.j, T, L, NoHook());
+    token = o.token;
+    lse = o.lse;
+    bits = o.bits;
+    slow = o.slow;
+  } else {
+    RowPartial p;
+    partial_init(p);
+    constexpr float kLog2e = 1.4426950408889634f;
+    stream_row<E, NT, U, false>(row, a.V, kLog2e, INFINITY, 0, p);
+    const RowResult res = finish_row<E, NT, U, false>(p, L.rs, row);
+    token = res.argmax;
+    lse = res.lse;
+    if (!(res.max < INFINITY) || token == INT32_MAX || !isfinite(res.lse)) bits |= VSV_FLAG_LOGITS;
+    if (token == INT32_MAX) token = 0;
+    if (m.req >= 0 && !(T >= 0.f)) bits |= VSV_FLAG_PARAMS;
+  }
+  uint32_t word = 0;
+  if (threadIdx.x == 0) {
+    word = row_word(a, m, token, m.draft == token, bits);
+    if (bits) set_flag(a, bits);
+    if (slow && a.slow_rows) atomicAdd(a.slow_rows, 1);
+    if (a.row_token) a.row_token[r] = token;
+    if (a.row_lse) a.row_lse[r] = static_cast<float>(lse);
+  }
+  publish_and_maybe_tail<NT>(a, r, word, *reinterpret_cast<TailScratch*>(&L.elem[0][0]));
+}
+
+template <typename E>
+static hipError_t launch_sampled_t(const VerifyArgs& a, hipStream_t s) {
+  verify_sampled_kernel<E, kVerifyThreads, kUnroll><<<dim3(a.R), dim3(kVerifyThreads), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify_sampled(const VerifyArgs& a, hipStream_t s) {
+  return a.dtype == VSV_BF16 ? launch_sampled_t<uint16_t>(a, s) : launch_sampled_t<float>(a, s);
+}
 
 // ---------------------------------------------------------------- workspace
 

@@ -80,6 +80,9 @@ typedef struct {
   float* row_lse;        /* [R] or NULL: log-sum-exp of the logits the row uses:     */
                          /* x for greedy rows, x / T for sampled rows                */
   int32_t* error_flag;   /* [1] or NULL: sticky VSV_FLAG_* bits                      */
+  int32_t* slow_rows;    /* [1] or NULL: incremented once per sampled row whose     */
+                         /* draw needed the exact whole-row path (the row is read  */
+                         /* again); diagnostics only, results are identical        */
 } vsv_outputs;
 
 /* Bytes of device workspace a verify call needs (B requests, R rows).

@@ -331,7 +331,10 @@ def sampled_row_margins(x, temperature, top_k, top_p, min_p, u):
     minp_margin = math.inf
     if min_p > 0.0:
         lm = math.log(min_p)
-        minp_margin = float(np.min(np.abs(z[S] - lm)))
+        # tokens equal to the maximum have z = 0 exactly on any machine
+        zs = z[S][x[S] < m]
+        if zs.size:
+            minp_margin = float(np.min(np.abs(zs - lm)))
         S = S[z[S] >= lm]
     c = np.cumsum(w[S])
     cn = c / c[-1]

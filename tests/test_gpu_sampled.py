@@ -1,0 +1,168 @@
+"""GPU parity of sampled (and mixed greedy/sampled) verification.
+
+Rows are drawn with a tie margin (tests/workloads.py) so that no decision
+hinges on rounding; tokens, accepted lengths and compacted outputs must be
+bit-exact, log-sum-exp within 1e-5 relative."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.workloads import (assert_lse_close, assert_same, cuda_or_skip, custom_sampled, host,
+                             oracle_custom, oracle_of, to_dev, upload, with_margins)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def vsv():
+    cuda_or_skip()
+    import draft_token_verification_packed_amd as m
+    m.lib()
+    return m
+
+
+def run_sampled(vsv, wl, d=None):
+    import torch
+    d = upload(wl) if d is None else d
+    out = vsv.verify_sampled(d["logits"], d["offsets"], d["owner"], d["drafts"], d["temperature"],
+                             d["top_k"], d["top_p"], d["min_p"], wl.seed, wl.offset, vocab=wl.V)
+    torch.cuda.synchronize()
+    return out
+
+
+def run_custom(vsv, b):
+    import torch
+    t = to_dev(b["store"])[:, b["shift"]:]
+    out = vsv.verify_sampled(t, to_dev(b["offsets"]), to_dev(b["owner"]), to_dev(b["drafts"]), to_dev(b["T"]),
+                             to_dev(b["TK"]), to_dev(b["TP"]), to_dev(b["MP"]), b["seed"], b["offset"],
+                             vocab=b["V"])
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("B", [16, 128])
+def test_c3_ragged_sampled(vsv, B):
+    wl = with_margins(synth.make(3, B=B))
+    out = run_sampled(vsv, wl)
+    assert_same(out, oracle_of(wl))
+
+
+@pytest.mark.parametrize("B", [8, 48])
+def test_c5_large_mixed(vsv, B):
+    wl = with_margins(synth.make(5, B=B))
+    out = run_sampled(vsv, wl)
+    ref = oracle_of(wl)
+    assert_same(out, ref)
+    # the exact whole-row path is for rare rows only at this shape
+    sampled_rows = int(sum(int(wl.offsets[i + 1] - wl.offsets[i]) for i in range(wl.B) if wl.temperature[i] > 0))
+    assert int(host(out["slow_rows"])[0]) <= max(1, sampled_rows // 20)
+
+
+def test_c5_full_size_sampled_requests(vsv):
+    """Full C5 batch on the GPU; 24 requests re-checked one by one."""
+    wl = synth.make(5)
+    rng = np.random.default_rng(55)
+    check = sorted(rng.choice(wl.B, size=24, replace=False).tolist())
+    rows = [r for i in check for r in range(int(wl.offsets[i]), int(wl.offsets[i + 1]))]
+    from tests.workloads import margin_rows
+    for _ in range(20):
+        bad = margin_rows(wl, rows)
+        if not bad:
+            break
+        synth.redraw_rows(wl, bad)
+    out = run_sampled(vsv, wl)
+    acc, nxt, rt = host(out["accepted_len"]), host(out["next_token"]), host(out["row_token"])
+    offs, toks, lse = host(out["out_offsets"]), host(out["out_tokens"]), host(out["row_lse"])
+    for i in check:
+        r0, r1 = int(wl.offsets[i]), int(wl.offsets[i + 1])
+        sub = wl.logits[r0:r1]
+        us = {(0, j): oracle.row_uniform(wl.seed, i, j, wl.offset) for j in range(r1 - r0)}
+        ref = oracle.verify_sampled(sub, wl.dtype, wl.V, np.array([0, r1 - r0]), None,
+                                    wl.drafts[r0 - i:r1 - i - 1], wl.temperature[i:i + 1], wl.top_k[i:i + 1],
+                                    wl.top_p[i:i + 1], wl.min_p[i:i + 1], wl.seed, wl.offset, uniforms=us)
+        assert acc[i] == ref["accepted_len"][0]
+        assert nxt[i] == ref["next_token"][0]
+        assert np.array_equal(rt[r0:r1], ref["row_token"])
+        assert_lse_close(lse[r0:r1], ref["row_lse"])
+        n = int(ref["out_offsets"][1])
+        assert np.array_equal(toks[offs[i]:offs[i] + n], ref["out_tokens"])
+    assert int(offs[-1]) == int(acc.sum()) + wl.B
+    assert int(host(out["error_flag"])[0]) == 0
+
+
+def test_temperature_zero_is_greedy(vsv):
+    import torch
+    wl = synth.make(5, B=16)
+    d = upload(wl)
+    z = torch.zeros_like(d["temperature"])
+    s = vsv.verify_sampled(d["logits"], d["offsets"], d["owner"], d["drafts"], z, d["top_k"], d["top_p"],
+                           d["min_p"], wl.seed)
+    g = vsv.verify_greedy(d["logits"], d["offsets"], d["owner"], d["drafts"])
+    torch.cuda.synchronize()
+    for k in ("accepted_len", "next_token", "out_offsets", "row_token"):
+        assert np.array_equal(host(s[k]), host(g[k])), k
+    assert np.array_equal(host(s["row_lse"]), host(g["row_lse"]))
+    ref = oracle.verify_greedy(wl.logits, wl.dtype, wl.V, wl.offsets, wl.owner, wl.drafts)
+    assert_same(s, ref)
+
+
+GRID = [
+    (1.0, 0, 1.0, 0.0), (0.5, 50, 0.9, 0.05), (1.0, 50, 0.9, 0.05), (0.7, 0, 0.95, 0.0), (1.3, 7, 1.0, 0.0),
+    (0.8, 0, 0.6, 0.0), (1.0, 0, 1.0, 0.2), (0.6, 3, 0.5, 0.3), (2.0, 0, 0.9, 0.0), (1.0, 1, 1.0, 0.0),
+    (1.0, 0, 1e-6, 0.0), (1.0, 0, 1.0, 1.0), (0.05, 0, 1.0, 0.0), (0.0, 5, 0.5, 0.1), (1.5, 200, 0.99, 0.01),
+    (0.9, 0, 1.0, 0.01),
+]
+
+
+@pytest.mark.parametrize("V,dtype", [(152064, oracle.BF16), (152064, oracle.F32), (4099, oracle.BF16),
+                                     (33, oracle.F32), (1, oracle.BF16)])
+def test_filter_grid(vsv, V, dtype):
+    rng = np.random.default_rng(V + dtype)
+    b = custom_sampled(rng, len(GRID), 3, V, dtype, lambda i: GRID[i], seed=77 + V, offset=5)
+    out = run_custom(vsv, b)
+    assert_same(out, oracle_custom(b))
+
+
+@pytest.mark.parametrize("dtype", [oracle.F32, oracle.BF16])
+def test_ties_and_misaligned_rows(vsv, dtype):
+    rng = np.random.default_rng(321 + dtype)
+    b = custom_sampled(rng, len(GRID), 2, 5000, dtype, lambda i: GRID[i], seed=9, ties=True, ld=5003, shift=1)
+    # (ties: 81 distinct values, so top-k cuts cross tie groups)
+    out = run_custom(vsv, b)
+    assert_same(out, oracle_custom(b))
+
+
+def test_exact_whole_row_path(vsv):
+    """Unfiltered sampling over a flat distribution: the draw usually lies
+    beyond the captured candidates and the exact path decides."""
+    rng = np.random.default_rng(2024)
+    b = custom_sampled(rng, 6, 2, 152064, oracle.BF16, lambda i: (1.5, 0, 1.0, 0.0), seed=3, sigma=1.0)
+    out = run_custom(vsv, b)
+    assert_same(out, oracle_custom(b))
+    assert int(host(out["slow_rows"])[0]) > 0
+
+
+def test_invalid_parameters_are_flagged(vsv):
+    import torch
+    wl = synth.make(5, B=4, V=1000)
+    d = upload(wl)
+    T = d["temperature"].clone()
+    T[1] = -1.0
+    tp = d["top_p"].clone()
+    tp[3] = 1.5
+    out = vsv.verify_sampled(d["logits"], d["offsets"], d["owner"], d["drafts"], T, d["top_k"], tp, d["min_p"],
+                             wl.seed)
+    torch.cuda.synchronize()
+    assert int(host(out["error_flag"])[0]) & vsv.FLAG_PARAMS
+
+
+def test_c5_draft_confidence(vsv):
+    import torch
+    wl = synth.make(5, B=16)
+    d = upload(wl)
+    conf, lse, flag = vsv.draft_confidence(d["draft_logits"], d["selected"])
+    torch.cuda.synchronize()
+    rc, rl = oracle.draft_confidence(wl.draft_logits, wl.dtype, wl.V, wl.selected)
+    assert_lse_close(host(lse), rl)
+    np.testing.assert_allclose(host(conf), rc, rtol=1e-5, atol=0)
