@@ -100,6 +100,7 @@ struct WaveCap {
   float tau;     // effective threshold, max(tau_w, running max - window)
   float dcap;    // capture window (x units)
   int ovf;       // the buffer could not hold the wave's candidates
+  int kmin;      // compaction never keeps fewer candidates than this
 };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
@@ -145,10 +146,14 @@ __device__ bool wave_compact(SampledLds<NT>& L, WaveCap& s, int target) {
   const int before = s.elem_n;
   wave_filter<NT>(L, s);
   if (s.elem_n <= target) return s.elem_n < before;
-  float hi = -INFINITY;
-  for (int q = lane; q < s.elem_n; q += kWave) hi = fmaxf(hi, buf[q].x);
+  // histogram range: the buffer's own values (the threshold may be far below)
+  float hi = -INFINITY, lo = INFINITY;
+  for (int q = lane; q < s.elem_n; q += kWave) {
+    hi = fmaxf(hi, buf[q].x);
+    lo = fminf(lo, buf[q].x);
+  }
   hi = uni(wave_reduce(hi, MaxOp()));
-  const float lo = s.tau;
+  lo = uni(wave_reduce(lo, MinOp()));
   if (!(hi > lo) || !(hi - lo < INFINITY)) return s.elem_n < before;
   const float inv = 64.0f / (hi - lo);
   L.whist[w][lane] = 0;
@@ -237,7 +242,7 @@ __device__ void wave_drain(SampledLds<NT>& L, WaveCap& s) {
     }
     // leave room for what is arriving; each round raises the threshold,
     // which also thins the arrivals
-    const int target = max(kEW / 8, min(kEW / 2, kEW - total));
+    const int target = max(s.kmin, max(kEW / 8, min(kEW / 2, kEW - total)));
     if (attempt == 7 || !wave_compact<NT>(L, s, target)) {
       s.ovf = 1;
       s.tau = INFINITY;  // stop capturing: this row goes to the exact path
@@ -272,7 +277,7 @@ __device__ __forceinline__ void wave_take_scalar(SampledLds<NT>& L, WaveCap& s, 
   const uint64_t bal = __ballot(take);
   if (bal == 0) return;
   const int n = __popcll(bal);
-  if (s.elem_n + n > kEW && !wave_compact<NT>(L, s, kEW / 2)) {
+  if (s.elem_n + n > kEW && !wave_compact<NT>(L, s, max(s.kmin, kEW / 2))) {
     s.ovf = 1;
     s.tau = INFINITY;
     return;
@@ -947,19 +952,25 @@ __device__ SampledOut sampled_row(const VerifyArgs& a, const E* __restrict__ row
   const double Td = static_cast<double>(T);
   const float c = 1.4426950408889634f / T;
 
-  // capture window: T * kZcap, or exactly the min-p cut when min-p alone filters
-  float dcap = T * kZcap;
+  // Capture window below the running max: T * kZcap (weights under e^-kZcap
+  // of the max's), or exactly the min-p cut when min-p alone filters. A
+  // top-k cut is a count, which an outlying max can push below any window,
+  // so top-k rows use no window: compaction alone raises their threshold and
+  // always keeps top_k + 32 candidates per wave (the union then holds the
+  // whole top-k set whenever top_k + 32 fits a wave's buffer).
   const bool tk = top_k > 0 && top_k < a.V;
+  float dcap = tk ? FLT_MAX : T * kZcap;
   if (min_p > 0.f && top_p >= 1.f && !tk) {
     const float dm = static_cast<float>(-Td * log(static_cast<double>(min_p))) * 1.0001f + 1e-6f;
     dcap = fminf(dcap, dm);
   }
   if (!(dcap < INFINITY)) dcap = FLT_MAX;
+  const int kmin = tk ? min(top_k + 32, kEW - 2 * kWave) : 0;
 
   const int w = wave_id();
   if (threadIdx.x == 0) L.mkey = INT32_MIN;
   __syncthreads();
-  WaveCap s{0, 0, -INFINITY, -INFINITY, dcap, 0};
+  WaveCap s{0, 0, -INFINITY, -INFINITY, dcap, 0, kmin};
 
   RowPartial p;
   partial_init(p);
