@@ -15,6 +15,20 @@ size_t elem_size(int32_t dtype) { return dtype == VSV_BF16 ? 2 : 4; }
 
 bool dtype_ok(int32_t dtype) { return dtype == VSV_F32 || dtype == VSV_BF16; }
 
+// Persistent workgroups for greedy verification: one per CU of the current
+// device (cached per device), at most kMaxGroups; 0 if the count is unknown.
+int persistent_groups() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
+  const int g = cus < vsv::kMaxGroups ? cus : vsv::kMaxGroups;
+  if (dev < 64) cached[dev] = g;
+  return g;
+}
+
 // Common checks of a batch and its outputs; fills the shared launch args.
 vsv_status prepare(const vsv_batch* b, const vsv_outputs* o, void* ws, size_t ws_bytes, int32_t sampled,
                    VerifyArgs* a, bool* empty) {
@@ -26,7 +40,7 @@ vsv_status prepare(const vsv_batch* b, const vsv_outputs* o, void* ws, size_t ws
     *empty = true;
     return VSV_OK;
   }
-  if (!dtype_ok(b->dtype) || b->vocab < 1 || b->ld < b->vocab) return VSV_EINVAL;
+  if (!dtype_ok(b->dtype) || b->vocab < 1 || b->vocab > vsv::kMaxVocab || b->ld < b->vocab) return VSV_EINVAL;
   if (!b->logits || !aligned(b->logits, elem_size(b->dtype))) return VSV_EINVAL;
   if (!b->row_offsets || !b->row_owner) return VSV_EINVAL;
   if (b->num_rows > b->num_requests && !b->draft_tokens) return VSV_EINVAL;
@@ -57,9 +71,10 @@ vsv_status prepare(const vsv_batch* b, const vsv_outputs* o, void* ws, size_t ws
   v.error_flag = o->error_flag;
   v.slow_rows = o->slow_rows;
   char* w = static_cast<char*>(ws);
-  v.ws_ticket = reinterpret_cast<int32_t*>(w);
-  w += vsv::kWsAlign;
-  v.ws_row = reinterpret_cast<uint32_t*>(w);
+  v.ws_epoch = reinterpret_cast<uint32_t*>(w);
+  v.ws_row = reinterpret_cast<uint64_t*>(w + vsv::kWsAlign);
+  v.ws_part = reinterpret_cast<uint64_t*>(w + vsv::kWsAlign + vsv::ws_row_bytes(b->num_rows));
+  v.groups = persistent_groups();
   return VSV_OK;
 }
 

@@ -20,12 +20,13 @@ __global__ __launch_bounds__(NT) void confidence_kernel(ConfidenceArgs a) {
   }
   RowPartial p;
   partial_init(p);
+  NoKeep nokeep;
   constexpr float kLog2e = 1.4426950408889634f;
-  stream_row<E, NT, U, false>(row, a.V, kLog2e, INFINITY, 0, p);
-  const RowResult res = finish_row<E, NT, U, false>(p, scr, row);
+  stream_row<E, NT, U, false>(row, a.V, kLog2e, INFINITY, 0, p, nokeep);
+  const RowResult res = finish_row<E, NT, U, false, false>(p, scr, nokeep, row, a.V);
   if (threadIdx.x == 0) {
     int bits = 0;
-    if (!(res.max < INFINITY) || res.argmax == INT32_MAX || !isfinite(res.lse)) bits |= VSV_FLAG_LOGITS;
+    if (!(res.max < INFINITY) || !(res.max > -INFINITY) || !isfinite(res.lse)) bits |= VSV_FLAG_LOGITS;
     double c;
     if (!a.selected) {
       c = exp(static_cast<double>(res.max) - res.lse);

@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace vsv {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -57,11 +59,9 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // ---------------------------------------------------------------- cross-workgroup data
 // Data one workgroup hands to another inside a launch moves only through
-// agent-scope relaxed atomics: on gfx950 these are sc1 accesses, coherent
-// across the XCDs' separate L2 caches, so no device-wide fence (an L2
-// write-back plus invalidate per workgroup) is needed. A writer waits for
-// its stores to be acknowledged before it bumps the ticket that publishes
-// them.
+// agent-scope relaxed atomic loads and stores: on gfx950 these are sc1
+// accesses, coherent across the XCDs' separate L2 caches, so no device-wide
+// fence (an L2 write-back plus invalidate per workgroup) is needed.
 
 __device__ __forceinline__ void store_agent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -69,15 +69,15 @@ __device__ __forceinline__ void store_agent(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
   return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ int ticket_agent(int* p) {
-  return __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_int_agent(int* p, int v) {
+// Wait until every memory access this wave issued has completed (on gfx950
+// stores are counted in vmcnt, so this includes their acknowledgement).
+__device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
+__device__ __forceinline__ void store_agent64(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Wait until every memory access this wave issued has completed (stores
-// acknowledged).
-__device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
+__device__ __forceinline__ uint64_t load_agent64(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // ---------------------------------------------------------------- reductions
 
@@ -111,6 +111,55 @@ struct MinOp {
 struct SumOp {
   template <typename T> __device__ __forceinline__ T operator()(T a, T b) const { return a + b; }
 };
+
+// Wave reductions without LDS: DPP row rotations (by 8, 4, 2, 1 lanes) give
+// every lane the value of its row of 16, and four lane reads combine the
+// rows. The result is uniform (every lane holds it).
+template <int CTRL>
+__device__ __forceinline__ int dpp_ror(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_all(T v, Op op) {
+  static_assert(sizeof(T) == 4, "32-bit values");
+  auto rot = [](T x, auto ctrl) {
+    const int b = dpp_ror<decltype(ctrl)::value>(__builtin_bit_cast(int, x));
+    return __builtin_bit_cast(T, b);
+  };
+  v = op(v, rot(v, std::integral_constant<int, 0x128>()));
+  v = op(v, rot(v, std::integral_constant<int, 0x124>()));
+  v = op(v, rot(v, std::integral_constant<int, 0x122>()));
+  v = op(v, rot(v, std::integral_constant<int, 0x121>()));
+  const int b = __builtin_bit_cast(int, v);
+  const T r0 = __builtin_bit_cast(T, __builtin_amdgcn_readlane(b, 0));
+  const T r1 = __builtin_bit_cast(T, __builtin_amdgcn_readlane(b, 16));
+  const T r2 = __builtin_bit_cast(T, __builtin_amdgcn_readlane(b, 32));
+  const T r3 = __builtin_bit_cast(T, __builtin_amdgcn_readlane(b, 48));
+  return op(op(r0, r1), op(r2, r3));
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  auto rot = [](double x, auto ctrl) {
+    const int2 h = __builtin_bit_cast(int2, x);
+    int2 o;
+    o.x = dpp_ror<decltype(ctrl)::value>(h.x);
+    o.y = dpp_ror<decltype(ctrl)::value>(h.y);
+    return __builtin_bit_cast(double, o);
+  };
+  v += rot(v, std::integral_constant<int, 0x128>());
+  v += rot(v, std::integral_constant<int, 0x124>());
+  v += rot(v, std::integral_constant<int, 0x122>());
+  v += rot(v, std::integral_constant<int, 0x121>());
+  const int2 h = __builtin_bit_cast(int2, v);
+  double r[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    int2 q;
+    q.x = __builtin_amdgcn_readlane(h.x, 16 * k);
+    q.y = __builtin_amdgcn_readlane(h.y, 16 * k);
+    r[k] = __builtin_bit_cast(double, q);
+  }
+  return (r[0] + r[1]) + (r[2] + r[3]);
+}
 
 // Inclusive prefix sum over a wave.
 __device__ __forceinline__ int wave_inclusive_scan(int v) {

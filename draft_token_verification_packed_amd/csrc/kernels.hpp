@@ -8,15 +8,30 @@
 
 namespace vsv {
 
-// Threads per row workgroup and 16-byte loads in flight per thread.
+// Threads per row workgroup, and 16-byte vectors per thread per group (the
+// loads of one group are in flight while the previous group is reduced). The
+// sampled stream carries the candidate capture and keeps smaller groups, so
+// its registers stay within two workgroups per CU.
 #ifndef VSV_VERIFY_THREADS
 #define VSV_VERIFY_THREADS 512
+#endif
+#ifndef VSV_GREEDY_THREADS
+#define VSV_GREEDY_THREADS 1024
+#endif
+#ifndef VSV_ROW_THREADS
+#define VSV_ROW_THREADS 256
 #endif
 #ifndef VSV_UNROLL
 #define VSV_UNROLL 2
 #endif
+#ifndef VSV_UNROLL_SAMPLED
+#define VSV_UNROLL_SAMPLED 2
+#endif
 constexpr int kVerifyThreads = VSV_VERIFY_THREADS;
+constexpr int kGreedyThreads = VSV_GREEDY_THREADS;
+constexpr int kRowThreads = VSV_ROW_THREADS;
 constexpr int kUnroll = VSV_UNROLL;
+constexpr int kUnrollSampled = VSV_UNROLL_SAMPLED;
 
 // Everything a verify launch needs, passed by value as the kernel argument.
 struct VerifyArgs {
@@ -27,6 +42,8 @@ struct VerifyArgs {
   const int32_t* owner;
   const int32_t* drafts;
   int32_t relaxed_k;
+  int32_t groups;       // greedy: persistent workgroups (one per CU)
+  int32_t cpr;          // greedy: chunks per row (set at launch)
   // sampled only
   const float* temperature;
   const int32_t* top_k;
@@ -42,9 +59,18 @@ struct VerifyArgs {
   float* row_lse;
   int32_t* error_flag;
   int32_t* slow_rows;
-  // workspace
-  int32_t* ws_ticket;   // finished-row counter
-  uint32_t* ws_row;     // [R] emitted token of the row | 0x80000000 if its draft was accepted
+  // workspace (zero before its first use). Words handed between workgroups
+  // carry the call's tag in their high half, so a call finds only its own
+  // and nothing has to be cleared afterwards:
+  //  ws_epoch [1] calls completed on this workspace; the call's tag is
+  //           derived from it and the last workgroup advances it
+  //  ws_row   [R] 64-bit words; a row handled by one workgroup stores the
+  //           token it emits | kAcceptBit if its draft was accepted
+  //  ws_part  [(R + kMaxGroups) * kPartWords] 64-bit words; slot r + p holds
+  //           the partial statistics persistent workgroup p gathered for row r
+  uint32_t* ws_epoch;
+  uint64_t* ws_row;
+  uint64_t* ws_part;
 };
 
 struct ConfidenceArgs {
@@ -57,13 +83,31 @@ struct ConfidenceArgs {
   int32_t* error_flag;
 };
 
+// Greedy verification runs one persistent workgroup per CU (at most
+// kMaxGroups). The batch's rows are cut into chunks of 64 * kUnroll 16-byte
+// vectors; each workgroup takes an equal contiguous range of the chunk list
+// and its waves pull chunks from it one at a time, so every CU and every wave
+// finishes at about the same moment however unevenly the memory system serves
+// them. A workgroup's range touches at most kMaxLocalRows rows; batches with
+// more rows per CU than that use one workgroup per row, which is then
+// balanced by itself.
+constexpr int kMaxGroups = 1024;
+constexpr int kMaxLocalRows = 32;
+constexpr int kPartWords = 6;   // best, index, exponent ref, sum, rank, row info
+inline bool greedy_persistent(int32_t R, int32_t groups) {
+  return groups > 0 && static_cast<int64_t>(R) <= static_cast<int64_t>(kMaxLocalRows - 1) * groups;
+}
+
 // Workspace layout (bytes, 256-aligned pieces).
 constexpr size_t kWsAlign = 256;
 inline size_t ws_align(size_t b) { return (b + kWsAlign - 1) / kWsAlign * kWsAlign; }
+inline size_t ws_row_bytes(int32_t R) { return ws_align(static_cast<size_t>(R > 0 ? R : 1) * 8); }
 inline size_t ws_bytes(int32_t B, int32_t R, int32_t /*sampled*/) {
   (void)B;
-  return kWsAlign + ws_align(static_cast<size_t>(R) * 4);
+  return kWsAlign + ws_row_bytes(R) + ws_align((static_cast<size_t>(R > 0 ? R : 0) + kMaxGroups) * kPartWords * 8);
 }
+// Tokens travel in the low 30 bits of a row word.
+constexpr int32_t kMaxVocab = 0x3FFFFFFF;
 
 hipError_t launch_verify_greedy(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_verify_sampled(const VerifyArgs& a, hipStream_t s);

@@ -5,13 +5,13 @@
 // Each thread walks 16-byte vectors tid, tid + NT, ... (a wave reads 1 KiB
 // contiguous per load instruction), so its own elements arrive in increasing
 // index order. Per group of U vectors it takes the group max (v_max3 chains)
-// and remembers the first group whose max beats its running best; only the
-// thread holding the row maximum re-reads that group at the end to find the
-// exact lane. Every element's exp2(x*c - mc) is summed in float32 within its
-// group (a short tree) and the group sums accumulate in float64; mc is a
-// per-thread exponent reference held at an integer (log2 units) just above
-// the thread's running max, so every rescale is an exact power of two and
-// the largest terms carry the smallest rounding.
+// and, when that max beats its running best, keeps the group's raw vectors in
+// registers, so the arg-max lane is found at the end without reading the row
+// again. Every element's exp2(x*c - mc) is summed in float32 within its group
+// (a short tree) and the group sums accumulate in float64; mc is a per-thread
+// exponent reference held at an integer (log2 units) just above the thread's
+// running max, so every rescale is an exact power of two and the largest
+// terms carry the smallest rounding.
 #pragma once
 
 #include "device.hpp"
@@ -24,6 +24,7 @@ struct RowPartial {
   int bvec;     // 0: bpos is its element index; 1: bpos is the element index
                 // of the 16-byte vector holding it; 2: bpos is the vector
                 // index of the first vector of the thread's group holding it
+                // (whose data the stream kept, see GroupKeep)
   float mc;     // exponent reference (log2 domain, integer-valued once set)
   double s;     // sum of exp2(x*c - mc)
   int rank;     // elements ordered before token d (relaxed acceptance)
@@ -38,11 +39,29 @@ struct RowResult {
   float mref;    // exponent reference of `sum`
 };
 
-// LDS for finish_row: one slot per wave per reduced quantity.
+// What finish_row combines across threads: the best value and its lowest
+// index, the exponent reference and the sum relative to it, the rank count.
+struct RowRed {
+  double s;
+  float best;
+  int idx;
+  float mc;
+  int rank;
+};
+
+// LDS for finish_row: one partial per wave.
 template <int NT> struct RowScratch {
-  float f[NT / kWave][2];
-  int i[NT / kWave][2];
-  double d[NT / kWave];
+  RowRed r[NT / kWave];
+};
+
+// Registers holding the raw vectors of the thread's best group (arg-max
+// rows), or nothing.
+struct NoKeep {
+  static constexpr bool kOn = false;
+};
+template <int U> struct GroupKeep {
+  static constexpr bool kOn = true;
+  u32x4 w[U];
 };
 
 __device__ __forceinline__ void partial_init(RowPartial& p) {
@@ -99,7 +118,7 @@ __device__ __forceinline__ float vec_max(const u32x4& w, float* f) {
   return vmax;
 }
 
-// A single vector (the predicated last group).
+// A single vector (the sampled stream's last group).
 template <typename E, bool kRank>
 __device__ __forceinline__ void take_vector(RowPartial& p, const u32x4& w, int e0, float c, float xd, int d) {
   constexpr int N = Elem<E>::kVec;
@@ -129,9 +148,13 @@ struct NoCapture {
 
 // A group of U vectors of one thread: one best/rescale update for the group.
 // `cap(u, vmax)` sees each vector's max before the exponentials are summed.
-template <typename E, int U, int NT, bool kRank, typename Cap = NoCapture>
+// kPartial: the group is a row's partial last one, and its vectors at or
+// beyond nvec (loaded duplicates or zeros) count as -inf; other groups carry
+// no masking code at all.
+template <typename E, int U, int NT, bool kRank, bool kPartial = false, typename Keep = NoKeep,
+          typename Cap = NoCapture>
 __device__ __forceinline__ void take_group(RowPartial& p, const u32x4* w, int v, int head, float c, float xd, int d,
-                                           Cap cap = Cap()) {
+                                           Keep& keep, int nvec = 0, Cap cap = Cap()) {
   constexpr int N = Elem<E>::kVec;
   float f[U][N];
   float vmx[U];
@@ -139,6 +162,11 @@ __device__ __forceinline__ void take_group(RowPartial& p, const u32x4* w, int v,
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     vmx[u] = vec_max<E>(w[u], f[u]);
+    if (kPartial && v + u * NT >= nvec) {
+      vmx[u] = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < N; ++k) f[u][k] = -INFINITY;
+    }
     gmax = fmaxf(gmax, vmx[u]);
   }
 #pragma unroll
@@ -147,6 +175,15 @@ __device__ __forceinline__ void take_group(RowPartial& p, const u32x4* w, int v,
   p.best = gt ? gmax : p.best;
   p.bpos = gt ? v : p.bpos;      // group: first vector index
   p.bvec = gt ? 2 : p.bvec;
+  if constexpr (Keep::kOn) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      keep.w[u].x = gt ? w[u].x : keep.w[u].x;
+      keep.w[u].y = gt ? w[u].y : keep.w[u].y;
+      keep.w[u].z = gt ? w[u].z : keep.w[u].z;
+      keep.w[u].w = gt ? w[u].w : keep.w[u].w;
+    }
+  }
   partial_rebase(p, gmax, c);
   const float nmc = -p.mc;
   float e[U * N];
@@ -159,7 +196,7 @@ __device__ __forceinline__ void take_group(RowPartial& p, const u32x4* w, int v,
   for (int u = 0; u < U; ++u) {
     if (kRank) {
       const int e0 = head + (v + u * NT) * N;
-      if (vmx[u] >= xd) {
+      if (vmx[u] >= xd && (!kPartial || v + u * NT < nvec)) {
 #pragma unroll
         for (int k = 0; k < N; ++k) p.rank += (f[u][k] > xd || (f[u][k] == xd && e0 + k < d)) ? 1 : 0;
       }
@@ -171,12 +208,26 @@ struct NoHook {
   __device__ __forceinline__ void operator()() const {}
 };
 
+// Issue the loads of group h: vectors h*U*NT + tid + u*NT, u < U. Addresses
+// are clamped to the row's last vector instead of predicated, so no load sits
+// behind a branch; the compiler can then count the loads in flight and wait
+// for exactly the group it reduces next (a predicated load makes it wait for
+// every load, including the prefetch just issued). Clamped duplicates are
+// never reduced. Requires nvec >= 1.
+template <int NT, int U>
+__device__ __forceinline__ void load_group(u32x4* dst, const u32x4* __restrict__ vp, int h, int nvec) {
+  const int base = h * (U * NT) + static_cast<int>(threadIdx.x);
+#pragma unroll
+  for (int u = 0; u < U; ++u) dst[u] = load_stream(vp + min(base + u * NT, nvec - 1));
+}
+
 // Stream row[0 .. V) into this thread's partial. c = log2(e) / T. `hook` runs
 // once, right after the first group's loads are issued, so loads it issues
-// overlap the stream instead of trailing it.
-template <typename E, int NT, int U, bool kRank, typename Hook = NoHook>
+// overlap the stream instead of trailing it. `keep` receives the thread's
+// best group (GroupKeep) or is ignored (NoKeep).
+template <typename E, int NT, int U, bool kRank, typename Keep = NoKeep, typename Hook = NoHook>
 __device__ __forceinline__ void stream_row(const E* __restrict__ row, int V, float c, float xd, int d,
-                                           RowPartial& p, Hook hook = Hook()) {
+                                           RowPartial& p, Keep& keep, Hook hook = Hook()) {
   constexpr int N = Elem<E>::kVec;
   const int tid = threadIdx.x;
   const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
@@ -184,116 +235,132 @@ __device__ __forceinline__ void stream_row(const E* __restrict__ row, int V, flo
   if (head > V) head = V;
   const int nvec = (V - head) / N;
   const int body_end = head + nvec * N;
-
   const u32x4* __restrict__ vp = reinterpret_cast<const u32x4*>(row + head);
-  // Groups of U vectors per thread, software-pipelined: the loads of group
-  // g + 1 are in flight while group g is reduced. Only the last group can be
-  // partial; its loads and updates are predicated on the vector index.
+
+  // Full groups of U vectors per thread, two buffers in turn: while one
+  // group is reduced the next one's loads are in flight. The group after the
+  // last full one is the partial group (possibly empty), reduced with its
+  // missing vectors masked.
   constexpr int G = U * NT;
-  const int ngroups = (nvec + G - 1) / G;
-  int v = tid;
-  u32x4 cur[U];
-  if (ngroups > 0) {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (ngroups > 1 || v + u * NT < nvec) cur[u] = load_stream(vp + v + u * NT);
-  }
-  hook();
-  if (tid < head) take_scalar<kRank>(p, Elem<E>::at(row, tid), tid, c, xd, d);
-  if (ngroups > 0) {
-    for (int g = 1; g < ngroups; ++g) {
-      u32x4 nxt[U];
-      const int vn = v + G;
-      const bool full = g + 1 < ngroups;
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (full || vn + u * NT < nvec) nxt[u] = load_stream(vp + vn + u * NT);
-      take_group<E, U, NT, kRank>(p, cur, v, head, c, xd, d);
-#pragma unroll
-      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
-      v = vn;
+  const int nfull = nvec / G;
+  if (nvec > 0) {
+    u32x4 a[U], b[U];
+    load_group<NT, U>(a, vp, 0, nvec);
+    hook();
+    int g = 0;
+    for (; g + 2 <= nfull; g += 2) {
+      load_group<NT, U>(b, vp, g + 1, nvec);
+      take_group<E, U, NT, kRank>(p, a, g * G + tid, head, c, xd, d, keep);
+      load_group<NT, U>(a, vp, g + 2, nvec);
+      take_group<E, U, NT, kRank>(p, b, (g + 1) * G + tid, head, c, xd, d, keep);
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (v + u * NT < nvec) take_vector<E, kRank>(p, cur[u], head + (v + u * NT) * N, c, xd, d);
+    if (g < nfull) {
+      load_group<NT, U>(b, vp, g + 1, nvec);
+      take_group<E, U, NT, kRank>(p, a, g * G + tid, head, c, xd, d, keep);
+      take_group<E, U, NT, kRank, true>(p, b, nfull * G + tid, head, c, xd, d, keep, nvec);
+    } else {
+      take_group<E, U, NT, kRank, true>(p, a, nfull * G + tid, head, c, xd, d, keep, nvec);
+    }
+  } else {
+    hook();
   }
 
+  if (tid < head) take_scalar<kRank>(p, Elem<E>::at(row, tid), tid, c, xd, d);
   const int tail = V - body_end;
   if (tid < tail) take_scalar<kRank>(p, Elem<E>::at(row, body_end + tid), body_end + tid, c, xd, d);
 }
 
-// Combine the block's partials in two rounds (max and exponent reference;
-// then arg-max index, sum and rank). Every thread receives the result. `row`
-// is the streamed row: the thread holding the maximum re-reads its group.
-template <typename E, int NT, int U, bool kRank, bool kArgmax = true>
-__device__ __forceinline__ RowResult finish_row(RowPartial& p, RowScratch<NT>& s, const E* __restrict__ row) {
+// Power-of-two rescale of a partial sum from reference mc to m >= mc (a
+// thread that saw nothing holds mc = -FLT_MAX and contributes 0).
+__device__ __forceinline__ double rebase_sum(double s, float mc, float m) {
+  return (mc > -FLT_MAX) ? ldexp(s, static_cast<int>(fmaxf(mc - m, -2000.f))) : 0.0;
+}
+
+__device__ __forceinline__ RowRed combine(const RowRed& a, const RowRed& b) {
+  RowRed r;
+  r.best = fmaxf(a.best, b.best);
+  r.idx = (a.best > b.best) ? a.idx : (b.best > a.best) ? b.idx : min(a.idx, b.idx);
+  r.mc = fmaxf(a.mc, b.mc);
+  r.s = rebase_sum(a.s, a.mc, r.mc) + rebase_sum(b.s, b.mc, r.mc);
+  r.rank = a.rank + b.rank;
+  return r;
+}
+
+// This thread's lowest index of its best value: the scalar position, or the
+// first match in the kept group (vectors bpos + u * STRIDE, u < U, of the
+// row's 16-byte-aligned body, which starts `head` elements in and holds
+// `nvec` vectors). INT32_MAX if the thread saw no finite value.
+template <typename E, int STRIDE, int U, typename Keep>
+__device__ __forceinline__ int lane_argmax(const RowPartial& p, const Keep& keep, int head, int nvec) {
+  static_assert(Keep::kOn, "the arg-max lane is found in the kept group");
+  constexpr int N = Elem<E>::kVec;
+  int idx = INT32_MAX;
+  if (p.best > -INFINITY) {
+    if (p.bvec == 2) {
+#pragma unroll
+      for (int u = U - 1; u >= 0; --u) {
+        const int q = p.bpos + u * STRIDE;
+        float f[N];
+        Elem<E>::decode(keep.w[u], f);
+#pragma unroll
+        for (int k = N - 1; k >= 0; --k) idx = (q < nvec && f[k] == p.best) ? head + q * N + k : idx;
+      }
+    } else {
+      idx = p.bpos;
+    }
+  }
+  return idx;
+}
+
+// The partial of a whole wave (every lane receives it; every lane must be
+// active): the largest value,
+// the lowest index holding it, every sum rebased to the largest exponent
+// reference and added, the rank counts added.
+template <bool kRank = true>
+__device__ __forceinline__ RowRed wave_red(const RowRed& r) {
+  RowRed o;
+  o.best = wave_all(r.best, MaxOp());
+  o.idx = wave_all(r.best == o.best ? r.idx : INT32_MAX, MinOp());
+  o.mc = wave_all(r.mc, MaxOp());
+  o.s = wave_sum_f64(rebase_sum(r.s, r.mc, o.mc));
+  o.rank = kRank ? wave_all(r.rank, SumOp()) : 0;
+  return o;
+}
+
+// Combine the block's partials in one round (wave shuffles, one LDS slot per
+// wave, one barrier). Every thread receives the result. With kArgmax, each
+// thread first finds the lowest index of its best value in the group `keep`
+// holds (or takes the scalar position); `row` and V locate that group.
+template <typename E, int NT, int U, bool kRank, bool kArgmax, typename Keep>
+__device__ __forceinline__ RowResult finish_row(const RowPartial& p, RowScratch<NT>& s, const Keep& keep,
+                                                const E* __restrict__ row, int V) {
   constexpr int N = Elem<E>::kVec;
   constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
 
-  const float m1 = wave_reduce(p.best, MaxOp());
-  const float m2 = wave_reduce(p.mc, MaxOp());
-  if (lane == 0) {
-    s.f[w][0] = m1;
-    s.f[w][1] = m2;
-  }
-  __syncthreads();
-  float mx = s.f[0][0], mref = s.f[0][1];
-#pragma unroll
-  for (int k = 1; k < NW; ++k) {
-    mx = fmaxf(mx, s.f[k][0]);
-    mref = fmaxf(mref, s.f[k][1]);
-  }
-
   int idx = INT32_MAX;
-  if (kArgmax && p.best == mx && mx > -INFINITY) {
-    if (p.bvec == 2) {
-      const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
-      const int head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(E));
-      const u32x4* vp = reinterpret_cast<const u32x4*>(row + head);
-#pragma unroll
-      for (int u = U - 1; u >= 0; --u) {
-        float f[N];
-        Elem<E>::decode(vp[p.bpos + u * NT], f);
-#pragma unroll
-        for (int k = N - 1; k >= 0; --k) idx = (f[k] == p.best) ? head + (p.bpos + u * NT) * N + k : idx;
-      }
-    } else if (p.bvec) {
-      float f[N];
-      Elem<E>::decode(*reinterpret_cast<const u32x4*>(row + p.bpos), f);
-#pragma unroll
-      for (int k = N - 1; k >= 0; --k) idx = (f[k] == p.best) ? p.bpos + k : idx;
-    } else {
-      idx = p.bpos;
-    }
+  if constexpr (kArgmax) {
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
+    int head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(E));
+    if (head > V) head = V;
+    idx = lane_argmax<E, NT, U>(p, keep, head, (V - head) / N);
   }
-  // both references are integers (or -FLT_MAX for a thread that saw nothing)
-  const double term = (p.mc > -FLT_MAX) ? ldexp(p.s, static_cast<int>(fmaxf(p.mc - mref, -2000.f))) : 0.0;
-  idx = wave_reduce(idx, MinOp());
-  const double sw = wave_reduce(term, SumOp());
-  const int rk = kRank ? wave_reduce(p.rank, SumOp()) : 0;
-  if (lane == 0) {
-    s.i[w][0] = idx;
-    s.i[w][1] = rk;
-    s.d[w] = sw;
-  }
+  RowRed r = wave_red<kRank>(RowRed{p.s, p.best, idx, p.mc, kRank ? p.rank : 0});
+  if (lane == 0) s.r[w] = r;
   __syncthreads();
-  RowResult r;
-  r.max = mx;
-  r.argmax = s.i[0][0];
-  r.rank = s.i[0][1];
-  double sum = s.d[0];
+  r = s.r[0];
 #pragma unroll
-  for (int k = 1; k < NW; ++k) {
-    r.argmax = min(r.argmax, s.i[k][0]);
-    r.rank += s.i[k][1];
-    sum += s.d[k];
-  }
-  r.lse = 0.69314718055994530942 * (static_cast<double>(mref) + log2(sum));
-  r.sum = sum;
-  r.mref = mref;
-  return r;
+  for (int k = 1; k < NW; ++k) r = combine(r, s.r[k]);
+
+  RowResult out;
+  out.max = r.best;
+  out.argmax = r.idx;
+  out.rank = r.rank;
+  out.sum = r.s;
+  out.mref = r.mc;
+  out.lse = 0.69314718055994530942 * (static_cast<double>(r.mc) + log2(r.s));
+  return out;
 }
 
 }  // namespace vsv

@@ -858,25 +858,29 @@ __device__ void stream_sampled(const E* __restrict__ row, int V, float c, RowPar
   const int nvec = (V - head) / N;
   const int body_end = head + nvec * N;
   const u32x4* __restrict__ vp = reinterpret_cast<const u32x4*>(row + head);
+  // One buffer plus the next group's loads: the next group is in flight
+  // while the current one is reduced and captured (loads are unconditional,
+  // load_group in row_stream.hpp). A second full buffer would double the
+  // inlined capture code and its registers.
   constexpr int G = U * NT;
-  const int ngroups = (nvec + G - 1) / G;
-  int v = tid;
+  const int nfull = nvec / G;
+  NoKeep nokeep;
+
+  // head elements first: a load issued after the groups' would make the
+  // first wait cover the prefetch too
+  const bool has_head = tid < head;
+  const float xh = has_head ? Elem<E>::at(row, tid) : -INFINITY;
   u32x4 cur[U];
-  if (ngroups > 0) {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (ngroups > 1 || v + u * NT < nvec) cur[u] = load_stream(vp + v + u * NT);
-  }
+  if (nvec > 0) load_group<NT, U>(cur, vp, 0, nvec);
   hook();
 
   // Starting threshold: the wave's max over its first group (and head).
   {
-    float m0 = -INFINITY;
-    if (tid < head) m0 = Elem<E>::at(row, tid);
-    if (ngroups > 0) {
+    float m0 = xh;
+    if (nvec > 0) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        if (ngroups > 1 || v + u * NT < nvec) {
+        if (tid + u * NT < nvec) {
           float f[N];
           m0 = fmaxf(m0, vec_max<E>(cur[u], f));
         }
@@ -884,38 +888,32 @@ __device__ void stream_sampled(const E* __restrict__ row, int V, float c, RowPar
     }
     wave_sync_max<NT>(L, s, m0);
   }
-
-  const bool has_head = tid < head;
-  const float xh = has_head ? Elem<E>::at(row, tid) : -INFINITY;
   if (has_head) take_scalar<false>(p, xh, tid, c, INFINITY, 0);
   wave_take_scalar<NT>(L, s, xh, tid, has_head);
 
-  if (ngroups > 0) {
-    for (int g = 1; g < ngroups; ++g) {
+  if (nvec > 0) {
+    for (int g = 0; g < nfull; ++g) {
       u32x4 nxt[U];
-      const int vn = v + G;
-      const bool full = g + 1 < ngroups;
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (full || vn + u * NT < nvec) nxt[u] = load_stream(vp + vn + u * NT);
-      take_group<E, U, NT, false>(p, cur, v, head, c, INFINITY, 0, [&](int u, float vmax) {
+      load_group<NT, U>(nxt, vp, g + 1, nvec);
+      const int v = g * G + tid;
+      take_group<E, U, NT, false>(p, cur, v, head, c, INFINITY, 0, nokeep, 0, [&](int u, float vmax) {
         wave_park<E, NT>(L, s, cur[u], head + (v + u * NT) * N, vmax, true);
       });
       if ((g & 3) == 0) wave_sync_max<NT>(L, s, p.best);
 #pragma unroll
       for (int u = 0; u < U; ++u) cur[u] = nxt[u];
-      v = vn;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool valid = v + u * NT < nvec;
+      const int q = nfull * G + tid + u * NT;
+      const bool valid = q < nvec;
       float f[N];
       float vmax = -INFINITY;
       if (valid) {
         vmax = vec_max<E>(cur[u], f);
-        take_vector<E, false>(p, cur[u], head + (v + u * NT) * N, c, INFINITY, 0);
+        take_vector<E, false>(p, cur[u], head + q * N, c, INFINITY, 0);
       }
-      wave_park<E, NT>(L, s, cur[u], head + (v + u * NT) * N, vmax, valid);
+      wave_park<E, NT>(L, s, cur[u], head + q * N, vmax, valid);
     }
   }
 
@@ -938,7 +936,7 @@ struct SampledOut {
 // One workgroup samples row `row` of request `req` (local row j) at
 // temperature T > 0. `hook` is forwarded to the stream.
 template <typename E, int NT, int U, typename Hook>
-__device__ SampledOut sampled_row(const VerifyArgs& a, const E* __restrict__ row, int req, int j, float T,
+__device__ __forceinline__ SampledOut sampled_row(const VerifyArgs& a, const E* __restrict__ row, int req, int j, float T,
                                   SampledLds<NT>& L, Hook hook) {
   SampledOut out{0, 0.0, 0, 0};
   int top_k = a.top_k[req];
@@ -980,7 +978,8 @@ __device__ SampledOut sampled_row(const VerifyArgs& a, const E* __restrict__ row
     L.wn[w] = s.elem_n;
     L.wovf[w] = s.ovf;
   }
-  const RowResult res = finish_row<E, NT, U, false, false>(p, L.rs, row);
+  const NoKeep nokeep;
+  const RowResult res = finish_row<E, NT, U, false, false>(p, L.rs, nokeep, row, a.V);
   out.lse = res.lse;
   if (!(res.max < INFINITY) || !(res.max > -INFINITY) || !isfinite(res.lse)) out.bits |= VSV_FLAG_LOGITS;
 

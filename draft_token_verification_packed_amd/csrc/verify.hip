@@ -1,14 +1,24 @@
 // Packed draft-token verification kernels (gfx950).
 //
-// One launch verifies a whole ragged batch. Workgroup r streams target row r
-// once from HBM and decides the row's target token and whether the row's
-// draft token is accepted. It publishes one word per row (the token the row
-// would emit, with the top bit set when its draft was accepted) and takes a
-// ticket; the workgroup that draws the last ticket runs the per-request
-// prefix-accept scan, the exclusive scan of emitted lengths over the batch
-// and the scatter of emitted tokens. No second launch and no host round trip
-// are needed: packing boundaries stay on the device (xLLM docs, "Adaptive
-// speculative inference", DSpark section "Launch example").
+// One launch verifies a whole ragged batch; packing boundaries stay on the
+// device and nothing waits on the host (xLLM docs, "Adaptive speculative
+// inference", DSpark section "Launch example").
+//
+// Greedy (persistent): one workgroup per CU streams an equal share of the
+// batch's chunks (kernels.hpp) and stores one partial per row it touched
+// (max and its lowest index, exponent reference and sum of exponentials,
+// rank count; the workgroup holding a row's first chunk adds the row's
+// draft information). The last workgroup merges each row, decides its token
+// and acceptance, and runs the per-request scan.
+//
+// Sampled, and greedy batches with many rows per CU: one workgroup per row
+// decides the row and stores its word (emitted token, accept bit); the
+// workgroup of the last row runs the same per-request scan.
+//
+// The per-request scan: prefix-accept count per request, exclusive scan of
+// emitted lengths over the batch, scatter of emitted tokens. No second
+// launch, no atomics on global memory, and nothing to clear afterwards:
+// every word handed between workgroups carries the call's tag.
 #include "kernels.hpp"
 #include "row_stream.hpp"
 #include "sampled_row.hpp"
@@ -16,6 +26,41 @@
 namespace vsv {
 
 constexpr uint32_t kAcceptBit = 0x80000000u;
+constexpr uint32_t kTokenMask = 0x3FFFFFFFu;
+constexpr uint32_t kNoDraft = kTokenMask;     // never a valid token (vocab < 2^30)
+// Polls one thread of a tail may spend waiting, over all the words it reads
+// (each poll waits for a load from the device-coherent level, about a
+// microsecond): past it the tail stops waiting, uses what it has and flags
+// the launch, so the grid always drains within a fraction of a second.
+constexpr int kPollBudget = 1 << 18;
+
+// ---------------------------------------------------------------- call tags
+
+// The tag of this call: derived from the workspace's call counter, never 0
+// and different from the previous 2^31 - 1 calls' tags.
+__device__ __forceinline__ uint32_t call_tag(const VerifyArgs& a) {
+  return ((load_agent(a.ws_epoch) + 1u) & 0x7FFFFFFFu) | 0x80000000u;
+}
+__device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t v) {
+  return (static_cast<uint64_t>(tag) << 32) | v;
+}
+// Wait (within the thread's poll budget) for the word at `w` to carry `tag`.
+__device__ __forceinline__ uint32_t poll_tagged(const uint64_t* w, uint32_t tag, int& budget, int& stalled) {
+  uint64_t x = load_agent64(w);
+  while (static_cast<uint32_t>(x >> 32) != tag && budget > 0) {
+    --budget;
+    __builtin_amdgcn_s_sleep(2);
+    x = load_agent64(w);
+  }
+  stalled |= (static_cast<uint32_t>(x >> 32) == tag) ? 0 : 1;
+  return static_cast<uint32_t>(x);
+}
+// The last workgroup ends the call: the next call uses the next tag.
+__device__ __forceinline__ void end_call(const VerifyArgs& a, uint32_t tag) {
+  if (threadIdx.x == 0) store_agent(a.ws_epoch, tag & 0x7FFFFFFFu);
+}
+
+// ---------------------------------------------------------------- rows
 
 // Per-row metadata: request, local row, draft token.
 struct RowMeta {
@@ -45,78 +90,8 @@ __device__ __forceinline__ void set_flag(const VerifyArgs& a, int bits) {
   if (a.error_flag) atomicOr(a.error_flag, bits);
 }
 
-// Rows whose words the tail stages in LDS with one round of loads.
-constexpr int kTailStage = 4096;
-
-struct TailScratch {
-  uint32_t words[kTailStage];
-  int scan[16];
-};
-
-// The last workgroup to finish: prefix-accept scan per request, exclusive
-// scan of (a_i + 1) over the batch, scatter of the emitted tokens. The words
-// of the first kTailStage rows are staged in LDS in the same round of loads
-// as the row offsets (row 0 of request 0 is row 0), so a batch of up to that
-// many rows costs one round trip; later rows are read directly.
-template <int NT>
-__device__ void batch_tail(const VerifyArgs& a, TailScratch& t) {
-  const int tid = threadIdx.x;
-  const int staged = min(a.R, kTailStage);
-  for (int k = tid; k < staged; k += NT) t.words[k] = load_agent(a.ws_row + k);
-  __syncthreads();
-  auto word = [&](int row) -> uint32_t { return row < staged ? t.words[row] : load_agent(a.ws_row + row); };
-  int carry = 0;
-  for (int base = 0; base < a.B; base += NT) {
-    const int i = base + tid;
-    int acc = 0, r0 = 0, len = 0;
-    uint32_t nxt = 0;
-    bool ok = false;
-    if (i < a.B) {
-      r0 = a.offsets[i];
-      const int r1 = a.offsets[i + 1];
-      ok = r0 >= 0 && r1 > r0 && r1 <= a.R && (i != 0 || r0 == 0) && (i != a.B - 1 || r1 == a.R);
-      if (ok) {
-        const int K = r1 - r0 - 1;
-        while (acc < K && (word(r0 + acc) & kAcceptBit)) ++acc;
-        nxt = word(r0 + acc);
-      } else {
-        set_flag(a, VSV_FLAG_LAYOUT);
-      }
-      len = acc + 1;
-    }
-    int total = 0;
-    const int pos = carry + block_exclusive_scan<NT>(len, t.scan, total);
-    if (i < a.B) {
-      const int nt = static_cast<int>(nxt & ~kAcceptBit);
-      a.accepted_len[i] = acc;
-      a.next_token[i] = nt;
-      a.out_offsets[i] = pos;
-      if (ok)
-        for (int q = 0; q < acc && pos + q < a.R; ++q) a.out_tokens[pos + q] = static_cast<int>(word(r0 + q) & ~kAcceptBit);
-      if (pos + acc < a.R) a.out_tokens[pos + acc] = nt;
-    }
-    carry += total;
-  }
-  if (tid == 0) {
-    a.out_offsets[a.B] = carry;
-    store_int_agent(a.ws_ticket, 0);  // leave the workspace zeroed for the next call
-  }
-}
-
-// Publish this row's word and, if this is the last row, run the tail.
-template <int NT>
-__device__ __forceinline__ void publish_and_maybe_tail(const VerifyArgs& a, int r, uint32_t word, TailScratch& tail) {
-  __shared__ int s_last;
-  if (threadIdx.x == 0) {
-    store_agent(a.ws_row + r, word);
-    wait_memory();
-    s_last = (ticket_agent(a.ws_ticket) == a.R - 1);
-  }
-  __syncthreads();
-  if (s_last) batch_tail<NT>(a, tail);
-}
-
-// The word a row publishes: the draft (accepted) or its own target token.
+// The word a row hands to the scan: the draft (accepted) or its own target
+// token. Flags layout and token-range problems in `bits`.
 __device__ __forceinline__ uint32_t row_word(const VerifyArgs& a, const RowMeta& m, int token, bool accept_ok,
                                              int& bits) {
   if (m.req < 0) {
@@ -133,30 +108,447 @@ __device__ __forceinline__ uint32_t row_word(const VerifyArgs& a, const RowMeta&
   return static_cast<uint32_t>(token);
 }
 
+// ---------------------------------------------------------------- scan
+
+// Rows whose words the scan stages in LDS.
+constexpr int kTailStage = 4096;
+
+struct TailScratch {
+  uint32_t words[kTailStage];
+  int scan[16];
+};
+
+// Row offsets of request i and the next one (the tails load those of the
+// first NT requests early, so the scan does not wait for them).
+struct ReqRange {
+  int r0, r1;
+};
+__device__ __forceinline__ ReqRange load_range(const VerifyArgs& a, int i) {
+  return i < a.B ? ReqRange{a.offsets[i], a.offsets[i + 1]} : ReqRange{0, 0};
+}
+
+// Per-request scan over the row words (token | kAcceptBit if the row's draft
+// was accepted): prefix-accept count, exclusive scan of (a_i + 1), scatter of
+// the emitted tokens. `word(r)` returns row r's word; `first` holds the range
+// of request tid.
+template <int NT, typename Word>
+__device__ __forceinline__ void scan_requests(const VerifyArgs& a, TailScratch& t, ReqRange first, Word word) {
+  const int tid = threadIdx.x;
+  int carry = 0;
+  for (int base = 0; base < a.B; base += NT) {
+    const int i = base + tid;
+    int acc = 0, r0 = 0, len = 0;
+    uint32_t nxt = 0;
+    bool ok = false;
+    if (i < a.B) {
+      const ReqRange rg = base == 0 ? first : load_range(a, i);
+      r0 = rg.r0;
+      const int r1 = rg.r1;
+      ok = r0 >= 0 && r1 > r0 && r1 <= a.R && (i != 0 || r0 == 0) && (i != a.B - 1 || r1 == a.R);
+      if (ok) {
+        const int K = r1 - r0 - 1;
+        while (acc < K && (word(r0 + acc) & kAcceptBit)) ++acc;
+        nxt = word(r0 + acc);
+      } else {
+        set_flag(a, VSV_FLAG_LAYOUT);
+      }
+      len = acc + 1;
+    }
+    int total = 0;
+    const int pos = carry + block_exclusive_scan<NT>(len, t.scan, total);
+    if (i < a.B) {
+      const int nt = static_cast<int>(nxt & kTokenMask);
+      a.accepted_len[i] = acc;
+      a.next_token[i] = nt;
+      a.out_offsets[i] = pos;
+      if (ok)
+        for (int q = 0; q < acc && pos + q < a.R; ++q) a.out_tokens[pos + q] = static_cast<int>(word(r0 + q) & kTokenMask);
+      if (pos + acc < a.R) a.out_tokens[pos + acc] = nt;
+    }
+    carry += total;
+  }
+  if (tid == 0) a.out_offsets[a.B] = carry;
+}
+
+// Run by the workgroup of row R - 1 after its own row (rows handled by one
+// workgroup each): gather every row's word (the first kTailStage in LDS,
+// later ones where they are read) and run the per-request scan.
+template <int NT>
+__device__ __forceinline__ void words_tail(const VerifyArgs& a, uint32_t tag, TailScratch& t) {
+  const int tid = threadIdx.x;
+  const ReqRange first = load_range(a, tid);
+  int stalled = 0, budget = kPollBudget;
+  const int staged = min(a.R, kTailStage);
+  for (int k = tid; k < staged; k += NT) t.words[k] = poll_tagged(a.ws_row + k, tag, budget, stalled);
+  __syncthreads();
+  scan_requests<NT>(a, t, first, [&](int row) -> uint32_t {
+    return row < staged ? t.words[row] : poll_tagged(a.ws_row + row, tag, budget, stalled);
+  });
+  if (stalled) set_flag(a, VSV_FLAG_STALLED);
+  end_call(a, tag);
+}
+
+// ---------------------------------------------------------------- greedy
+
+// Fields of a partial (one tagged 64-bit word each).
+enum : int { kPBest = 0, kPIdx, kPMc, kPSum, kPRank, kPInfo };
+// Row information, stored with the partial of the workgroup holding the
+// row's first chunk: the draft token in the low 30 bits (kNoDraft if the row
+// has none or it is out of range), whether the row is a verify row, whether
+// its owner entry is inconsistent.
+constexpr uint32_t kInfoVerify = 1u << 30;
+constexpr uint32_t kInfoBadLayout = 1u << 31;
+
+__device__ __forceinline__ uint32_t row_info(const VerifyArgs& a, const RowMeta& m, int& bits) {
+  if (m.req < 0) {
+    bits |= VSV_FLAG_LAYOUT;
+    return kInfoBadLayout | kNoDraft;
+  }
+  if (m.j >= m.K) return kNoDraft;
+  if (m.draft < 0 || m.draft >= a.V) {
+    bits |= VSV_FLAG_TOKEN;
+    return kInfoVerify | kNoDraft;
+  }
+  return kInfoVerify | static_cast<uint32_t>(m.draft);
+}
+
+// The row's word from its merged statistics and its information.
+template <bool kRelaxed>
+__device__ __forceinline__ uint32_t greedy_word(const VerifyArgs& a, const RowRed& red, uint32_t info, int token) {
+  const uint32_t d = info & kTokenMask;
+  if ((info & kInfoVerify) && !(info & kInfoBadLayout) && d != kNoDraft) {
+    const bool ok = kRelaxed ? (red.rank < a.relaxed_k) : (static_cast<int>(d) == token);
+    if (ok) return d | kAcceptBit;
+  }
+  return static_cast<uint32_t>(token);
+}
+
+// Geometry of the persistent decomposition: R rows of cpr chunks each,
+// Q = R * cpr chunks, workgroup p owning chunks [Q p / P, Q (p + 1) / P).
+struct ChunkPlan {
+  int64_t Q;
+  int P, cpr;
+  __device__ int64_t lo(int p) const { return Q * p / P; }
+};
+
+__device__ __forceinline__ uint64_t* slot_word(const VerifyArgs& a, int64_t slot, int f) {
+  return a.ws_part + static_cast<size_t>(slot) * kPartWords + f;
+}
+
+// Store field f of a partial (lanes 0 .. kPartWords - 1 of a wave together
+// store the whole slot).
+__device__ __forceinline__ void put_partial_field(const VerifyArgs& a, int64_t slot, int f, const RowRed& r,
+                                                  uint32_t info, uint32_t tag) {
+  uint32_t v = info;
+  if (f == kPBest) v = __float_as_uint(r.best);
+  if (f == kPIdx) v = static_cast<uint32_t>(r.idx);
+  if (f == kPMc) v = __float_as_uint(r.mc);
+  if (f == kPSum) v = __float_as_uint(static_cast<float>(r.s));
+  if (f == kPRank) v = static_cast<uint32_t>(r.rank);
+  store_agent64(slot_word(a, slot, f), tagged(tag, v));
+}
+
+template <bool kRelaxed>
+__device__ __forceinline__ RowRed slot_red(const uint32_t* v) {
+  return RowRed{static_cast<double>(__uint_as_float(v[kPSum])), __uint_as_float(v[kPBest]), static_cast<int>(v[kPIdx]),
+                __uint_as_float(v[kPMc]), kRelaxed ? static_cast<int>(v[kPRank]) : 0};
+}
+
+// The workgroup whose range holds chunk g, from the table lo[0 .. P] of
+// range starts: a double-precision estimate, then exact steps.
+__device__ __forceinline__ int owner_in(const int64_t* lo, const ChunkPlan& plan, int64_t g) {
+  int p = static_cast<int>(static_cast<double>(g) * plan.P / static_cast<double>(plan.Q));
+  p = p < 0 ? 0 : (p >= plan.P ? plan.P - 1 : p);
+  while (p > 0 && lo[p] > g) --p;
+  while (p < plan.P - 1 && lo[p + 1] <= g) ++p;
+  return p;
+}
+
+// Row r merged over the workgroups whose ranges hold its chunks (slots
+// r + p; with fewer chunks than workgroups some ranges between them are
+// empty and store nothing). The loads of the next slot are issued before
+// the current one is consumed.
+template <bool kRelaxed>
+__device__ __forceinline__ RowRed merge_slots(const VerifyArgs& a, const ChunkPlan& plan, const int64_t* lo, int r,
+                                              uint32_t tag, uint32_t& info, int& budget, int& stalled) {
+  const int64_t g0 = static_cast<int64_t>(r) * plan.cpr;
+  const int p1 = owner_in(lo, plan, g0 + plan.cpr - 1);
+  int q = owner_in(lo, plan, g0);
+  RowRed acc{0.0, -INFINITY, INT32_MAX, -FLT_MAX, 0};
+  uint64_t w[kPartWords];
+#pragma unroll
+  for (int f = 0; f < kPartWords; ++f) w[f] = load_agent64(slot_word(a, r + q, f));
+  bool first = true;
+  while (true) {
+    int qn = q + 1;
+    while (qn <= p1 && lo[qn] == lo[qn + 1]) ++qn;
+    uint64_t wn[kPartWords];
+    if (qn <= p1) {
+#pragma unroll
+      for (int f = 0; f < kPartWords; ++f) wn[f] = load_agent64(slot_word(a, r + qn, f));
+    }
+    uint32_t v[kPartWords];
+#pragma unroll
+    for (int f = 0; f < kPartWords; ++f)
+      v[f] = (static_cast<uint32_t>(w[f] >> 32) == tag) ? static_cast<uint32_t>(w[f])
+                                                         : poll_tagged(slot_word(a, r + q, f), tag, budget, stalled);
+    acc = combine(acc, slot_red<kRelaxed>(v));
+    if (first) info = v[kPInfo];
+    first = false;
+    if (qn > p1) break;
+    q = qn;
+#pragma unroll
+    for (int f = 0; f < kPartWords; ++f) w[f] = wn[f];
+  }
+  return acc;
+}
+
+// Run by the last persistent workgroup after its own range: merge every
+// row, decide its token and acceptance, write the row outputs, then the
+// per-request scan.
+template <int NT, bool kRelaxed>
+__device__ __forceinline__ void greedy_tail(const VerifyArgs& a, const ChunkPlan& plan, uint32_t tag, TailScratch& t,
+                                            int64_t* lo) {
+  const int tid = threadIdx.x;
+  const ReqRange first = load_range(a, tid);
+  for (int q = tid; q <= plan.P; q += NT) lo[q] = plan.lo(q);
+  __syncthreads();
+  int stalled = 0, bits = 0, budget = kPollBudget;
+  for (int r = tid; r < a.R; r += NT) {
+    uint32_t info = kNoDraft;
+    const RowRed red = merge_slots<kRelaxed>(a, plan, lo, r, tag, info, budget, stalled);
+    int token = red.idx;
+    // the sum holds the maximum's own term (at least 1/2), so float log2
+    // keeps the log-sum-exp within a few units of float rounding
+    const float lse = 0.69314718f * (red.mc + __log2f(static_cast<float>(red.s)));
+    if (!(red.best < INFINITY) || token == INT32_MAX || !isfinite(lse)) {
+      bits |= VSV_FLAG_LOGITS;
+      if (token == INT32_MAX) token = 0;
+    }
+    const uint32_t word = greedy_word<kRelaxed>(a, red, info, token);
+    if (a.row_token) a.row_token[r] = token;
+    if (a.row_lse) a.row_lse[r] = lse;
+    if (r < kTailStage) t.words[r] = word;
+    else store_agent64(a.ws_row + r, word);
+  }
+  if (bits) set_flag(a, bits);
+  if (stalled) set_flag(a, VSV_FLAG_STALLED);
+  if (a.R > kTailStage) wait_memory();  // words of later rows went to the workspace
+  __syncthreads();
+  scan_requests<NT>(a, t, first, [&](int row) -> uint32_t {
+    return row < kTailStage ? t.words[row] : static_cast<uint32_t>(load_agent64(a.ws_row + row));
+  });
+  end_call(a, tag);
+}
+
+// A row's 16-byte-aligned body: `head` elements in, `nvec` vectors long,
+// and a buffer resource covering exactly those vectors (or none at all).
+template <typename E>
+struct RowGeo {
+  const E* row;
+  int head, nvec;
+  __amdgpu_buffer_rsrc_t rsrc;
+};
+
+template <typename E>
+__device__ __forceinline__ RowGeo<E> row_geo(const VerifyArgs& a, int r, bool valid) {
+  constexpr int N = Elem<E>::kVec;
+  RowGeo<E> g;
+  g.row = static_cast<const E*>(a.logits) + static_cast<int64_t>(r) * a.ld;
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(g.row);
+  g.head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(E));
+  if (g.head > a.V) g.head = a.V;
+  g.nvec = (a.V - g.head) / N;
+  g.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<E*>(g.row + g.head), 0, valid ? g.nvec * 16 : 0, 0x00020000);
+  return g;
+}
+
+// Loads of chunk k's vectors k * CH + u * 64 + lane: buffer loads bounded by
+// the row's body, so vectors past its end (and every load through an empty
+// resource) return zero without touching memory, and no load needs a branch.
+template <int U>
+__device__ __forceinline__ void load_chunk(u32x4* dst, __amdgpu_buffer_rsrc_t rsrc, int k, int lane) {
+  constexpr int CH = kWave * U;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    dst[u] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, static_cast<uint32_t>((k * CH + u * kWave + lane) * 16), 0,
+                                                   2 /* nt */);
+}
+
+// Persistent greedy verification: one workgroup per CU, an equal contiguous
+// range of chunks each, chunks handed to waves through an LDS counter. A wave
+// keeps the partial of the row it is in and parks it in LDS when it moves on;
+// the workgroup then stores one partial per row it touched (slot r + p).
 template <typename E, int NT, int U, bool kRelaxed>
 __global__ __launch_bounds__(NT) void verify_greedy_kernel(VerifyArgs a) {
+  constexpr int NW = NT / kWave;
+  constexpr int CH = kWave * U;
+  static_assert(NW >= kPartWords, "one lane per partial field");
+  __shared__ RowRed slots[kMaxLocalRows][NW];
+  __shared__ float s_xd[kMaxLocalRows];
+  __shared__ int s_d[kMaxLocalRows];
+  __shared__ uint32_t s_info[kMaxLocalRows];
+  __shared__ int s_next;
+  __shared__ TailScratch tail;
+  __shared__ int64_t s_lo[kMaxGroups + 1];
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const int p = blockIdx.x;
+  const uint32_t tag = call_tag(a);
+  const ChunkPlan plan{static_cast<int64_t>(a.R) * a.cpr, static_cast<int>(gridDim.x), a.cpr};
+  const int64_t lo = plan.lo(p), hi = plan.lo(p + 1);
+  const int row_lo = static_cast<int>(lo / a.cpr);
+  const int t_lo = static_cast<int>(lo - static_cast<int64_t>(row_lo) * a.cpr);  // first chunk's index in its row
+  const int nch = static_cast<int>(hi - lo);
+  const int nloc = nch > 0 ? static_cast<int>((hi - 1) / a.cpr) - row_lo + 1 : 0;
+
+  for (int k = tid; k < nloc * NW; k += NT) slots[k / NW][k % NW] = RowRed{0.0, -INFINITY, INT32_MAX, -FLT_MAX, 0};
+  if (tid == 0) s_next = 0;
+  // Row information. Relaxed rows need the draft's own logit before their
+  // chunks are reduced, so wave 0 gathers it first; otherwise the last wave
+  // gathers the information of the rows whose first chunk is here while the
+  // other waves stream (it joins them afterwards).
+  auto gather_info = [&]() {
+    if (lane < nloc) {
+      const int r = row_lo + lane;
+      const bool first = static_cast<int64_t>(r) * a.cpr >= lo;
+      if (kRelaxed || first) {
+        const RowMeta m = load_meta(a, r, a.owner[r]);
+        int bits = 0;
+        const uint32_t info = row_info(a, m, bits);
+        if (first) {
+          s_info[lane] = info;
+          if (bits) set_flag(a, bits);
+        }
+        if (kRelaxed) {
+          const E* row = static_cast<const E*>(a.logits) + static_cast<int64_t>(r) * a.ld;
+          const bool dv = m.draft >= 0 && m.draft < a.V;
+          s_d[lane] = dv ? m.draft : -1;
+          s_xd[lane] = dv ? Elem<E>::at(row, m.draft) : INFINITY;
+        }
+      }
+    }
+  };
+  if (kRelaxed && w == 0) gather_info();
+  __syncthreads();
+  if (!kRelaxed && w == NW - 1) gather_info();
+
+  auto grab = [&]() -> int {
+    int c = 0;
+    if (lane == 0) c = atomicAdd(&s_next, 1);
+    return __builtin_amdgcn_readfirstlane(c);
+  };
+
+  RowPartial pt;
+  partial_init(pt);
+  GroupKeep<U> keep{};
+  int row = -1, row_head = 0, row_nvec = 0;
+  float xd = INFINITY;
+  int d = 0;
+  constexpr float kLog2e = 1.4426950408889634f;
+  auto flush = [&]() {
+    if (row < 0) return;
+    const int idx = lane_argmax<E, kWave, U>(pt, keep, row_head, row_nvec);
+    const RowRed r = wave_red<kRelaxed>(RowRed{pt.s, pt.best, idx, pt.mc, kRelaxed ? pt.rank : 0});
+    if (lane == 0) slots[row - row_lo][w] = r;
+  };
+
+  // The wave's position (row, chunk index in the row) moves forward by the
+  // difference of the chunk numbers it is handed; it and the row geometry
+  // are the same for every lane, so they stay on the scalar unit.
+  int c = grab();
+  int cr, ck;
+  {
+    const int t = t_lo + c;
+    cr = row_lo + t / a.cpr;
+    ck = t - (cr - row_lo) * a.cpr;
+  }
+  RowGeo<E> cg = row_geo<E>(a, cr, c < nch);
+  u32x4 buf[U];
+  load_chunk<U>(buf, cg.rsrc, ck, lane);
+  while (c < nch) {
+    const int cn = grab();
+    const bool nvalid = cn < nch;
+    int nr = cr, nk = ck + (nvalid ? cn - c : 0);
+    while (nk >= a.cpr) {
+      nk -= a.cpr;
+      ++nr;
+    }
+    RowGeo<E> ng = cg;
+    if (nr != cr || !nvalid) ng = row_geo<E>(a, nr, nvalid);
+    u32x4 nb[U];
+    load_chunk<U>(nb, ng.rsrc, nk, lane);
+
+    if (cr != row) {
+      flush();
+      partial_init(pt);
+      row = cr;
+      row_head = cg.head;
+      row_nvec = cg.nvec;
+      if (kRelaxed) {
+        xd = s_xd[row - row_lo];
+        d = s_d[row - row_lo];
+      }
+    }
+    const int v0 = ck * CH + lane;
+    if ((ck + 1) * CH > cg.nvec)
+      take_group<E, U, kWave, kRelaxed, true>(pt, buf, v0, cg.head, kLog2e, xd, d, keep, cg.nvec);
+    else
+      take_group<E, U, kWave, kRelaxed>(pt, buf, v0, cg.head, kLog2e, xd, d, keep);
+    // elements outside the row's 16-byte body (misaligned rows or a vocab
+    // that is not a multiple of the vector): with the first and last chunk
+    if (ck == 0 && lane < cg.head)
+      take_scalar<kRelaxed>(pt, Elem<E>::at(cg.row, lane), lane, kLog2e, xd, d);
+    if (ck == a.cpr - 1) {
+      const int e = cg.head + cg.nvec * Elem<E>::kVec + lane;
+      if (e < a.V) take_scalar<kRelaxed>(pt, Elem<E>::at(cg.row, e), e, kLog2e, xd, d);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) buf[u] = nb[u];
+    cr = nr;
+    ck = nk;
+    cg = ng;
+    c = cn;
+  }
+  flush();
+  __syncthreads();
+
+  // one partial per row touched (slot r + p), a wave per row: its lanes
+  // combine the waves' slots; the row information goes with the first
+  for (int k = w; k < nloc; k += NW) {
+    RowRed r = lane < NW ? slots[k][lane] : RowRed{0.0, -INFINITY, INT32_MAX, -FLT_MAX, 0};
+    r = wave_red<kRelaxed>(r);
+    const int rr = row_lo + k;
+    const bool first = static_cast<int64_t>(rr) * a.cpr >= lo;
+    if (lane < kPartWords) put_partial_field(a, static_cast<int64_t>(rr) + p, lane, r, first ? s_info[k] : kNoDraft, tag);
+  }
+  if (p == plan.P - 1) greedy_tail<NT, kRelaxed>(a, plan, tag, tail, s_lo);
+}
+
+// One workgroup per row (batches with many rows per CU): the row's word is
+// decided here and handed to the scan like a sampled row's.
+template <typename E, int NT, int U, bool kRelaxed>
+__global__ __launch_bounds__(NT) void verify_greedy_rows_kernel(VerifyArgs a) {
   __shared__ RowScratch<NT> scr;
   __shared__ TailScratch tail;
   const int r = blockIdx.x;
+  const uint32_t tag = call_tag(a);
   const E* __restrict__ row = static_cast<const E*>(a.logits) + static_cast<int64_t>(r) * a.ld;
   const int owner = a.owner[r];
-
   RowMeta m{-1, 0, 0, -1};
   float xd = INFINITY;
   if (kRelaxed) {
-    // the rank test needs the draft's own logit before streaming
     m = load_meta(a, r, owner);
     if (m.draft >= 0 && m.draft < a.V) xd = Elem<E>::at(row, m.draft);
   }
   RowPartial p;
   partial_init(p);
+  GroupKeep<U> keep{};
   constexpr float kLog2e = 1.4426950408889634f;
-  stream_row<E, NT, U, kRelaxed>(row, a.V, kLog2e, xd, kRelaxed ? m.draft : 0, p, [&]() {
+  stream_row<E, NT, U, kRelaxed>(row, a.V, kLog2e, xd, kRelaxed ? m.draft : 0, p, keep, [&]() {
     if (!kRelaxed) m = load_meta(a, r, owner);
   });
-  const RowResult res = finish_row<E, NT, U, kRelaxed>(p, scr, row);
-
-  uint32_t word = 0;
+  const RowResult res = finish_row<E, NT, U, kRelaxed, true>(p, scr, keep, row, a.V);
   if (threadIdx.x == 0) {
     int token = res.argmax;
     int bits = 0;
@@ -165,26 +557,33 @@ __global__ __launch_bounds__(NT) void verify_greedy_kernel(VerifyArgs a) {
       if (token == INT32_MAX) token = 0;
     }
     const bool ok = kRelaxed ? (res.rank < a.relaxed_k) : (m.draft == token);
-    word = row_word(a, m, token, ok, bits);
+    const uint32_t word = row_word(a, m, token, ok, bits);
     if (bits) set_flag(a, bits);
     if (a.row_token) a.row_token[r] = token;
     if (a.row_lse) a.row_lse[r] = static_cast<float>(res.lse);
+    store_agent64(a.ws_row + r, tagged(tag, word));
   }
-  publish_and_maybe_tail<NT>(a, r, word, tail);
+  if (r == a.R - 1) words_tail<NT>(a, tag, tail);
 }
 
-template <typename E>
-static hipError_t launch_greedy_t(const VerifyArgs& a, hipStream_t s) {
-  const dim3 grid(a.R), block(kVerifyThreads);
-  if (a.relaxed_k > 1)
-    verify_greedy_kernel<E, kVerifyThreads, kUnroll, true><<<grid, block, 0, s>>>(a);
-  else
-    verify_greedy_kernel<E, kVerifyThreads, kUnroll, false><<<grid, block, 0, s>>>(a);
+template <typename E, bool kRelaxed>
+static hipError_t launch_greedy_t(VerifyArgs a, hipStream_t s) {
+  constexpr int N = Elem<E>::kVec;
+  constexpr int CH = kWave * kUnroll;
+  if (greedy_persistent(a.R, a.groups)) {
+    const int nvmax = a.V / N;
+    a.cpr = nvmax > 0 ? (nvmax + CH - 1) / CH : 1;
+    verify_greedy_kernel<E, kGreedyThreads, kUnroll, kRelaxed><<<dim3(a.groups), dim3(kGreedyThreads), 0, s>>>(a);
+  } else {
+    verify_greedy_rows_kernel<E, kRowThreads, kUnroll, kRelaxed><<<dim3(a.R), dim3(kRowThreads), 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_verify_greedy(const VerifyArgs& a, hipStream_t s) {
-  return a.dtype == VSV_BF16 ? launch_greedy_t<uint16_t>(a, s) : launch_greedy_t<float>(a, s);
+  if (a.dtype == VSV_BF16)
+    return a.relaxed_k > 1 ? launch_greedy_t<uint16_t, true>(a, s) : launch_greedy_t<uint16_t, false>(a, s);
+  return a.relaxed_k > 1 ? launch_greedy_t<float, true>(a, s) : launch_greedy_t<float, false>(a, s);
 }
 
 // ---------------------------------------------------------------- sampled
@@ -197,13 +596,14 @@ __global__ __launch_bounds__(NT) void verify_sampled_kernel(VerifyArgs a) {
   __shared__ SampledLds<NT> L;
   static_assert(sizeof(TailScratch) <= sizeof(L.elem), "tail staging aliases the candidate buffers");
   const int r = blockIdx.x;
+  const uint32_t tag = call_tag(a);
   const E* __restrict__ row = static_cast<const E*>(a.logits) + static_cast<int64_t>(r) * a.ld;
   const RowMeta m = load_meta(a, r, a.owner[r]);
   const float T = a.temperature[m.req < 0 ? 0 : m.req];
   int token = 0, bits = 0, slow = 0;
   double lse = 0.0;
   if (m.req >= 0 && T > 0.f) {
-    const SampledOut o = sampled_row<E, NT, U>(a, row, m.req, m.j, T, L, NoHook());
+    const SampledOut o = sampled_row<E, NT, kUnrollSampled>(a, row, m.req, m.j, T, L, NoHook());
     token = o.token;
     lse = o.lse;
     bits = o.bits;
@@ -211,24 +611,25 @@ __global__ __launch_bounds__(NT) void verify_sampled_kernel(VerifyArgs a) {
   } else {
     RowPartial p;
     partial_init(p);
+    GroupKeep<U> keep{};
     constexpr float kLog2e = 1.4426950408889634f;
-    stream_row<E, NT, U, false>(row, a.V, kLog2e, INFINITY, 0, p);
-    const RowResult res = finish_row<E, NT, U, false>(p, L.rs, row);
+    stream_row<E, NT, U, false>(row, a.V, kLog2e, INFINITY, 0, p, keep);
+    const RowResult res = finish_row<E, NT, U, false, true>(p, L.rs, keep, row, a.V);
     token = res.argmax;
     lse = res.lse;
     if (!(res.max < INFINITY) || token == INT32_MAX || !isfinite(res.lse)) bits |= VSV_FLAG_LOGITS;
     if (token == INT32_MAX) token = 0;
     if (m.req >= 0 && !(T >= 0.f)) bits |= VSV_FLAG_PARAMS;
   }
-  uint32_t word = 0;
   if (threadIdx.x == 0) {
-    word = row_word(a, m, token, m.draft == token, bits);
+    const uint32_t word = row_word(a, m, token, m.draft == token, bits);
     if (bits) set_flag(a, bits);
     if (slow && a.slow_rows) atomicAdd(a.slow_rows, 1);
     if (a.row_token) a.row_token[r] = token;
     if (a.row_lse) a.row_lse[r] = static_cast<float>(lse);
+    store_agent64(a.ws_row + r, tagged(tag, word));
   }
-  publish_and_maybe_tail<NT>(a, r, word, *reinterpret_cast<TailScratch*>(&L.elem[0][0]));
+  if (r == a.R - 1) words_tail<NT>(a, tag, *reinterpret_cast<TailScratch*>(&L.elem[0][0]));
 }
 
 template <typename E>

@@ -56,11 +56,14 @@ typedef enum { VSV_F32 = 0, VSV_BF16 = 1 } vsv_dtype;
 #define VSV_FLAG_TOKEN 2   /* a draft / selected token outside [0, vocab): treated as a mismatch */
 #define VSV_FLAG_LOGITS 4  /* NaN or +inf logit, or a row with no finite logit                  */
 #define VSV_FLAG_PARAMS 8  /* temperature < 0, top_p outside (0, 1], min_p outside [0, 1]       */
+#define VSV_FLAG_STALLED 16 /* a row's result did not reach the batch scan within the scan's    */
+                            /* bounded wait (rows of one launch could not all be resident;   */
+                            /* not expected on a dedicated GPU); outputs are unspecified     */
 
 typedef struct {
   const void* logits;          /* [num_rows, ld] vocab-wide target logits             */
   int32_t dtype;               /* vsv_dtype                                           */
-  int32_t vocab;               /* V >= 1                                              */
+  int32_t vocab;               /* 1 <= V < 2^30                                       */
   int64_t ld;                  /* row stride in elements, >= vocab                    */
   int32_t num_requests;        /* B >= 0                                              */
   int32_t num_rows;            /* R = sum_i (K_i + 1) >= B                            */
@@ -85,11 +88,13 @@ typedef struct {
                          /* again); diagnostics only, results are identical        */
 } vsv_outputs;
 
-/* Bytes of device workspace a verify call needs (B requests, R rows).
- * The workspace must be zero-filled before its first use (vsv_workspace_init
- * or any zeroed allocation); every call leaves it zeroed again when it
- * completes, so one workspace can serve any later call on the same stream.
- * Two calls that may overlap in time need two workspaces. */
+/* Bytes of device workspace a verify call needs (B requests, R rows): the
+ * words through which rows and workgroups hand their results to the
+ * batch-wide scan, and a call counter. The workspace must be zero-filled
+ * before its first use (vsv_workspace_init or any zeroed allocation); after
+ * that every call leaves it ready for the next one, so one workspace serves
+ * any later call on the same stream. Two calls that may overlap in time
+ * need two workspaces. */
 size_t vsv_workspace_bytes(int32_t num_requests, int32_t num_rows, int32_t sampled);
 
 /* Zero-fill `bytes` of workspace on `stream` with a kernel (no memset node,

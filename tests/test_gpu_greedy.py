@@ -105,6 +105,18 @@ def test_full_vocab_ragged(vsv):
     assert_same(out, oracle.verify_greedy(store, oracle.BF16, synth.VOCAB, off, owner, drafts))
 
 
+@pytest.mark.parametrize("B,k", [(1000, 1), (1000, 3), (1800, 1), (1800, 3)])
+def test_many_rows(vsv, B, k):
+    """About 5 B rows: beyond the 4096 rows the scan stages in LDS, and with
+    1800 requests (about 9000 rows) more than 31 rows per CU of a 256-CU part,
+    where every row gets a workgroup of its own."""
+    rng = np.random.default_rng(B + k)
+    store, off, owner, drafts = _custom(rng, B, 8, 640, oracle.BF16)
+    assert int(off[-1]) > 4096
+    out = vsv.verify_greedy(to_dev(store), to_dev(off), to_dev(owner), to_dev(drafts), relaxed_topk=k)
+    assert_same(out, oracle.verify_greedy(store, oracle.BF16, 640, off, owner, drafts, relaxed_topk=k))
+
+
 def test_single_row_requests_and_empty_batch(vsv):
     import torch
     rng = np.random.default_rng(6)

@@ -102,9 +102,12 @@ def test_temperature_zero_is_greedy(vsv):
     torch.cuda.synchronize()
     for k in ("accepted_len", "next_token", "out_offsets", "row_token"):
         assert np.array_equal(host(s[k]), host(g[k])), k
-    assert np.array_equal(host(s["row_lse"]), host(g["row_lse"]))
+    # the greedy entry point sums a row in pieces, so the two log-sum-exps may
+    # differ in their last float bits; both are held to the oracle
+    assert_lse_close(host(s["row_lse"]), host(g["row_lse"]), rtol=1e-6)
     ref = oracle.verify_greedy(wl.logits, wl.dtype, wl.V, wl.offsets, wl.owner, wl.drafts)
     assert_same(s, ref)
+    assert_same(g, ref)
 
 
 GRID = [
