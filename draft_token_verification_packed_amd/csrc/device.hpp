@@ -21,6 +21,7 @@ template <typename E> struct Elem;
 
 template <> struct Elem<float> {
   static constexpr int kVec = 4;
+  __device__ static __forceinline__ u32x4 neg_inf() { return u32x4{0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u}; }
   __device__ static __forceinline__ float at(const float* p, int64_t i) { return p[i]; }
   __device__ static __forceinline__ void decode(const u32x4& w, float* f) {
     f[0] = __uint_as_float(w.x);
@@ -34,6 +35,7 @@ template <> struct Elem<float> {
 // is widened by a shift, the high one by masking.
 template <> struct Elem<uint16_t> {
   static constexpr int kVec = 8;
+  __device__ static __forceinline__ u32x4 neg_inf() { return u32x4{0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u}; }
   __device__ static __forceinline__ float at(const uint16_t* p, int64_t i) {
     return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
   }

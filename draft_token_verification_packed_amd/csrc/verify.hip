@@ -266,8 +266,9 @@ __device__ __forceinline__ int owner_in(const int64_t* lo, const ChunkPlan& plan
 
 // Row r merged over the workgroups whose ranges hold its chunks (slots
 // r + p; with fewer chunks than workgroups some ranges between them are
-// empty and store nothing). The loads of the next slot are issued before
-// the current one is consumed.
+// empty and store nothing). Slots are taken two at a time: both are loaded
+// together and, while either is still in flight, reloaded together, so a
+// wait costs one round trip however many of its words are missing.
 template <bool kRelaxed>
 __device__ __forceinline__ RowRed merge_slots(const VerifyArgs& a, const ChunkPlan& plan, const int64_t* lo, int r,
                                               uint32_t tag, uint32_t& info, int& budget, int& stalled) {
@@ -275,30 +276,49 @@ __device__ __forceinline__ RowRed merge_slots(const VerifyArgs& a, const ChunkPl
   const int p1 = owner_in(lo, plan, g0 + plan.cpr - 1);
   int q = owner_in(lo, plan, g0);
   RowRed acc{0.0, -INFINITY, INT32_MAX, -FLT_MAX, 0};
-  uint64_t w[kPartWords];
-#pragma unroll
-  for (int f = 0; f < kPartWords; ++f) w[f] = load_agent64(slot_word(a, r + q, f));
   bool first = true;
-  while (true) {
-    int qn = q + 1;
-    while (qn <= p1 && lo[qn] == lo[qn + 1]) ++qn;
-    uint64_t wn[kPartWords];
-    if (qn <= p1) {
+  while (q <= p1) {
+    int q2 = q + 1;
+    while (q2 <= p1 && lo[q2] == lo[q2 + 1]) ++q2;
+    const bool two = q2 <= p1;
+    uint64_t w[2][kPartWords];
+    auto load_all = [&]() {
 #pragma unroll
-      for (int f = 0; f < kPartWords; ++f) wn[f] = load_agent64(slot_word(a, r + qn, f));
+      for (int f = 0; f < kPartWords; ++f) w[0][f] = load_agent64(slot_word(a, r + q, f));
+      if (two) {
+#pragma unroll
+        for (int f = 0; f < kPartWords; ++f) w[1][f] = load_agent64(slot_word(a, r + q2, f));
+      }
+    };
+    auto complete = [&]() {
+      bool ok = true;
+#pragma unroll
+      for (int f = 0; f < kPartWords; ++f) {
+        ok = ok && static_cast<uint32_t>(w[0][f] >> 32) == tag;
+        ok = ok && (!two || static_cast<uint32_t>(w[1][f] >> 32) == tag);
+      }
+      return ok;
+    };
+    load_all();
+    while (!complete() && budget > 0) {
+      --budget;
+      __builtin_amdgcn_s_sleep(2);
+      load_all();
     }
-    uint32_t v[kPartWords];
+    stalled |= complete() ? 0 : 1;
 #pragma unroll
-    for (int f = 0; f < kPartWords; ++f)
-      v[f] = (static_cast<uint32_t>(w[f] >> 32) == tag) ? static_cast<uint32_t>(w[f])
-                                                         : poll_tagged(slot_word(a, r + q, f), tag, budget, stalled);
-    acc = combine(acc, slot_red<kRelaxed>(v));
-    if (first) info = v[kPInfo];
-    first = false;
-    if (qn > p1) break;
-    q = qn;
+    for (int k = 0; k < 2; ++k) {
+      if (k == 1 && !two) break;
+      uint32_t v[kPartWords];
 #pragma unroll
-    for (int f = 0; f < kPartWords; ++f) w[f] = wn[f];
+      for (int f = 0; f < kPartWords; ++f) v[f] = static_cast<uint32_t>(w[k][f]);
+      acc = combine(acc, slot_red<kRelaxed>(v));
+      if (first) info = v[kPInfo];
+      first = false;
+    }
+    // next pair
+    q = two ? q2 + 1 : p1 + 1;
+    while (q <= p1 && lo[q] == lo[q + 1]) ++q;
   }
   return acc;
 }
@@ -453,62 +473,91 @@ __global__ __launch_bounds__(NT) void verify_greedy_kernel(VerifyArgs a) {
     if (lane == 0) slots[row - row_lo][w] = r;
   };
 
-  // The wave's position (row, chunk index in the row) moves forward by the
-  // difference of the chunk numbers it is handed; it and the row geometry
-  // are the same for every lane, so they stay on the scalar unit.
-  int c = grab();
-  int cr, ck;
-  {
+  // A chunk handed to this wave: its number in the workgroup's range, its
+  // row and index in the row, and that row's geometry. A wave's chunks come
+  // in increasing order, so each position is the previous one moved forward
+  // by the difference of the numbers. All of it is the same for every lane
+  // and stays on the scalar unit.
+  struct Slot {
+    int c, r, k;
+    RowGeo<E> g;
+  };
+  auto first_slot = [&](int c) {
+    Slot sl;
+    sl.c = c;
     const int t = t_lo + c;
-    cr = row_lo + t / a.cpr;
-    ck = t - (cr - row_lo) * a.cpr;
-  }
-  RowGeo<E> cg = row_geo<E>(a, cr, c < nch);
-  u32x4 buf[U];
-  load_chunk<U>(buf, cg.rsrc, ck, lane);
-  while (c < nch) {
-    const int cn = grab();
-    const bool nvalid = cn < nch;
-    int nr = cr, nk = ck + (nvalid ? cn - c : 0);
-    while (nk >= a.cpr) {
-      nk -= a.cpr;
-      ++nr;
+    sl.r = row_lo + t / a.cpr;
+    sl.k = t - (sl.r - row_lo) * a.cpr;
+    sl.g = row_geo<E>(a, sl.r, c < nch);
+    return sl;
+  };
+  auto after = [&](const Slot& prev, int c) {
+    Slot sl;
+    sl.c = c;
+    const bool valid = c < nch;
+    sl.r = prev.r;
+    sl.k = prev.k + (valid ? c - prev.c : 0);
+    while (sl.k >= a.cpr) {
+      sl.k -= a.cpr;
+      ++sl.r;
     }
-    RowGeo<E> ng = cg;
-    if (nr != cr || !nvalid) ng = row_geo<E>(a, nr, nvalid);
-    u32x4 nb[U];
-    load_chunk<U>(nb, ng.rsrc, nk, lane);
-
-    if (cr != row) {
+    sl.g = (sl.r == prev.r && valid) ? prev.g : row_geo<E>(a, sl.r, valid);
+    return sl;
+  };
+  auto process = [&](const Slot& sl, u32x4* w) {
+    if (sl.r != row) {
       flush();
       partial_init(pt);
-      row = cr;
-      row_head = cg.head;
-      row_nvec = cg.nvec;
+      row = sl.r;
+      row_head = sl.g.head;
+      row_nvec = sl.g.nvec;
       if (kRelaxed) {
         xd = s_xd[row - row_lo];
         d = s_d[row - row_lo];
       }
     }
-    const int v0 = ck * CH + lane;
-    if ((ck + 1) * CH > cg.nvec)
-      take_group<E, U, kWave, kRelaxed, true>(pt, buf, v0, cg.head, kLog2e, xd, d, keep, cg.nvec);
-    else
-      take_group<E, U, kWave, kRelaxed>(pt, buf, v0, cg.head, kLog2e, xd, d, keep);
+    const int v0 = sl.k * CH + lane;
+    const bool partial = (sl.k + 1) * CH > sl.g.nvec;   // the row's last chunk
+    if (kRelaxed && partial) {
+      take_group<E, U, kWave, true, true>(pt, w, v0, sl.g.head, kLog2e, xd, d, keep, sl.g.nvec);
+    } else {
+      // vectors past the row's body read as zeros: make them -inf (only the
+      // last chunk of a row has any)
+      if (partial) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (v0 + u * kWave >= sl.g.nvec) w[u] = Elem<E>::neg_inf();
+      }
+      take_group<E, U, kWave, kRelaxed>(pt, w, v0, sl.g.head, kLog2e, xd, d, keep);
+    }
     // elements outside the row's 16-byte body (misaligned rows or a vocab
     // that is not a multiple of the vector): with the first and last chunk
-    if (ck == 0 && lane < cg.head)
-      take_scalar<kRelaxed>(pt, Elem<E>::at(cg.row, lane), lane, kLog2e, xd, d);
-    if (ck == a.cpr - 1) {
-      const int e = cg.head + cg.nvec * Elem<E>::kVec + lane;
-      if (e < a.V) take_scalar<kRelaxed>(pt, Elem<E>::at(cg.row, e), e, kLog2e, xd, d);
+    if (sl.k == 0 && lane < sl.g.head)
+      take_scalar<kRelaxed>(pt, Elem<E>::at(sl.g.row, lane), lane, kLog2e, xd, d);
+    if (sl.k == a.cpr - 1) {
+      const int e = sl.g.head + sl.g.nvec * Elem<E>::kVec + lane;
+      if (e < a.V) take_scalar<kRelaxed>(pt, Elem<E>::at(sl.g.row, e), e, kLog2e, xd, d);
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) buf[u] = nb[u];
-    cr = nr;
-    ck = nk;
-    cg = ng;
-    c = cn;
+  };
+
+  // Two buffers in turn, no copies: while one chunk is reduced the other's
+  // loads are in flight, and the next chunk number is fetched before the
+  // reduction so its LDS round trip is hidden.
+  Slot sa = first_slot(grab());
+  u32x4 A[U], B[U];
+  load_chunk<U>(A, sa.g.rsrc, sa.k, lane);
+  Slot sb = after(sa, grab());
+  load_chunk<U>(B, sb.g.rsrc, sb.k, lane);
+  while (sa.c < nch) {
+    const int ca = grab();
+    process(sa, A);
+    sa = after(sb, ca);
+    load_chunk<U>(A, sa.g.rsrc, sa.k, lane);
+    if (sb.c >= nch) break;
+    const int cb = grab();
+    process(sb, B);
+    sb = after(sa, cb);
+    load_chunk<U>(B, sb.g.rsrc, sb.k, lane);
   }
   flush();
   __syncthreads();
