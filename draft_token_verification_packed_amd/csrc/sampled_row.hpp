@@ -240,9 +240,11 @@ __device__ void wave_drain(SampledLds<NT>& L, WaveCap& s) {
       s.elem_n += total;
       break;
     }
-    // leave room for what is arriving; each round raises the threshold,
-    // which also thins the arrivals
-    const int target = max(s.kmin, max(kEW / 8, min(kEW / 2, kEW - total)));
+    // Leave room for what is arriving; each round raises the threshold,
+    // which also thins the arrivals. A top-k row keeps only its top_k + 32:
+    // the k-th largest of the elements seen so far can only rise, so it is a
+    // safe threshold, and a high one parks far fewer vectors later.
+    const int target = s.kmin > 0 ? s.kmin : max(kEW / 8, min(kEW / 2, kEW - total));
     if (attempt == 7 || !wave_compact<NT>(L, s, target)) {
       s.ovf = 1;
       s.tau = INFINITY;  // stop capturing: this row goes to the exact path
@@ -277,7 +279,7 @@ __device__ __forceinline__ void wave_take_scalar(SampledLds<NT>& L, WaveCap& s, 
   const uint64_t bal = __ballot(take);
   if (bal == 0) return;
   const int n = __popcll(bal);
-  if (s.elem_n + n > kEW && !wave_compact<NT>(L, s, max(s.kmin, kEW / 2))) {
+  if (s.elem_n + n > kEW && !wave_compact<NT>(L, s, s.kmin > 0 ? s.kmin : kEW / 2)) {
     s.ovf = 1;
     s.tau = INFINITY;
     return;
