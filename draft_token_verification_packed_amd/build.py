@@ -7,18 +7,23 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 LIB = os.path.join(PKG, "libvspec_verify.so")
-SOURCES = ["abi.cpp", "verify.hip", "confidence.hip"]
+SOURCES = ["abi.cpp", "verify.hip", "sampled.hip", "confidence.hip"]
 ARCH = "gfx950"
 # Packed-FP32 VALU forms are kept out of the code objects: the compiler would
 # otherwise fuse float pairs into v_pk_* instructions.
-FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=" + ARCH,
+FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function"]
+# The sampled kernel loops over rows: with loop-invariant code motion the
+# compiler hoists a hundred constants out of that loop into registers and
+# the kernel no longer fits two workgroups per CU.
+SOURCE_FLAGS = {"sampled.hip": ["-mllvm", "-disable-machine-licm"]}
 
 
 def hipcc():
@@ -28,16 +33,31 @@ def hipcc():
     return p
 
 
-def build(extra_flags=(), out=LIB, verbose=False):
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    cmd = [hipcc()] + FLAGS + list(extra_flags) + ["-I", CSRC, "-I", INCLUDE] + srcs + ["-o", out + ".tmp"]
+def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + msgs)
-    if verbose and msgs.strip():
-        print(msgs, file=sys.stderr)
+    return msgs
+
+
+def build(extra_flags=(), out=LIB, verbose=False):
+    """Compile every source to an object (with its own flags) and link the library."""
+    objdir = tempfile.mkdtemp(prefix="vsv_build_")
+    try:
+        objs, msgs = [], []
+        for s in SOURCES:
+            obj = os.path.join(objdir, s + ".o")
+            cmd = ([hipcc()] + FLAGS + SOURCE_FLAGS.get(s, []) + list(extra_flags) +
+                   ["-I", CSRC, "-I", INCLUDE, "-c", os.path.join(CSRC, s), "-o", obj])
+            msgs.append(_run(cmd))
+            objs.append(obj)
+        msgs.append(_run([hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH] + objs + ["-o", out + ".tmp"]))
+    finally:
+        shutil.rmtree(objdir, ignore_errors=True)
+    if verbose and any(m.strip() for m in msgs):
+        print("\n".join(m for m in msgs if m.strip()), file=sys.stderr)
     os.replace(out + ".tmp", out)
     return out
 

@@ -72,6 +72,7 @@ vsv_status prepare(const vsv_batch* b, const vsv_outputs* o, void* ws, size_t ws
   v.slow_rows = o->slow_rows;
   char* w = static_cast<char*>(ws);
   v.ws_epoch = reinterpret_cast<uint32_t*>(w);
+  v.ws_queue = reinterpret_cast<uint32_t*>(w + 64);
   v.ws_row = reinterpret_cast<uint64_t*>(w + vsv::kWsAlign);
   v.ws_part = reinterpret_cast<uint64_t*>(w + vsv::kWsAlign + vsv::ws_row_bytes(b->num_rows));
   v.groups = persistent_groups();

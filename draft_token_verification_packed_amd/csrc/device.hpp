@@ -83,12 +83,66 @@ __device__ __forceinline__ uint64_t load_agent64(const uint64_t* p) {
 
 // ---------------------------------------------------------------- reductions
 
+struct MaxOp {
+  template <typename T> __device__ __forceinline__ T operator()(T a, T b) const { return a > b ? a : b; }
+};
+struct MinOp {
+  template <typename T> __device__ __forceinline__ T operator()(T a, T b) const { return a < b ? a : b; }
+};
+struct SumOp {
+  template <typename T> __device__ __forceinline__ T operator()(T a, T b) const { return a + b; }
+};
+
+// Wave-wide exchanges without LDS. A DPP move reads another lane's register
+// in the same instruction; lanes whose source lies outside the pattern (or
+// whose row is masked off) read 0. 64-bit values move as two halves.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ int dpp_move(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS = 0xF, typename T>
+__device__ __forceinline__ T dpp_val(T x) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, dpp_move<CTRL, ROWS>(__builtin_bit_cast(int, x)));
+  } else {
+    const int2 h = __builtin_bit_cast(int2, x);
+    int2 o;
+    o.x = dpp_move<CTRL, ROWS>(h.x);
+    o.y = dpp_move<CTRL, ROWS>(h.y);
+    return __builtin_bit_cast(T, o);
+  }
+}
+template <typename T>
+__device__ __forceinline__ T read_lane(T x, int lane) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+  } else {
+    const int2 h = __builtin_bit_cast(int2, x);
+    int2 o;
+    o.x = __builtin_amdgcn_readlane(h.x, lane);
+    o.y = __builtin_amdgcn_readlane(h.y, lane);
+    return __builtin_bit_cast(T, o);
+  }
+}
+
+// Reduction over the wave: row rotations by 8, 4, 2 and 1 lanes give every
+// lane the value of its row of 16, and four lane reads combine the rows as
+// (row0 op row1) op (row2 op row3). The result is uniform (every lane holds
+// it). Every lane of the wave must be active.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_all(T v, Op op) {
+  v = op(v, dpp_val<0x128>(v));
+  v = op(v, dpp_val<0x124>(v));
+  v = op(v, dpp_val<0x122>(v));
+  v = op(v, dpp_val<0x121>(v));
+  return op(op(read_lane(v, 0), read_lane(v, 16)), op(read_lane(v, 32), read_lane(v, 48)));
+}
 template <typename T, typename Op>
 __device__ __forceinline__ T wave_reduce(T v, Op op) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = op(v, __shfl_xor(v, o, kWave));
-  return v;
+  return wave_all(v, op);
 }
+__device__ __forceinline__ double wave_sum_f64(double v) { return wave_all(v, SumOp()); }
 
 // Every thread receives the reduction of `v` over the block. `scratch` holds
 // NT / 64 values; the leading barrier makes back-to-back calls safe.
@@ -104,75 +158,22 @@ __device__ __forceinline__ T block_reduce(T v, Op op, T* scratch) {
   return r;
 }
 
-struct MaxOp {
-  template <typename T> __device__ __forceinline__ T operator()(T a, T b) const { return a > b ? a : b; }
-};
-struct MinOp {
-  template <typename T> __device__ __forceinline__ T operator()(T a, T b) const { return a < b ? a : b; }
-};
-struct SumOp {
-  template <typename T> __device__ __forceinline__ T operator()(T a, T b) const { return a + b; }
-};
-
-// Wave reductions without LDS: DPP row rotations (by 8, 4, 2, 1 lanes) give
-// every lane the value of its row of 16, and four lane reads combine the
-// rows. The result is uniform (every lane holds it).
-template <int CTRL>
-__device__ __forceinline__ int dpp_ror(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
-template <typename T, typename Op>
-__device__ __forceinline__ T wave_all(T v, Op op) {
-  static_assert(sizeof(T) == 4, "32-bit values");
-  auto rot = [](T x, auto ctrl) {
-    const int b = dpp_ror<decltype(ctrl)::value>(__builtin_bit_cast(int, x));
-    return __builtin_bit_cast(T, b);
-  };
-  v = op(v, rot(v, std::integral_constant<int, 0x128>()));
-  v = op(v, rot(v, std::integral_constant<int, 0x124>()));
-  v = op(v, rot(v, std::integral_constant<int, 0x122>()));
-  v = op(v, rot(v, std::integral_constant<int, 0x121>()));
-  const int b = __builtin_bit_cast(int, v);
-  const T r0 = __builtin_bit_cast(T, __builtin_amdgcn_readlane(b, 0));
-  const T r1 = __builtin_bit_cast(T, __builtin_amdgcn_readlane(b, 16));
-  const T r2 = __builtin_bit_cast(T, __builtin_amdgcn_readlane(b, 32));
-  const T r3 = __builtin_bit_cast(T, __builtin_amdgcn_readlane(b, 48));
-  return op(op(r0, r1), op(r2, r3));
-}
-__device__ __forceinline__ double wave_sum_f64(double v) {
-  auto rot = [](double x, auto ctrl) {
-    const int2 h = __builtin_bit_cast(int2, x);
-    int2 o;
-    o.x = dpp_ror<decltype(ctrl)::value>(h.x);
-    o.y = dpp_ror<decltype(ctrl)::value>(h.y);
-    return __builtin_bit_cast(double, o);
-  };
-  v += rot(v, std::integral_constant<int, 0x128>());
-  v += rot(v, std::integral_constant<int, 0x124>());
-  v += rot(v, std::integral_constant<int, 0x122>());
-  v += rot(v, std::integral_constant<int, 0x121>());
-  const int2 h = __builtin_bit_cast(int2, v);
-  double r[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    int2 q;
-    q.x = __builtin_amdgcn_readlane(h.x, 16 * k);
-    q.y = __builtin_amdgcn_readlane(h.y, 16 * k);
-    r[k] = __builtin_bit_cast(double, q);
-  }
-  return (r[0] + r[1]) + (r[2] + r[3]);
-}
-
-// Inclusive prefix sum over a wave.
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int n = __shfl_up(v, o, kWave);
-    if (lane >= o) v += n;
-  }
+// Inclusive prefix sum over the wave: right shifts by 1, 2, 4 and 8 lanes
+// scan each row of 16, then row broadcasts carry the last lane of row 0
+// into row 1 and of row 2 into row 3 (broadcast 15), and the last lane of
+// row 1 into rows 2 and 3 (broadcast 31). Every lane must be active.
+template <typename T>
+__device__ __forceinline__ T wave_scan_incl(T v) {
+  v += dpp_val<0x111>(v);
+  v += dpp_val<0x112>(v);
+  v += dpp_val<0x114>(v);
+  v += dpp_val<0x118>(v);
+  v += dpp_val<0x142, 0xA>(v);
+  v += dpp_val<0x143, 0xC>(v);
   return v;
 }
+
+__device__ __forceinline__ int wave_inclusive_scan(int v) { return wave_scan_incl(v); }
 
 // Exclusive prefix sum over the block; `total` receives the block sum.
 // `scratch` holds NT / 64 ints.

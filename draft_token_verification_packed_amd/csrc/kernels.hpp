@@ -25,7 +25,7 @@ namespace vsv {
 #define VSV_UNROLL 2
 #endif
 #ifndef VSV_UNROLL_SAMPLED
-#define VSV_UNROLL_SAMPLED 2
+#define VSV_UNROLL_SAMPLED 3
 #endif
 constexpr int kVerifyThreads = VSV_VERIFY_THREADS;
 constexpr int kGreedyThreads = VSV_GREEDY_THREADS;
@@ -64,11 +64,15 @@ struct VerifyArgs {
   // and nothing has to be cleared afterwards:
   //  ws_epoch [1] calls completed on this workspace; the call's tag is
   //           derived from it and the last workgroup advances it
+  //  ws_queue [kQueueWords] sampled verification's row queue: the next row
+  //           to hand out and the workgroups done; the last workgroup of a
+  //           call resets both to 0
   //  ws_row   [R] 64-bit words; a row handled by one workgroup stores the
   //           token it emits | kAcceptBit if its draft was accepted
   //  ws_part  [(R + kMaxGroups) * kPartWords] 64-bit words; slot r + p holds
   //           the partial statistics persistent workgroup p gathered for row r
   uint32_t* ws_epoch;
+  uint32_t* ws_queue;
   uint64_t* ws_row;
   uint64_t* ws_part;
 };
@@ -98,8 +102,13 @@ inline bool greedy_persistent(int32_t R, int32_t groups) {
   return groups > 0 && static_cast<int64_t>(R) <= static_cast<int64_t>(kMaxLocalRows - 1) * groups;
 }
 
-// Workspace layout (bytes, 256-aligned pieces).
+// Workspace layout (bytes, 256-aligned pieces). The first piece holds the
+// call counter (offset 0) and the row queue's two words (offsets 64 and 128,
+// apart so that they sit in different cache lines).
 constexpr size_t kWsAlign = 256;
+constexpr int kQueueNext = 0;
+constexpr int kQueueDone = 16;
+constexpr int kQueueWords = 17;
 inline size_t ws_align(size_t b) { return (b + kWsAlign - 1) / kWsAlign * kWsAlign; }
 inline size_t ws_row_bytes(int32_t R) { return ws_align(static_cast<size_t>(R > 0 ? R : 1) * 8); }
 inline size_t ws_bytes(int32_t B, int32_t R, int32_t /*sampled*/) {

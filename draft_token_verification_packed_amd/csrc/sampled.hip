@@ -1,0 +1,132 @@
+// Sampled verification kernel (gfx950): rows of requests with temperature
+// > 0 draw their token (sampled_row.hpp), rows of greedy requests take the
+// arg-max, and the per-request scan (verify_common.hpp) ends the launch.
+#include "verify_common.hpp"
+#include "sampled_row.hpp"
+
+namespace vsv {
+
+// ---------------------------------------------------------------- sampled
+
+// Rows of requests with temperature > 0 draw their token (sampled_row.hpp);
+// rows of greedy requests take the arg-max exactly as verify_greedy does.
+// Acceptance is strict: the draft must equal the row's token.
+//
+// A sampled row costs several times a greedy one, and the hardware's
+// in-order workgroup dispatch leaves CUs idle behind such uneven rows. So
+// the grid is persistent (as many workgroups as fit on the device at once)
+// and each workgroup takes rows from a queue in the workspace. It asks for
+// its next row once the current row has been read from memory, so the
+// request's latency hides behind the row's last steps while the rows still
+// go to the workgroups that free up first. The workgroup that finishes last
+// resets the queue and runs the per-request scan.
+template <typename E, int NT, int U, typename Hook>
+__device__ __forceinline__ void sampled_kernel_row(const VerifyArgs& a, uint32_t tag, int r, SampledLds<NT>& L,
+                                                   Hook after_stream) {
+  const E* __restrict__ row = static_cast<const E*>(a.logits) + static_cast<int64_t>(r) * a.ld;
+  const RowMeta m = load_meta(a, r, a.owner[r]);
+  const float T = a.temperature[m.req < 0 ? 0 : m.req];
+  int token = 0, bits = 0, slow = 0;
+  double lse = 0.0;
+  if (m.req >= 0 && T > 0.f) {
+    const SampledOut o = sampled_row<E, NT, kUnrollSampled>(a, row, m.req, m.j, T, L, after_stream);
+    token = o.token;
+    lse = o.lse;
+    bits = o.bits;
+    slow = o.slow;
+  } else {
+    RowPartial p;
+    partial_init(p);
+    GroupKeep<U> keep{};
+    constexpr float kLog2e = 1.4426950408889634f;
+    stream_row<E, NT, U, false>(row, a.V, kLog2e, INFINITY, 0, p, keep);
+    after_stream();
+    const RowResult res = finish_row<E, NT, U, false, true>(p, L.rs, keep, row, a.V);
+    token = res.argmax;
+    lse = res.lse;
+    if (!(res.max < INFINITY) || token == INT32_MAX || !isfinite(res.lse)) bits |= VSV_FLAG_LOGITS;
+    if (token == INT32_MAX) token = 0;
+    if (m.req >= 0 && !(T >= 0.f)) bits |= VSV_FLAG_PARAMS;
+  }
+  if (threadIdx.x == 0) {
+    const uint32_t word = row_word(a, m, token, m.draft == token, bits);
+    if (bits) set_flag(a, bits);
+    if (slow && a.slow_rows) atomicAdd(a.slow_rows, 1);
+    if (a.row_token) a.row_token[r] = token;
+    if (a.row_lse) a.row_lse[r] = static_cast<float>(lse);
+    store_agent64(a.ws_row + r, tagged(tag, word));
+  }
+}
+
+__device__ __forceinline__ uint32_t queue_take(const VerifyArgs& a) {
+  return __hip_atomic_fetch_add(a.ws_queue + kQueueNext, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename E, int NT, int U>
+__global__ __launch_bounds__(NT) void verify_sampled_kernel(VerifyArgs a) {
+  __shared__ SampledLds<NT> L;
+  static_assert(sizeof(TailScratch) <= sizeof(L.elem), "tail staging aliases the candidate buffers");
+  const uint32_t tag = call_tag(a);
+  if (threadIdx.x == 0) L.row_next = static_cast<int>(min(queue_take(a), static_cast<uint32_t>(a.R)));
+  __syncthreads();
+  int r = L.row_next;
+  while (r < a.R) {
+    // the next row's ticket is in flight during the row's last steps; the
+    // row's barriers separate this read of row_next from the write below
+    uint32_t next = 0;
+    sampled_kernel_row<E, NT, U>(a, tag, r, L, [&]() {
+      if (threadIdx.x == 0) next = queue_take(a);
+    });
+    if (threadIdx.x == 0) L.row_next = static_cast<int>(min(next, static_cast<uint32_t>(a.R)));
+    __syncthreads();
+    r = L.row_next;
+  }
+  // Every ticket of this workgroup has been taken and its rows published
+  // (release); the last workgroup to get here sees all rows (acquire).
+  if (threadIdx.x == 0) {
+    const uint32_t done = __hip_atomic_fetch_add(a.ws_queue + kQueueDone, 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    L.last = done + 1 == gridDim.x;
+  }
+  __syncthreads();
+  if (L.last) {
+    if (threadIdx.x == 0) {
+      store_agent(a.ws_queue + kQueueNext, 0u);
+      store_agent(a.ws_queue + kQueueDone, 0u);
+    }
+    words_tail<NT>(a, tag, *reinterpret_cast<TailScratch*>(&L.elem[0][0]));
+  }
+}
+
+// Workgroups of the sampled kernel that fit on the current device at once
+// (cached per device), or 0 if unknown.
+template <typename E>
+static int sampled_resident(int cus) {
+  static int cached[64];
+  int dev = 0;
+  if (cus <= 0 || hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, verify_sampled_kernel<E, kVerifyThreads, kUnroll>,
+                                                   kVerifyThreads, 0) != hipSuccess ||
+      per_cu <= 0)
+    return 0;
+  const int n = per_cu * cus;
+  if (dev < 64) cached[dev] = n;
+  return n;
+}
+
+template <typename E>
+static hipError_t launch_sampled_t(const VerifyArgs& a, hipStream_t s) {
+  int grid = sampled_resident<E>(a.groups);
+  if (grid <= 0) grid = 256;
+  if (grid > a.R) grid = a.R;
+  verify_sampled_kernel<E, kVerifyThreads, kUnroll><<<dim3(grid), dim3(kVerifyThreads), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify_sampled(const VerifyArgs& a, hipStream_t s) {
+  return a.dtype == VSV_BF16 ? launch_sampled_t<uint16_t>(a, s) : launch_sampled_t<float>(a, s);
+}
+
+}  // namespace vsv

@@ -90,6 +90,8 @@ template <int NT> struct SampledLds {
   int red_i[NW];
   double red_d[2 * NW];
   RowScratch<NT> rs;
+  int row_next;  // the workgroup's next row (row queue)
+  int last;      // this workgroup finished the call's last row
 };
 
 // Per-wave capture state; every lane holds the same values.
@@ -170,7 +172,7 @@ __device__ bool wave_compact(SampledLds<NT>& L, WaveCap& s, int target) {
   const int b = reach ? __builtin_ctzll(reach) : 63;
   // entries of bins 0 .. b-1 stay; refine bin b with 64 sub-bins so that the
   // kept count lands near the target instead of jumping a whole bin
-  const int before_b = uni(__shfl(incl - c1, b, kWave));
+  const int before_b = read_lane(incl - c1, b);
   const float bhi = hi - static_cast<float>(b) / inv;
   const float sinv = inv * 64.0f;
   L.whist[w][lane] = 0;
@@ -198,70 +200,77 @@ __device__ bool wave_compact(SampledLds<NT>& L, WaveCap& s, int target) {
   return s.elem_n < before;
 }
 
-// Move the parked vectors' elements above the threshold into the buffer.
+// Move the parked vectors' elements at or above the threshold into the
+// buffer. Lane l reads 32-bit word l % 4 of parked vector l / 4 (one or two
+// elements), so a step covers 16 vectors with one compare, ballot and write
+// per element; the words of four steps (64 vectors) are read together, so a
+// batch costs a single LDS round trip. When a batch does not fit, the buffer
+// is compacted first (which raises the threshold) and the batch re-tested.
 template <typename E, int NT>
-__device__ void wave_drain(SampledLds<NT>& L, WaveCap& s) {
-  constexpr int N = Elem<E>::kVec;
+__device__ __forceinline__ void wave_drain(SampledLds<NT>& L, WaveCap& s) {
+  constexpr int EPW = 4 / sizeof(E);   // elements per 32-bit word
+  constexpr int kStep = kWave / 4;     // vectors per step
+  constexpr int kBatch = 4;            // steps per batch
+  constexpr int M = kBatch * EPW;      // elements per lane per batch
   const int w = wave_id(), lane = lane_id();
   if (s.ring_n == 0) return;
   wave_lds_sync();
-  float f0[N], f1[N];
-  int e0 = 0, e1 = 0;
-  const bool h0 = lane < s.ring_n, h1 = lane + kWave < s.ring_n;
+  const int q = lane & 3, jl = lane >> 2;
+  const uint32_t* ring = reinterpret_cast<const uint32_t*>(&L.u.ring.v[w][0]);
+  for (int j0 = 0; j0 < s.ring_n; j0 += kStep * kBatch) {
+    float x[M];
+    int e[M];
+    bool have[kBatch];
 #pragma unroll
-  for (int k = 0; k < N; ++k) f0[k] = f1[k] = -INFINITY;
-  if (h0) {
-    Elem<E>::decode(L.u.ring.v[w][lane], f0);
-    e0 = L.u.ring.e0[w][lane];
-  }
-  if (h1) {
-    Elem<E>::decode(L.u.ring.v[w][lane + kWave], f1);
-    e1 = L.u.ring.e0[w][lane + kWave];
-  }
-  for (int attempt = 0; attempt < 8; ++attempt) {
-    uint32_t m0 = 0, m1 = 0;
+    for (int b = 0; b < kBatch; ++b) {
+      const int jj = j0 + b * kStep + jl;
+      have[b] = jj < s.ring_n;
+      const int j = min(jj, kRing - 1);
+      const uint32_t word = ring[j * 4 + q];
+      const int e0 = L.u.ring.e0[w][j] + q * EPW;
 #pragma unroll
-    for (int k = 0; k < N; ++k) {
-      m0 |= (f0[k] >= s.tau ? 1u : 0u) << k;
-      m1 |= (f1[k] >= s.tau ? 1u : 0u) << k;
+      for (int h = 0; h < EPW; ++h) {
+        x[b * EPW + h] = EPW == 1 ? __uint_as_float(word)
+                                  : __uint_as_float(h == 0 ? (word << 16) : (word & 0xFFFF0000u));
+        e[b * EPW + h] = e0 + h;
+      }
     }
-    const int cnt = __popc(m0) + __popc(m1);
-    const int incl = wave_inclusive_scan(cnt);
-    const int total = uni(__shfl(incl, kWave - 1, kWave));
-    if (s.elem_n + total <= kEW) {
-      Cand* dst = L.elem[w] + s.elem_n + (incl - cnt);
-      int o = 0;
+    auto count = [&]() {
+      int n = 0;
 #pragma unroll
-      for (int k = 0; k < N; ++k)
-        if (m0 & (1u << k)) dst[o++] = Cand{f0[k], e0 + k};
-#pragma unroll
-      for (int k = 0; k < N; ++k)
-        if (m1 & (1u << k)) dst[o++] = Cand{f1[k], e1 + k};
-      s.elem_n += total;
-      break;
+      for (int i = 0; i < M; ++i) n += __popcll(__ballot(have[i / EPW] && x[i] >= s.tau));
+      return n;
+    };
+    if (s.elem_n + count() > kEW) {
+      // A top-k row keeps only its top_k + 32: the k-th largest of the
+      // elements seen so far can only rise, so it is a safe threshold, and
+      // a high one parks far fewer vectors later. Other rows keep half.
+      if (!wave_compact<NT>(L, s, s.kmin > 0 ? s.kmin : kEW / 2) || s.elem_n + count() > kEW) {
+        s.ovf = 1;
+        s.tau = INFINITY;  // stop capturing: this row goes to the exact path
+        break;
+      }
     }
-    // Leave room for what is arriving; each round raises the threshold,
-    // which also thins the arrivals. A top-k row keeps only its top_k + 32:
-    // the k-th largest of the elements seen so far can only rise, so it is a
-    // safe threshold, and a high one parks far fewer vectors later.
-    const int target = s.kmin > 0 ? s.kmin : max(kEW / 8, min(kEW / 2, kEW - total));
-    if (attempt == 7 || !wave_compact<NT>(L, s, target)) {
-      s.ovf = 1;
-      s.tau = INFINITY;  // stop capturing: this row goes to the exact path
-      break;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const bool take = have[i / EPW] && x[i] >= s.tau;
+      const uint64_t bal = __ballot(take);
+      if (take) L.elem[w][s.elem_n + mbcnt(bal)] = Cand{x[i], e[i]};
+      s.elem_n += __popcll(bal);
     }
   }
   s.ring_n = 0;
   wave_lds_sync();
 }
 
-// Park vector `w` (elements e0 ..) if its max clears the threshold.
-template <typename E, int NT>
-__device__ __forceinline__ void wave_park(SampledLds<NT>& L, WaveCap& s, const u32x4& v, int e0, float vmax,
-                                          bool valid) {
+// Park without draining; returns true when the ring needs a drain before
+// the next park.
+template <int NT>
+__device__ __forceinline__ bool wave_park_only(SampledLds<NT>& L, WaveCap& s, const u32x4& v, int e0, float vmax,
+                                               bool valid) {
   const bool take = valid && vmax >= s.tau;
   const uint64_t bal = __ballot(take);
-  if (bal == 0) return;
+  if (bal == 0) return false;
   const int w = wave_id();
   if (take) {
     const int pos = s.ring_n + mbcnt(bal);
@@ -269,7 +278,20 @@ __device__ __forceinline__ void wave_park(SampledLds<NT>& L, WaveCap& s, const u
     L.u.ring.e0[w][pos] = e0;
   }
   s.ring_n += __popcll(bal);
-  if (s.ring_n > kRing - kWave) wave_drain<E, NT>(L, s);
+  return s.ring_n > kRing - kWave;
+}
+
+// Row statistics of one decoded vector: running max and exponent sum (a
+// sampled row needs no argmax position).
+template <int N>
+__device__ __forceinline__ void take_floats(RowPartial& p, const float* f, float vmax, float c) {
+  p.best = fmaxf(p.best, vmax);
+  partial_rebase(p, vmax, c);
+  const float nmc = -p.mc;
+  float e[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) e[k] = fast_exp2(fmaf(f[k], c, nmc));
+  p.s += static_cast<double>(tree_sum<N>(e));
 }
 
 // Append single elements (row head / tail) directly to the buffer.
@@ -294,6 +316,18 @@ __device__ __forceinline__ void wave_take_scalar(SampledLds<NT>& L, WaveCap& s, 
   if (take2) L.elem[wave_id()][s.elem_n + mbcnt(bal2)] = Cand{x, e};
   s.elem_n += __popcll(bal2);
   wave_lds_sync();
+}
+
+// Starting threshold from the whole block's first group: every wave
+// publishes its max before any reads it back.
+template <int NT>
+__device__ __forceinline__ void block_start_max(SampledLds<NT>& L, WaveCap& s, float lane_best) {
+  const float wm = wave_reduce(lane_best, MaxOp());
+  if (lane_id() == 0 && wm > -INFINITY) atomicMax(&L.mkey, ord_key(wm));
+  __syncthreads();
+  const float m = key_float(uni(L.mkey));
+  const float t = m - s.dcap;
+  if (t > s.tau) s.tau = t;
 }
 
 // Share the wave's running max and pull in the block's.
@@ -327,11 +361,7 @@ __device__ __forceinline__ double weight(float x, float m, double T) {
 template <int NT, typename T>
 __device__ __forceinline__ T block_scan_incl(T v, T* scr, T& total) {
   const int lane = lane_id(), w = wave_id();
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const T n = __shfl_up(v, o, kWave);
-    if (lane >= o) v += n;
-  }
+  v = wave_scan_incl(v);
   __syncthreads();
   if (lane == kWave - 1) scr[w] = v;
   __syncthreads();
@@ -849,9 +879,9 @@ __device__ bool decide(Loc& loc, int V, int top_k, double top_p, double min_p, d
 namespace vsv {
 
 // Stream one sampled row: the statistics of stream_row plus candidate capture.
-template <typename E, int NT, int U, typename Hook>
-__device__ void stream_sampled(const E* __restrict__ row, int V, float c, RowPartial& p, SampledLds<NT>& L,
-                               WaveCap& s, Hook hook) {
+template <typename E, int NT, int U>
+__device__ __forceinline__ void stream_sampled(const E* __restrict__ row, int V, float c, RowPartial& p,
+                                               SampledLds<NT>& L, WaveCap& s) {
   constexpr int N = Elem<E>::kVec;
   const int tid = threadIdx.x;
   const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
@@ -860,23 +890,22 @@ __device__ void stream_sampled(const E* __restrict__ row, int V, float c, RowPar
   const int nvec = (V - head) / N;
   const int body_end = head + nvec * N;
   const u32x4* __restrict__ vp = reinterpret_cast<const u32x4*>(row + head);
-  // One buffer plus the next group's loads: the next group is in flight
-  // while the current one is reduced and captured (loads are unconditional,
-  // load_group in row_stream.hpp). A second full buffer would double the
-  // inlined capture code and its registers.
+  // Rolling slots: slot u holds vector g*G + u*NT + tid of group g; it is
+  // decoded and parked, then reloaded at once with the same vector of group
+  // g+1, so U-1 vectors per lane are always in flight and the loop carries
+  // no register copies (a copy at the latch would wait for every load).
+  // Loads are unconditional (clamped as in load_group, row_stream.hpp).
   constexpr int G = U * NT;
   const int nfull = nvec / G;
-  NoKeep nokeep;
 
-  // head elements first: a load issued after the groups' would make the
-  // first wait cover the prefetch too
+  // head elements first: a load issued after the slots' would make the
+  // first wait cover them too
   const bool has_head = tid < head;
   const float xh = has_head ? Elem<E>::at(row, tid) : -INFINITY;
-  u32x4 cur[U];
-  if (nvec > 0) load_group<NT, U>(cur, vp, 0, nvec);
-  hook();
+  u32x4 slot[U];
+  if (nvec > 0) load_group<NT, U>(slot, vp, 0, nvec);
 
-  // Starting threshold: the wave's max over its first group (and head).
+  // Starting threshold: the block's max over its first group (and head).
   {
     float m0 = xh;
     if (nvec > 0) {
@@ -884,27 +913,31 @@ __device__ void stream_sampled(const E* __restrict__ row, int V, float c, RowPar
       for (int u = 0; u < U; ++u) {
         if (tid + u * NT < nvec) {
           float f[N];
-          m0 = fmaxf(m0, vec_max<E>(cur[u], f));
+          m0 = fmaxf(m0, vec_max<E>(slot[u], f));
         }
       }
     }
-    wave_sync_max<NT>(L, s, m0);
+    block_start_max<NT>(L, s, m0);
   }
   if (has_head) take_scalar<false>(p, xh, tid, c, INFINITY, 0);
   wave_take_scalar<NT>(L, s, xh, tid, has_head);
 
   if (nvec > 0) {
     for (int g = 0; g < nfull; ++g) {
-      u32x4 nxt[U];
-      load_group<NT, U>(nxt, vp, g + 1, nvec);
       const int v = g * G + tid;
-      take_group<E, U, NT, false>(p, cur, v, head, c, INFINITY, 0, nokeep, 0, [&](int u, float vmax) {
-        wave_park<E, NT>(L, s, cur[u], head + (v + u * NT) * N, vmax, true);
-      });
-      if ((g & 3) == 0) wave_sync_max<NT>(L, s, p.best);
 #pragma unroll
-      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+      for (int u = 0; u < U; ++u) {
+        float f[N];
+        const float vmax = vec_max<E>(slot[u], f);
+        const int e0 = head + (v + u * NT) * N;
+        const bool full = wave_park_only<NT>(L, s, slot[u], e0, vmax, true);
+        slot[u] = load_stream(vp + min(v + G + u * NT, nvec - 1));
+        take_floats<N>(p, f, vmax, c);
+        if (full) wave_drain<E, NT>(L, s);
+      }
+      wave_sync_max<NT>(L, s, p.best);
     }
+    // the slots now hold group nfull, the partial last one
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int q = nfull * G + tid + u * NT;
@@ -912,10 +945,10 @@ __device__ void stream_sampled(const E* __restrict__ row, int V, float c, RowPar
       float f[N];
       float vmax = -INFINITY;
       if (valid) {
-        vmax = vec_max<E>(cur[u], f);
-        take_vector<E, false>(p, cur[u], head + q * N, c, INFINITY, 0);
+        vmax = vec_max<E>(slot[u], f);
+        take_floats<N>(p, f, vmax, c);
       }
-      wave_park<E, NT>(L, s, cur[u], head + q * N, vmax, valid);
+      if (wave_park_only<NT>(L, s, slot[u], head + q * N, vmax, valid)) wave_drain<E, NT>(L, s);
     }
   }
 
@@ -936,10 +969,10 @@ struct SampledOut {
 };
 
 // One workgroup samples row `row` of request `req` (local row j) at
-// temperature T > 0. `hook` is forwarded to the stream.
+// temperature T > 0. `after_stream` runs once the row has been read.
 template <typename E, int NT, int U, typename Hook>
 __device__ __forceinline__ SampledOut sampled_row(const VerifyArgs& a, const E* __restrict__ row, int req, int j, float T,
-                                  SampledLds<NT>& L, Hook hook) {
+                                  SampledLds<NT>& L, Hook after_stream) {
   SampledOut out{0, 0.0, 0, 0};
   int top_k = a.top_k[req];
   float top_p = a.top_p[req];
@@ -974,7 +1007,8 @@ __device__ __forceinline__ SampledOut sampled_row(const VerifyArgs& a, const E* 
 
   RowPartial p;
   partial_init(p);
-  stream_sampled<E, NT, U>(row, a.V, c, p, L, s, hook);
+  stream_sampled<E, NT, U>(row, a.V, c, p, L, s);
+  after_stream();
   if (lane_id() == 0) {
     L.wtau[w] = s.ovf ? INFINITY : s.tau;
     L.wn[w] = s.elem_n;

@@ -1,192 +1,19 @@
-// Packed draft-token verification kernels (gfx950).
+// Greedy verification kernels (gfx950).
 //
-// One launch verifies a whole ragged batch; packing boundaries stay on the
-// device and nothing waits on the host (xLLM docs, "Adaptive speculative
-// inference", DSpark section "Launch example").
+// Persistent: one workgroup per CU streams an equal share of the batch's
+// chunks (kernels.hpp) and stores one partial per row it touched (max and
+// its lowest index, exponent reference and sum of exponentials, rank count;
+// the workgroup holding a row's first chunk adds the row's draft
+// information). The last workgroup merges each row, decides its token and
+// acceptance, and runs the per-request scan (verify_common.hpp). No atomics
+// on global memory.
 //
-// Greedy (persistent): one workgroup per CU streams an equal share of the
-// batch's chunks (kernels.hpp) and stores one partial per row it touched
-// (max and its lowest index, exponent reference and sum of exponentials,
-// rank count; the workgroup holding a row's first chunk adds the row's
-// draft information). The last workgroup merges each row, decides its token
-// and acceptance, and runs the per-request scan.
-//
-// Sampled, and greedy batches with many rows per CU: one workgroup per row
-// decides the row and stores its word (emitted token, accept bit); the
-// workgroup of the last row runs the same per-request scan.
-//
-// The per-request scan: prefix-accept count per request, exclusive scan of
-// emitted lengths over the batch, scatter of emitted tokens. No second
-// launch, no atomics on global memory, and nothing to clear afterwards:
-// every word handed between workgroups carries the call's tag.
-#include "kernels.hpp"
-#include "row_stream.hpp"
-#include "sampled_row.hpp"
+// Batches with many rows per CU: one workgroup per row decides the row and
+// stores its word (emitted token, accept bit); the workgroup of the last row
+// runs the same per-request scan.
+#include "verify_common.hpp"
 
 namespace vsv {
-
-constexpr uint32_t kAcceptBit = 0x80000000u;
-constexpr uint32_t kTokenMask = 0x3FFFFFFFu;
-constexpr uint32_t kNoDraft = kTokenMask;     // never a valid token (vocab < 2^30)
-// Polls one thread of a tail may spend waiting, over all the words it reads
-// (each poll waits for a load from the device-coherent level, about a
-// microsecond): past it the tail stops waiting, uses what it has and flags
-// the launch, so the grid always drains within a fraction of a second.
-constexpr int kPollBudget = 1 << 18;
-
-// ---------------------------------------------------------------- call tags
-
-// The tag of this call: derived from the workspace's call counter, never 0
-// and different from the previous 2^31 - 1 calls' tags.
-__device__ __forceinline__ uint32_t call_tag(const VerifyArgs& a) {
-  return ((load_agent(a.ws_epoch) + 1u) & 0x7FFFFFFFu) | 0x80000000u;
-}
-__device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t v) {
-  return (static_cast<uint64_t>(tag) << 32) | v;
-}
-// Wait (within the thread's poll budget) for the word at `w` to carry `tag`.
-__device__ __forceinline__ uint32_t poll_tagged(const uint64_t* w, uint32_t tag, int& budget, int& stalled) {
-  uint64_t x = load_agent64(w);
-  while (static_cast<uint32_t>(x >> 32) != tag && budget > 0) {
-    --budget;
-    __builtin_amdgcn_s_sleep(2);
-    x = load_agent64(w);
-  }
-  stalled |= (static_cast<uint32_t>(x >> 32) == tag) ? 0 : 1;
-  return static_cast<uint32_t>(x);
-}
-// The last workgroup ends the call: the next call uses the next tag.
-__device__ __forceinline__ void end_call(const VerifyArgs& a, uint32_t tag) {
-  if (threadIdx.x == 0) store_agent(a.ws_epoch, tag & 0x7FFFFFFFu);
-}
-
-// ---------------------------------------------------------------- rows
-
-// Per-row metadata: request, local row, draft token.
-struct RowMeta {
-  int req;    // owning request (-1 if the owner map is inconsistent)
-  int j;      // local row within the request
-  int K;      // draft rows of the request
-  int draft;  // draft token for verify rows, -1 otherwise
-};
-
-// Metadata of row r whose owner entry has already been read as `i`.
-__device__ __forceinline__ RowMeta load_meta(const VerifyArgs& a, int r, int i) {
-  RowMeta m{-1, 0, 0, -1};
-  if (i < 0 || i >= a.B) return m;
-  const int r0 = a.offsets[i];
-  const int r1 = a.offsets[i + 1];
-  const int q = r - i;
-  const int dq = (q >= 0 && q < a.R - a.B) ? a.drafts[q] : -1;
-  if (r < r0 || r >= r1) return m;
-  m.req = i;
-  m.j = r - r0;
-  m.K = r1 - r0 - 1;
-  m.draft = (m.j < m.K) ? dq : -1;
-  return m;
-}
-
-__device__ __forceinline__ void set_flag(const VerifyArgs& a, int bits) {
-  if (a.error_flag) atomicOr(a.error_flag, bits);
-}
-
-// The word a row hands to the scan: the draft (accepted) or its own target
-// token. Flags layout and token-range problems in `bits`.
-__device__ __forceinline__ uint32_t row_word(const VerifyArgs& a, const RowMeta& m, int token, bool accept_ok,
-                                             int& bits) {
-  if (m.req < 0) {
-    bits |= VSV_FLAG_LAYOUT;
-    return static_cast<uint32_t>(token);
-  }
-  if (m.j < m.K) {
-    if (m.draft < 0 || m.draft >= a.V) {
-      bits |= VSV_FLAG_TOKEN;
-    } else if (accept_ok) {
-      return static_cast<uint32_t>(m.draft) | kAcceptBit;
-    }
-  }
-  return static_cast<uint32_t>(token);
-}
-
-// ---------------------------------------------------------------- scan
-
-// Rows whose words the scan stages in LDS.
-constexpr int kTailStage = 4096;
-
-struct TailScratch {
-  uint32_t words[kTailStage];
-  int scan[16];
-};
-
-// Row offsets of request i and the next one (the tails load those of the
-// first NT requests early, so the scan does not wait for them).
-struct ReqRange {
-  int r0, r1;
-};
-__device__ __forceinline__ ReqRange load_range(const VerifyArgs& a, int i) {
-  return i < a.B ? ReqRange{a.offsets[i], a.offsets[i + 1]} : ReqRange{0, 0};
-}
-
-// Per-request scan over the row words (token | kAcceptBit if the row's draft
-// was accepted): prefix-accept count, exclusive scan of (a_i + 1), scatter of
-// the emitted tokens. `word(r)` returns row r's word; `first` holds the range
-// of request tid.
-template <int NT, typename Word>
-__device__ __forceinline__ void scan_requests(const VerifyArgs& a, TailScratch& t, ReqRange first, Word word) {
-  const int tid = threadIdx.x;
-  int carry = 0;
-  for (int base = 0; base < a.B; base += NT) {
-    const int i = base + tid;
-    int acc = 0, r0 = 0, len = 0;
-    uint32_t nxt = 0;
-    bool ok = false;
-    if (i < a.B) {
-      const ReqRange rg = base == 0 ? first : load_range(a, i);
-      r0 = rg.r0;
-      const int r1 = rg.r1;
-      ok = r0 >= 0 && r1 > r0 && r1 <= a.R && (i != 0 || r0 == 0) && (i != a.B - 1 || r1 == a.R);
-      if (ok) {
-        const int K = r1 - r0 - 1;
-        while (acc < K && (word(r0 + acc) & kAcceptBit)) ++acc;
-        nxt = word(r0 + acc);
-      } else {
-        set_flag(a, VSV_FLAG_LAYOUT);
-      }
-      len = acc + 1;
-    }
-    int total = 0;
-    const int pos = carry + block_exclusive_scan<NT>(len, t.scan, total);
-    if (i < a.B) {
-      const int nt = static_cast<int>(nxt & kTokenMask);
-      a.accepted_len[i] = acc;
-      a.next_token[i] = nt;
-      a.out_offsets[i] = pos;
-      if (ok)
-        for (int q = 0; q < acc && pos + q < a.R; ++q) a.out_tokens[pos + q] = static_cast<int>(word(r0 + q) & kTokenMask);
-      if (pos + acc < a.R) a.out_tokens[pos + acc] = nt;
-    }
-    carry += total;
-  }
-  if (tid == 0) a.out_offsets[a.B] = carry;
-}
-
-// Run by the workgroup of row R - 1 after its own row (rows handled by one
-// workgroup each): gather every row's word (the first kTailStage in LDS,
-// later ones where they are read) and run the per-request scan.
-template <int NT>
-__device__ __forceinline__ void words_tail(const VerifyArgs& a, uint32_t tag, TailScratch& t) {
-  const int tid = threadIdx.x;
-  const ReqRange first = load_range(a, tid);
-  int stalled = 0, budget = kPollBudget;
-  const int staged = min(a.R, kTailStage);
-  for (int k = tid; k < staged; k += NT) t.words[k] = poll_tagged(a.ws_row + k, tag, budget, stalled);
-  __syncthreads();
-  scan_requests<NT>(a, t, first, [&](int row) -> uint32_t {
-    return row < staged ? t.words[row] : poll_tagged(a.ws_row + row, tag, budget, stalled);
-  });
-  if (stalled) set_flag(a, VSV_FLAG_STALLED);
-  end_call(a, tag);
-}
 
 // ---------------------------------------------------------------- greedy
 
@@ -633,62 +460,6 @@ hipError_t launch_verify_greedy(const VerifyArgs& a, hipStream_t s) {
   if (a.dtype == VSV_BF16)
     return a.relaxed_k > 1 ? launch_greedy_t<uint16_t, true>(a, s) : launch_greedy_t<uint16_t, false>(a, s);
   return a.relaxed_k > 1 ? launch_greedy_t<float, true>(a, s) : launch_greedy_t<float, false>(a, s);
-}
-
-// ---------------------------------------------------------------- sampled
-
-// Rows of requests with temperature > 0 draw their token (sampled_row.hpp);
-// rows of greedy requests take the arg-max exactly as verify_greedy does.
-// Acceptance is strict: the draft must equal the row's token.
-template <typename E, int NT, int U>
-__global__ __launch_bounds__(NT) void verify_sampled_kernel(VerifyArgs a) {
-  __shared__ SampledLds<NT> L;
-  static_assert(sizeof(TailScratch) <= sizeof(L.elem), "tail staging aliases the candidate buffers");
-  const int r = blockIdx.x;
-  const uint32_t tag = call_tag(a);
-  const E* __restrict__ row = static_cast<const E*>(a.logits) + static_cast<int64_t>(r) * a.ld;
-  const RowMeta m = load_meta(a, r, a.owner[r]);
-  const float T = a.temperature[m.req < 0 ? 0 : m.req];
-  int token = 0, bits = 0, slow = 0;
-  double lse = 0.0;
-  if (m.req >= 0 && T > 0.f) {
-    const SampledOut o = sampled_row<E, NT, kUnrollSampled>(a, row, m.req, m.j, T, L, NoHook());
-    token = o.token;
-    lse = o.lse;
-    bits = o.bits;
-    slow = o.slow;
-  } else {
-    RowPartial p;
-    partial_init(p);
-    GroupKeep<U> keep{};
-    constexpr float kLog2e = 1.4426950408889634f;
-    stream_row<E, NT, U, false>(row, a.V, kLog2e, INFINITY, 0, p, keep);
-    const RowResult res = finish_row<E, NT, U, false, true>(p, L.rs, keep, row, a.V);
-    token = res.argmax;
-    lse = res.lse;
-    if (!(res.max < INFINITY) || token == INT32_MAX || !isfinite(res.lse)) bits |= VSV_FLAG_LOGITS;
-    if (token == INT32_MAX) token = 0;
-    if (m.req >= 0 && !(T >= 0.f)) bits |= VSV_FLAG_PARAMS;
-  }
-  if (threadIdx.x == 0) {
-    const uint32_t word = row_word(a, m, token, m.draft == token, bits);
-    if (bits) set_flag(a, bits);
-    if (slow && a.slow_rows) atomicAdd(a.slow_rows, 1);
-    if (a.row_token) a.row_token[r] = token;
-    if (a.row_lse) a.row_lse[r] = static_cast<float>(lse);
-    store_agent64(a.ws_row + r, tagged(tag, word));
-  }
-  if (r == a.R - 1) words_tail<NT>(a, tag, *reinterpret_cast<TailScratch*>(&L.elem[0][0]));
-}
-
-template <typename E>
-static hipError_t launch_sampled_t(const VerifyArgs& a, hipStream_t s) {
-  verify_sampled_kernel<E, kVerifyThreads, kUnroll><<<dim3(a.R), dim3(kVerifyThreads), 0, s>>>(a);
-  return hipGetLastError();
-}
-
-hipError_t launch_verify_sampled(const VerifyArgs& a, hipStream_t s) {
-  return a.dtype == VSV_BF16 ? launch_sampled_t<uint16_t>(a, s) : launch_sampled_t<float>(a, s);
 }
 
 // ---------------------------------------------------------------- workspace
