@@ -29,8 +29,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 ROTATE_BYTES = 1 << 30
-KERNEL_SOURCES = ("csrc/device.hpp", "csrc/row_stream.hpp", "csrc/sampled_row.hpp", "csrc/verify.hip",
-                  "csrc/confidence.hip", "csrc/kernels.hpp")
+KERNEL_SOURCES = ("csrc/device.hpp", "csrc/row_stream.hpp", "csrc/sampled_row.hpp", "csrc/verify_common.hpp",
+                  "csrc/verify.hip", "csrc/sampled.hip", "csrc/confidence.hip", "csrc/kernels.hpp")
 
 
 def kernel_source_sha():
