@@ -1,0 +1,131 @@
+"""Mutation check of the oracle's pins (CPU only).
+
+Each mutant plants one plausible mistake in a copy of `oracle/` (a dropped
+term, a wrong tie rule or boundary, an off-by-one index, a swapped filter
+order, a wrong Philox constant). The pin suite `test_oracle_pins.py` then
+runs against the mutant in a subprocess and must fail: a mistake that no
+pin catches would also slip past parity, since parity compares the HIP path
+with this oracle.
+"""
+import concurrent.futures
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")
+
+# (name, file, original text, mutated text); the original must occur once.
+MUTANTS = [
+    ("argmax_last_tie", "verify.py",
+     "return int(np.flatnonzero(x == m)[0])",
+     "return int(np.flatnonzero(x == m)[-1])"),
+    ("lse_drops_max", "verify.py",
+     "return float(m / temperature + math.log(np.sum(np.exp(z))))",
+     "return float(math.log(np.sum(np.exp(z))))"),
+    ("rank_ties_after", "verify.py",
+     "np.count_nonzero(x[:t] == v)",
+     "np.count_nonzero(x[t + 1:] == v)"),
+    ("rank_order_index_desc", "verify.py",
+     "np.lexsort((np.arange(x.shape[0]), -x))",
+     "np.lexsort((-np.arange(x.shape[0]), -x))"),
+    ("topk_keeps_one_more", "verify.py",
+     "        S = S[:top_k]\n    if top_p < 1.0:\n        c = np.cumsum(w[S])\n        W = c[-1]",
+     "        S = S[:top_k + 1]\n    if top_p < 1.0:\n        c = np.cumsum(w[S])\n        W = c[-1]"),
+    ("topp_drops_crossing_token", "verify.py",
+     "L = int(np.flatnonzero(c >= top_p * W)[0]) + 1",
+     "L = max(1, int(np.flatnonzero(c >= top_p * W)[0]))"),
+    ("minp_strict", "verify.py",
+     "keep = z[S] >= math.log(min_p)",
+     "keep = z[S] > math.log(min_p)"),
+    ("temperature_multiplies", "verify.py",
+     "    z = (x - m) / temperature\n    w = np.exp(z)\n    order = rank_order(x)",
+     "    z = (x - m) * temperature\n    w = np.exp(z)\n    order = rank_order(x)"),
+    ("filters_topp_before_topk", "verify.py",
+     "    if 0 < top_k < V:\n        S = S[:top_k]\n    if top_p < 1.0:\n        c = np.cumsum(w[S])\n"
+     "        W = c[-1]\n        L = int(np.flatnonzero(c >= top_p * W)[0]) + 1\n        S = S[:L]\n",
+     "    if top_p < 1.0:\n        c = np.cumsum(w[S])\n        W = c[-1]\n"
+     "        L = int(np.flatnonzero(c >= top_p * W)[0]) + 1\n        S = S[:L]\n"
+     "    if 0 < top_k < V:\n        S = S[:top_k]\n"),
+    ("draw_boundary_inclusive", "verify.py",
+     "n = int(np.flatnonzero(c > u * c[-1])[0])\n    return int(S[n])",
+     "n = int(np.flatnonzero(c >= u * c[-1])[0])\n    return int(S[n])"),
+    ("accepts_not_prefix", "verify.py",
+     "    a = 0\n    while a < len(accepts) and accepts[a]:\n        a += 1\n",
+     "    a = int(sum(bool(v) for v in accepts))\n"),
+    ("next_token_from_last_row", "verify.py",
+     "nxt = int(tokens[a])",
+     "nxt = int(tokens[-1])"),
+    ("offsets_miss_next_token", "verify.py",
+     "out_off[i + 1] = out_off[i] + a + 1",
+     "out_off[i + 1] = out_off[i] + a"),
+    ("relaxed_rank_inclusive", "verify.py",
+     "accepts.append(rank_of(x, t) < relaxed_topk)",
+     "accepts.append(rank_of(x, t) <= relaxed_topk)"),
+    ("greedy_drafts_shifted", "verify.py",
+     "        d = drafts[r0 - i : r0 - i + K]\n        accepts = []\n        for j in range(K + 1):\n"
+     "            x = row_f64(logits, dtype, r0 + j, vocab)\n            check_row(x)\n            row_token[r0 + j] = greedy_token(x)",
+     "        d = drafts[r0 - i + 1 : r0 - i + K + 1]\n        accepts = []\n        for j in range(K + 1):\n"
+     "            x = row_f64(logits, dtype, r0 + j, vocab)\n            check_row(x)\n            row_token[r0 + j] = greedy_token(x)"),
+    ("sampled_lse_ignores_temperature", "verify.py",
+     "row_lse[r0 + j] = logsumexp(x, T[i])",
+     "row_lse[r0 + j] = logsumexp(x)"),
+    ("confidence_against_max", "verify.py",
+     "conf[q] = math.exp(y[s] - lse[q])",
+     "conf[q] = math.exp(y[s] - np.max(y))"),
+    ("philox_multiplier", "philox.py",
+     "PHILOX_M0 = 0xD2511F53",
+     "PHILOX_M0 = 0xD2511F55"),
+    ("philox_weyl_key", "philox.py",
+     "PHILOX_W1 = 0xBB67AE85",
+     "PHILOX_W1 = 0xBB67AE87"),
+    ("uniform_drops_a_bit", "philox.py",
+     "return (w[0] >> 8) * (1.0 / 16777216.0)",
+     "return (w[0] >> 9) * (1.0 / 16777216.0)"),
+]
+
+
+def _run_pins_on(name, fname, old, new):
+    """Exit status of the pin suite against a mutant oracle, and its output tail."""
+    tmp = tempfile.mkdtemp(prefix="oracle_mutant_")
+    try:
+        shutil.copytree(os.path.join(ROOT, "oracle"), os.path.join(tmp, "oracle"),
+                        ignore=shutil.ignore_patterns("__pycache__"))
+        path = os.path.join(tmp, "oracle", fname)
+        src = open(path).read()
+        assert src.count(old) == 1, "mutant %s: anchor text must occur exactly once" % name
+        open(path, "w").write(src.replace(old, new))
+        env = dict(os.environ)
+        # the mutant package comes first; the repository (synth, tests) after it
+        env["PYTHONPATH"] = os.pathsep.join([tmp, ROOT])
+        env["PYTHONDONTWRITEBYTECODE"] = "1"
+        cmd = [sys.executable, "-m", "pytest", PINS, "-x", "-q", "-p", "no:cacheprovider",
+               "--import-mode=append", "--rootdir", ROOT]
+        if fname != "philox.py":
+            cmd += ["-k", "not rocrand"]
+        r = subprocess.run(cmd, cwd=tmp, env=env, capture_output=True, text=True, timeout=600)
+        # the suite must really have run against the mutant
+        return r.returncode, (r.stdout + r.stderr)[-1500:]
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+
+
+def test_every_mutant_fails_a_pin():
+    with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
+        futs = {ex.submit(_run_pins_on, *m): m[0] for m in MUTANTS}
+        results = {futs[f]: f.result() for f in concurrent.futures.as_completed(futs)}
+    survived = [n for n, (rc, _) in results.items() if rc == 0]
+    broken = {n: out for n, (rc, out) in results.items() if rc not in (0, 1)}
+    assert not broken, "mutants that did not run as tests: %s" % broken
+    assert not survived, "mutants no pin catches: %s" % survived
+
+
+def test_unmutated_copy_passes_the_pins():
+    # the same harness with a no-op substitution must pass, so a failure above
+    # comes from the planted mistake and not from the harness
+    rc, out = _run_pins_on("identity", "verify.py", "F32 = 0", "F32 = 0")
+    assert rc == 0, out

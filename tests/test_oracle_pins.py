@@ -61,6 +61,30 @@ def test_row_uniform_is_on_the_24bit_grid():
     assert len(us) == 128
 
 
+def test_row_uniform_is_rocrand_word0_on_the_grid(rocrand_ref):
+    # reading c10: key = (seed lo, seed hi), counter = (row, request, offset
+    # lo, offset hi), u = (word 0 >> 8) * 2^-24, word 0 from rocRAND's engine
+    cases = [(0, 0, 0, 0), (2005, 3, 6, 0), (2**40 + 3, 511, 7, 2**33 + 1), (2**64 - 1, 7, 1, 2**64 - 1)]
+    rng = np.random.default_rng(9)
+    for _ in range(60):
+        cases.append((int(rng.integers(0, 2**63)), int(rng.integers(0, 4096)), int(rng.integers(0, 8)),
+                      int(rng.integers(0, 2**40))))
+    m = 0xFFFFFFFF
+    inp = "".join("%d %d %d %d %d %d\n" % (j, i, o & m, o >> 32, s_ & m, s_ >> 32) for (s_, i, j, o) in cases)
+    out = subprocess.run([rocrand_ref], input=inp, capture_output=True, text=True, check=True).stdout
+    words = [int(line.split()[0]) for line in out.strip().splitlines()]
+    assert len(words) == len(cases)
+    for (s_, i, j, o), w0 in zip(cases, words):
+        assert oracle.row_uniform(s_, i, j, o) == (w0 >> 8) / GRID
+
+
+def test_row_uniform_spans_the_unit_interval():
+    us = np.array([oracle.row_uniform(2003, i, j, 0) for i in range(512) for j in range(8)])
+    assert abs(us.mean() - 0.5) < 0.02
+    assert us.min() < 0.01 and us.max() > 0.99
+    assert abs(np.mean(us < 0.25) - 0.25) < 0.03
+
+
 # ---------------------------------------------------------------- reductions
 
 def _tied_rows(rng, n, V):
@@ -193,6 +217,29 @@ def test_temperature_zero_equals_greedy():
     for key in ("accepted_len", "next_token", "out_offsets", "out_tokens", "row_token"):
         assert np.array_equal(s[key], g[key])
     assert np.allclose(s["row_lse"], g["row_lse"], rtol=0, atol=0)
+
+
+def test_sampled_row_lse_is_logsumexp_of_x_over_t():
+    # reading c12: a sampled row reports the log-sum-exp of x / T
+    w = synth.make(3, B=5, V=2048)
+    T = np.full(w.B, 0.5, dtype=np.float32)
+    res = oracle.verify_sampled(w.logits, w.dtype, w.V, w.offsets, w.owner, w.drafts,
+                                T, w.top_k, w.top_p, w.min_p, w.seed, 0)
+    for r in range(w.R):
+        x = oracle.row_f64(w.logits, w.dtype, r, w.V)
+        assert res["row_lse"][r] == pytest.approx(scipy.special.logsumexp(x / 0.5), rel=1e-12)
+
+
+def test_draw_is_the_first_cumulative_weight_strictly_above_u():
+    # the inverse CDF worked by hand: equal logits 0, 0, 0, 0 (weights 1 each,
+    # rank order 0, 1, 2, 3, total 4); u * 4 = 1 lies exactly on the first
+    # cumulative boundary, so the draw is the second token; just below it, the
+    # first; u * 4 = 3 gives the last token
+    x = np.zeros(4)
+    assert oracle.sample_from_u(x, 1.0, 0, 1.0, 0.0, 0.25) == 1
+    assert oracle.sample_from_u(x, 1.0, 0, 1.0, 0.0, 0.25 - 2.0**-24) == 0
+    assert oracle.sample_from_u(x, 1.0, 0, 1.0, 0.0, 0.75) == 3
+    assert oracle.sample_from_u(x, 1.0, 0, 1.0, 0.0, 0.0) == 0
 
 
 # ---------------------------------------------------------------- sampling law
