@@ -41,6 +41,8 @@ vsv_status prepare(const vsv_batch* b, const vsv_outputs* o, void* ws, size_t ws
     return VSV_OK;
   }
   if (!dtype_ok(b->dtype) || b->vocab < 1 || b->vocab > vsv::kMaxVocab || b->ld < b->vocab) return VSV_EINVAL;
+  // a row is addressed through a buffer resource with a 32-bit byte size
+  if (static_cast<int64_t>(b->vocab) * elem_size(b->dtype) > vsv::kMaxRowBytes) return VSV_EINVAL;
   if (!b->logits || !aligned(b->logits, elem_size(b->dtype))) return VSV_EINVAL;
   if (!b->row_offsets || !b->row_owner) return VSV_EINVAL;
   if (b->num_rows > b->num_requests && !b->draft_tokens) return VSV_EINVAL;

@@ -81,6 +81,20 @@ __device__ __forceinline__ uint64_t load_agent64(const uint64_t* p) {
   return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---------------------------------------------------------------- barriers
+
+// Workgroup barrier for LDS traffic. The kernels exchange data between waves
+// only through LDS (global words between workgroups carry tags and are
+// polled), so a barrier needs to order LDS operations alone. A full
+// __syncthreads also waits for every global store and load the wave has in
+// flight (on this architecture one counter covers both), which puts a
+// memory round trip on the critical path wherever results were just stored.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------- reductions
 
 struct MaxOp {
@@ -149,9 +163,9 @@ __device__ __forceinline__ double wave_sum_f64(double v) { return wave_all(v, Su
 template <int NT, typename T, typename Op>
 __device__ __forceinline__ T block_reduce(T v, Op op, T* scratch) {
   v = wave_reduce(v, op);
-  __syncthreads();
+  lds_barrier();
   if ((threadIdx.x & (kWave - 1)) == 0) scratch[threadIdx.x / kWave] = v;
-  __syncthreads();
+  lds_barrier();
   T r = scratch[0];
 #pragma unroll
   for (int w = 1; w < NT / kWave; ++w) r = op(r, scratch[w]);
@@ -182,9 +196,9 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int& to
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
   const int incl = wave_inclusive_scan(v);
-  __syncthreads();
+  lds_barrier();
   if (lane == kWave - 1) scratch[w] = incl;
-  __syncthreads();
+  lds_barrier();
   int before = 0, sum = 0;
 #pragma unroll
   for (int k = 0; k < NT / kWave; ++k) {

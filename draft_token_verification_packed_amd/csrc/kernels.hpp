@@ -69,8 +69,9 @@ struct VerifyArgs {
   //           call resets both to 0
   //  ws_row   [R] 64-bit words; a row handled by one workgroup stores the
   //           token it emits | kAcceptBit if its draft was accepted
-  //  ws_part  [(R + kMaxGroups) * kPartWords] 64-bit words; slot r + p holds
-  //           the partial statistics persistent workgroup p gathered for row r
+  //  ws_part  [kPartWords][R + kMaxGroups] 64-bit words, field-major; slot
+  //           r + p holds the partial statistics persistent workgroup p
+  //           gathered for row r
   uint32_t* ws_epoch;
   uint32_t* ws_queue;
   uint64_t* ws_row;
@@ -117,6 +118,9 @@ inline size_t ws_bytes(int32_t B, int32_t R, int32_t /*sampled*/) {
 }
 // Tokens travel in the low 30 bits of a row word.
 constexpr int32_t kMaxVocab = 0x3FFFFFFF;
+// Bytes of one row of logits: rows are read through buffer resources whose
+// size is a signed 32-bit count.
+constexpr int64_t kMaxRowBytes = 0x7FFFFFF0;
 
 hipError_t launch_verify_greedy(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_verify_sampled(const VerifyArgs& a, hipStream_t s);

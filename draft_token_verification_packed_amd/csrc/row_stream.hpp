@@ -348,7 +348,7 @@ __device__ __forceinline__ RowResult finish_row(const RowPartial& p, RowScratch<
   }
   RowRed r = wave_red<kRank>(RowRed{p.s, p.best, idx, p.mc, kRank ? p.rank : 0});
   if (lane == 0) s.r[w] = r;
-  __syncthreads();
+  lds_barrier();
   r = s.r[0];
 #pragma unroll
   for (int k = 1; k < NW; ++k) r = combine(r, s.r[k]);

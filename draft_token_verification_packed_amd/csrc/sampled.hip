@@ -68,7 +68,7 @@ __global__ __launch_bounds__(NT) void verify_sampled_kernel(VerifyArgs a) {
   static_assert(sizeof(TailScratch) <= sizeof(L.elem), "tail staging aliases the candidate buffers");
   const uint32_t tag = call_tag(a);
   if (threadIdx.x == 0) L.row_next = static_cast<int>(min(queue_take(a), static_cast<uint32_t>(a.R)));
-  __syncthreads();
+  lds_barrier();
   int r = L.row_next;
   while (r < a.R) {
     // the next row's ticket is in flight during the row's last steps; the
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(NT) void verify_sampled_kernel(VerifyArgs a) {
       if (threadIdx.x == 0) next = queue_take(a);
     });
     if (threadIdx.x == 0) L.row_next = static_cast<int>(min(next, static_cast<uint32_t>(a.R)));
-    __syncthreads();
+    lds_barrier();
     r = L.row_next;
   }
   // Every ticket of this workgroup has been taken and its rows published
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(NT) void verify_sampled_kernel(VerifyArgs a) {
                                                  __HIP_MEMORY_SCOPE_AGENT);
     L.last = done + 1 == gridDim.x;
   }
-  __syncthreads();
+  lds_barrier();
   if (L.last) {
     if (threadIdx.x == 0) {
       store_agent(a.ws_queue + kQueueNext, 0u);

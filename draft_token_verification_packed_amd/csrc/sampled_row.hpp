@@ -235,10 +235,13 @@ __device__ __forceinline__ void wave_drain(SampledLds<NT>& L, WaveCap& s) {
         e[b * EPW + h] = e0 + h;
       }
     }
+    // steps past the ring's fill level hold nothing: skip them (uniform)
+    const int steps = min(kBatch, (s.ring_n - j0 + kStep - 1) / kStep);
     auto count = [&]() {
       int n = 0;
 #pragma unroll
-      for (int i = 0; i < M; ++i) n += __popcll(__ballot(have[i / EPW] && x[i] >= s.tau));
+      for (int i = 0; i < M; ++i)
+        if (i / EPW < steps) n += __popcll(__ballot(have[i / EPW] && x[i] >= s.tau));
       return n;
     };
     if (s.elem_n + count() > kEW) {
@@ -253,6 +256,7 @@ __device__ __forceinline__ void wave_drain(SampledLds<NT>& L, WaveCap& s) {
     }
 #pragma unroll
     for (int i = 0; i < M; ++i) {
+      if (i / EPW >= steps) break;
       const bool take = have[i / EPW] && x[i] >= s.tau;
       const uint64_t bal = __ballot(take);
       if (take) L.elem[w][s.elem_n + mbcnt(bal)] = Cand{x[i], e[i]};
@@ -324,7 +328,7 @@ template <int NT>
 __device__ __forceinline__ void block_start_max(SampledLds<NT>& L, WaveCap& s, float lane_best) {
   const float wm = wave_reduce(lane_best, MaxOp());
   if (lane_id() == 0 && wm > -INFINITY) atomicMax(&L.mkey, ord_key(wm));
-  __syncthreads();
+  lds_barrier();
   const float m = key_float(uni(L.mkey));
   const float t = m - s.dcap;
   if (t > s.tau) s.tau = t;
@@ -362,9 +366,9 @@ template <int NT, typename T>
 __device__ __forceinline__ T block_scan_incl(T v, T* scr, T& total) {
   const int lane = lane_id(), w = wave_id();
   v = wave_scan_incl(v);
-  __syncthreads();
+  lds_barrier();
   if (lane == kWave - 1) scr[w] = v;
-  __syncthreads();
+  lds_barrier();
   T before = 0, sum = 0;
 #pragma unroll
   for (int k = 0; k < NT / kWave; ++k) {
@@ -428,7 +432,7 @@ struct CandLocator {
       L.u.post.cnt[b] = 0;
       L.u.post.mass[b] = 0.0;
     }
-    __syncthreads();
+    lds_barrier();
     // the stream summed every element with the rounded scale c; the
     // candidates' share is replaced by their exact weights
     double corr = 0.0;
@@ -446,7 +450,7 @@ struct CandLocator {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     constexpr int PER = kNB / NT;
     int lc[PER];
     double lm[PER];
@@ -495,7 +499,7 @@ struct CandLocator {
       L.u.post.cnt[kNB] = tc;
       L.u.post.mass[kNB] = tm;
     }
-    __syncthreads();
+    lds_barrier();
     nc = tc;
   }
 
@@ -505,7 +509,7 @@ struct CandLocator {
   template <typename Pred>
   __device__ int first_bin(Pred pred) {
     if (threadIdx.x == 0) L.bi[0] = kNB;
-    __syncthreads();
+    lds_barrier();
     constexpr int PER = kNB / NT;
     // bins threadIdx.x * PER .. : a wave covers a contiguous bin range, so the
     // first qualifying lane of the first qualifying wave holds the answer
@@ -517,9 +521,9 @@ struct CandLocator {
     }
     const uint64_t bal = __ballot(mine < kNB);
     if (bal && lane_id() == __builtin_ctzll(bal)) atomicMin(&L.bi[0], mine);
-    __syncthreads();
+    lds_barrier();
     const int b = L.bi[0];
-    __syncthreads();
+    lds_barrier();
     return b;
   }
 
@@ -527,7 +531,7 @@ struct CandLocator {
   // prefixes their weights into gpm. Returns the count (or -1 if too many).
   __device__ int gather(int b) {
     if (threadIdx.x == 0) L.gn = 0;
-    __syncthreads();
+    lds_barrier();
     for (int w = 0; w < NW; ++w) {
       const int n = L.wn[w];
       for (int j = threadIdx.x; j < n; j += NT) {
@@ -537,9 +541,9 @@ struct CandLocator {
         if (pos < kGather) L.u.post.g[pos] = e;
       }
     }
-    __syncthreads();
+    lds_barrier();
     const int cb = L.gn;
-    __syncthreads();
+    lds_barrier();
     if (cb > kGather) return -1;
     for (int q = threadIdx.x; q < cb; q += NT) {
       const Cand e = L.u.post.g[q];
@@ -550,14 +554,14 @@ struct CandLocator {
       }
       L.u.post.gs[r] = e;
     }
-    __syncthreads();
+    lds_barrier();
     if (!kCode) {
       double wv = 0.0;
       if (static_cast<int>(threadIdx.x) < cb) wv = weight(L.u.post.gs[threadIdx.x].x, m, T);
       double tot;
       const double incl = block_scan_incl<NT, double>(wv, L.red_d, tot);
       if (static_cast<int>(threadIdx.x) < cb) L.u.post.gpm[threadIdx.x] = incl;
-      __syncthreads();
+      lds_barrier();
     }
     return cb;
   }
@@ -588,7 +592,7 @@ struct CandLocator {
     p.off = j;
     p.cum = cum_at(b, j);
     p.ok = true;
-    __syncthreads();
+    lds_barrier();
     return p;
   }
 
@@ -632,7 +636,7 @@ struct CandLocator {
     p.rank = L.u.post.cnt[b] + j;
     p.cum = cum_at(b, j);
     p.ok = true;
-    __syncthreads();
+    lds_barrier();
     return p;
   }
 
@@ -660,7 +664,7 @@ struct CandLocator {
       return 0;
     }
     const int t = L.u.post.gs[p.off].idx;
-    __syncthreads();
+    lds_barrier();
     return t;
   }
 };
@@ -704,7 +708,7 @@ struct FullLocator {
         L.u.radix.cnt[b] = 0;
         L.u.radix.mass[b] = 0.0;
       }
-      __syncthreads();
+      lds_barrier();
       for (int e = threadIdx.x; e < V; e += NT) {
         const float x = at(e);
         const uint32_t k = ord_ukey(x);
@@ -713,7 +717,7 @@ struct FullLocator {
         atomicAdd(&L.u.radix.cnt[dig], 1);
         atomicAdd(&L.u.radix.mass[dig], weight(x, m, T));
       }
-      __syncthreads();
+      lds_barrier();
       if (threadIdx.x == 0) {
         int dsel = 0, c = above_c;
         double w = above_m;
@@ -734,12 +738,12 @@ struct FullLocator {
         L.bd[0] = w;
         L.bi[2] = L.u.radix.cnt[dsel];
       }
-      __syncthreads();
+      lds_barrier();
       prefix = (prefix << 8) | static_cast<uint32_t>(L.bi[0]);
       above_c = L.bi[1];
       above_m = L.bd[0];
       tie_c = L.bi[2];
-      __syncthreads();
+      lds_barrier();
     }
     key = prefix;
     const int kk = static_cast<int>(prefix ^ 0x80000000u);
@@ -758,7 +762,7 @@ struct FullLocator {
       const int incl = block_scan_incl<NT, int>(c, L.red_i, tot);
       const int excl = incl - c;
       if (threadIdx.x == 0) L.bi[3] = -1;
-      __syncthreads();
+      lds_barrier();
       if (need >= excl && need < incl) {
         int k = need - excl;
         for (int e = lo; e < lo + 8 && e < V; ++e) {
@@ -771,9 +775,9 @@ struct FullLocator {
           }
         }
       }
-      __syncthreads();
+      lds_barrier();
       const int found = L.bi[3];
-      __syncthreads();
+      lds_barrier();
       if (found >= 0) return found;
       need -= tot;
     }
@@ -1002,7 +1006,7 @@ __device__ __forceinline__ SampledOut sampled_row(const VerifyArgs& a, const E* 
 
   const int w = wave_id();
   if (threadIdx.x == 0) L.mkey = INT32_MIN;
-  __syncthreads();
+  lds_barrier();
   WaveCap s{0, 0, -INFINITY, -INFINITY, dcap, 0, kmin};
 
   RowPartial p;
@@ -1044,14 +1048,14 @@ __device__ __forceinline__ SampledOut sampled_row(const VerifyArgs& a, const E* 
     if (done) token = t;
   }
   if (!done && !(out.bits & VSV_FLAG_LOGITS)) {
-    __syncthreads();
+    lds_barrier();
     FullLocator<E, NT> fl(L, row, a.V, m, Td);
     int t = 0;
     decide(fl, a.V, top_k, static_cast<double>(top_p), static_cast<double>(min_p), u, t);
     token = t;
     out.slow = 1;
   }
-  __syncthreads();
+  lds_barrier();
   out.token = token;
   return out;
 }

@@ -58,8 +58,12 @@ struct ChunkPlan {
   __device__ int64_t lo(int p) const { return Q * p / P; }
 };
 
+// Partials are stored field-major (field f of every slot, then field f + 1),
+// so the lanes of a tail wave, which merge consecutive rows, read
+// consecutive words: a wave's load touches a few cache lines, not one line
+// per lane.
 __device__ __forceinline__ uint64_t* slot_word(const VerifyArgs& a, int64_t slot, int f) {
-  return a.ws_part + static_cast<size_t>(slot) * kPartWords + f;
+  return a.ws_part + static_cast<size_t>(f) * (static_cast<size_t>(a.R) + kMaxGroups) + static_cast<size_t>(slot);
 }
 
 // Store field f of a partial (lanes 0 .. kPartWords - 1 of a wave together
@@ -157,9 +161,8 @@ template <int NT, bool kRelaxed>
 __device__ __forceinline__ void greedy_tail(const VerifyArgs& a, const ChunkPlan& plan, uint32_t tag, TailScratch& t,
                                             int64_t* lo) {
   const int tid = threadIdx.x;
-  const ReqRange first = load_range(a, tid);
   for (int q = tid; q <= plan.P; q += NT) lo[q] = plan.lo(q);
-  __syncthreads();
+  lds_barrier();
   int stalled = 0, bits = 0, budget = kPollBudget;
   for (int r = tid; r < a.R; r += NT) {
     uint32_t info = kNoDraft;
@@ -180,20 +183,33 @@ __device__ __forceinline__ void greedy_tail(const VerifyArgs& a, const ChunkPlan
   }
   if (bits) set_flag(a, bits);
   if (stalled) set_flag(a, VSV_FLAG_STALLED);
-  if (a.R > kTailStage) wait_memory();  // words of later rows went to the workspace
-  __syncthreads();
-  scan_requests<NT>(a, t, first, [&](int row) -> uint32_t {
-    return row < kTailStage ? t.words[row] : static_cast<uint32_t>(load_agent64(a.ws_row + row));
-  });
+  if (a.R > kTailStage) {
+    // words of later rows went to the workspace: a full barrier after their
+    // stores have completed, so no read of them moves above it
+    wait_memory();
+    __syncthreads();
+  } else {
+    lds_barrier();
+  }
+  // a batch whose words all sit in LDS scans without any global load, so no
+  // wait in the scan can stall behind the row outputs just stored
+  if (a.R <= kTailStage)
+    scan_requests<NT>(a, t, [&](int row) -> uint32_t { return t.words[row]; });
+  else
+    scan_requests<NT>(a, t, [&](int row) -> uint32_t {
+      return row < kTailStage ? t.words[row] : static_cast<uint32_t>(load_agent64(a.ws_row + row));
+    });
   end_call(a, tag);
 }
 
-// A row's 16-byte-aligned body: `head` elements in, `nvec` vectors long,
-// and a buffer resource covering exactly those vectors (or none at all).
+// A row's geometry: its 16-byte-aligned body starts `head` elements in (at
+// byte `boff`) and is `nvec` vectors long; one buffer resource covers the
+// whole row [0, V) (or nothing at all).
 template <typename E>
 struct RowGeo {
   const E* row;
   int head, nvec;
+  uint32_t boff;
   __amdgpu_buffer_rsrc_t rsrc;
 };
 
@@ -206,20 +222,45 @@ __device__ __forceinline__ RowGeo<E> row_geo(const VerifyArgs& a, int r, bool va
   g.head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(E));
   if (g.head > a.V) g.head = a.V;
   g.nvec = (a.V - g.head) / N;
-  g.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<E*>(g.row + g.head), 0, valid ? g.nvec * 16 : 0, 0x00020000);
+  g.boff = static_cast<uint32_t>(g.head * sizeof(E));
+  g.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<E*>(g.row), 0,
+                                             valid ? static_cast<int>(a.V * sizeof(E)) : 0, 0x00020000);
   return g;
 }
 
-// Loads of chunk k's vectors k * CH + u * 64 + lane: buffer loads bounded by
-// the row's body, so vectors past its end (and every load through an empty
-// resource) return zero without touching memory, and no load needs a branch.
-template <int U>
-__device__ __forceinline__ void load_chunk(u32x4* dst, __amdgpu_buffer_rsrc_t rsrc, int k, int lane) {
+// Buffer offset no row reaches: a load through it returns zero without
+// touching memory.
+constexpr uint32_t kNoOffset = 0xFFFFFFF0u;
+
+// Loads of chunk k: vectors k * CH + u * 64 + lane of the row's body, and the
+// lane's edge element (lanes 0 .. 7: the head elements before the body, with
+// the row's first chunk; lanes 8 .. 15: the tail elements after it, with the
+// last chunk). Every load is issued unconditionally through the row's
+// resource (what lies outside the row reads as zero and is masked where it
+// is reduced), so no load sits behind a branch and the waits before a chunk
+// is reduced count only the loads issued after it.
+template <typename E, int U>
+__device__ __forceinline__ void load_chunk(u32x4* dst, uint32_t& edge, const RowGeo<E>& g, int k, int cpr, int V,
+                                           int lane) {
   constexpr int CH = kWave * U;
+  constexpr int N = Elem<E>::kVec;
 #pragma unroll
   for (int u = 0; u < U; ++u)
-    dst[u] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, static_cast<uint32_t>((k * CH + u * kWave + lane) * 16), 0,
-                                                   2 /* nt */);
+    dst[u] = __builtin_amdgcn_raw_buffer_load_b128(g.rsrc, g.boff + static_cast<uint32_t>((k * CH + u * kWave + lane) * 16),
+                                                   0, 2 /* nt */);
+  const int te = g.head + g.nvec * N + (lane - 8);
+  uint32_t off = kNoOffset;
+  off = (k == 0 && lane < g.head) ? static_cast<uint32_t>(lane * sizeof(E)) : off;
+  off = (k == cpr - 1 && lane >= 8 && lane < 16 && te < V) ? static_cast<uint32_t>(te * sizeof(E)) : off;
+  if constexpr (sizeof(E) == 2)
+    edge = __builtin_amdgcn_raw_buffer_load_b16(g.rsrc, off, 0, 0);
+  else
+    edge = __builtin_amdgcn_raw_buffer_load_b32(g.rsrc, off, 0, 0);
+}
+
+template <typename E>
+__device__ __forceinline__ float edge_value(uint32_t e) {
+  return sizeof(E) == 2 ? __uint_as_float(e << 16) : __uint_as_float(e);
 }
 
 // Persistent greedy verification: one workgroup per CU, an equal contiguous
@@ -242,6 +283,9 @@ __global__ __launch_bounds__(NT) void verify_greedy_kernel(VerifyArgs a) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   const int p = blockIdx.x;
   const uint32_t tag = call_tag(a);
+  // request ranges for the scan (used by the last workgroup only): loaded
+  // now and staged in LDS right after streaming, where the wait is free
+  const ReqRange first = load_range(a, tid);
   const ChunkPlan plan{static_cast<int64_t>(a.R) * a.cpr, static_cast<int>(gridDim.x), a.cpr};
   const int64_t lo = plan.lo(p), hi = plan.lo(p + 1);
   const int row_lo = static_cast<int>(lo / a.cpr);
@@ -277,7 +321,7 @@ __global__ __launch_bounds__(NT) void verify_greedy_kernel(VerifyArgs a) {
     }
   };
   if (kRelaxed && w == 0) gather_info();
-  __syncthreads();
+  lds_barrier();
   if (!kRelaxed && w == NW - 1) gather_info();
 
   auto grab = [&]() -> int {
@@ -331,7 +375,7 @@ __global__ __launch_bounds__(NT) void verify_greedy_kernel(VerifyArgs a) {
     sl.g = (sl.r == prev.r && valid) ? prev.g : row_geo<E>(a, sl.r, valid);
     return sl;
   };
-  auto process = [&](const Slot& sl, u32x4* w) {
+  auto process = [&](const Slot& sl, u32x4* w, uint32_t edge) {
     if (sl.r != row) {
       flush();
       partial_init(pt);
@@ -344,50 +388,49 @@ __global__ __launch_bounds__(NT) void verify_greedy_kernel(VerifyArgs a) {
       }
     }
     const int v0 = sl.k * CH + lane;
-    const bool partial = (sl.k + 1) * CH > sl.g.nvec;   // the row's last chunk
-    if (kRelaxed && partial) {
-      take_group<E, U, kWave, true, true>(pt, w, v0, sl.g.head, kLog2e, xd, d, keep, sl.g.nvec);
-    } else {
-      // vectors past the row's body read as zeros: make them -inf (only the
-      // last chunk of a row has any)
-      if (partial) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          if (v0 + u * kWave >= sl.g.nvec) w[u] = Elem<E>::neg_inf();
-      }
+    const bool live = sl.c < nch;   // past the range: reduces nothing
+    // the row's last chunk: its vectors past the body count as -inf (they
+    // are masked after decoding; the load registers are never overwritten,
+    // which would make the compiler wait for every load in flight)
+    if (live && (sl.k + 1) * CH <= sl.g.nvec)
       take_group<E, U, kWave, kRelaxed>(pt, w, v0, sl.g.head, kLog2e, xd, d, keep);
-    }
+    else
+      take_group<E, U, kWave, kRelaxed, true>(pt, w, v0, sl.g.head, kLog2e, xd, d, keep, live ? sl.g.nvec : 0);
+    if (!live) return;
     // elements outside the row's 16-byte body (misaligned rows or a vocab
-    // that is not a multiple of the vector): with the first and last chunk
-    if (sl.k == 0 && lane < sl.g.head)
-      take_scalar<kRelaxed>(pt, Elem<E>::at(sl.g.row, lane), lane, kLog2e, xd, d);
+    // that is not a multiple of the vector), loaded with the chunk
+    if (sl.k == 0 && lane < sl.g.head) take_scalar<kRelaxed>(pt, edge_value<E>(edge), lane, kLog2e, xd, d);
     if (sl.k == a.cpr - 1) {
-      const int e = sl.g.head + sl.g.nvec * Elem<E>::kVec + lane;
-      if (e < a.V) take_scalar<kRelaxed>(pt, Elem<E>::at(sl.g.row, e), e, kLog2e, xd, d);
+      const int e = sl.g.head + sl.g.nvec * Elem<E>::kVec + (lane - 8);
+      if (lane >= 8 && lane < 16 && e < a.V) take_scalar<kRelaxed>(pt, edge_value<E>(edge), e, kLog2e, xd, d);
     }
   };
 
   // Two buffers in turn, no copies: while one chunk is reduced the other's
   // loads are in flight, and the next chunk number is fetched before the
-  // reduction so its LDS round trip is hidden.
+  // reduction so its LDS round trip is hidden. Both halves run every
+  // iteration (the loop's only exit is at its top), so every path into a
+  // reduction has the same loads in flight and the compiler's waits count
+  // exactly the other buffer's loads.
   Slot sa = first_slot(grab());
   u32x4 A[U], B[U];
-  load_chunk<U>(A, sa.g.rsrc, sa.k, lane);
+  uint32_t ea, eb;
+  load_chunk<E, U>(A, ea, sa.g, sa.k, a.cpr, a.V, lane);
   Slot sb = after(sa, grab());
-  load_chunk<U>(B, sb.g.rsrc, sb.k, lane);
+  load_chunk<E, U>(B, eb, sb.g, sb.k, a.cpr, a.V, lane);
   while (sa.c < nch) {
     const int ca = grab();
-    process(sa, A);
+    process(sa, A, ea);
     sa = after(sb, ca);
-    load_chunk<U>(A, sa.g.rsrc, sa.k, lane);
-    if (sb.c >= nch) break;
+    load_chunk<E, U>(A, ea, sa.g, sa.k, a.cpr, a.V, lane);
     const int cb = grab();
-    process(sb, B);
+    process(sb, B, eb);
     sb = after(sa, cb);
-    load_chunk<U>(B, sb.g.rsrc, sb.k, lane);
+    load_chunk<E, U>(B, eb, sb.g, sb.k, a.cpr, a.V, lane);
   }
   flush();
-  __syncthreads();
+  tail.first[tid] = first;
+  lds_barrier();
 
   // one partial per row touched (slot r + p), a wave per row: its lanes
   // combine the waves' slots; the row information goes with the first

@@ -104,16 +104,20 @@ __device__ __forceinline__ uint32_t row_word(const VerifyArgs& a, const RowMeta&
 // Rows whose words the scan stages in LDS.
 constexpr int kTailStage = 4096;
 
-struct TailScratch {
-  uint32_t words[kTailStage];
-  int scan[16];
-};
-
-// Row offsets of request i and the next one (the tails load those of the
-// first NT requests early, so the scan does not wait for them).
+// Row offsets of request i and the next one.
 struct ReqRange {
   int r0, r1;
 };
+
+struct TailScratch {
+  uint32_t words[kTailStage];
+  int scan[16];
+  ReqRange first[1024];  // ranges of the first blockDim requests, staged early
+};
+
+// The tails load the ranges of the first NT requests early and stage them
+// in LDS, so the scan never waits on a global load: on this architecture
+// such a wait would also wait for every store issued before it.
 __device__ __forceinline__ ReqRange load_range(const VerifyArgs& a, int i) {
   return i < a.B ? ReqRange{a.offsets[i], a.offsets[i + 1]} : ReqRange{0, 0};
 }
@@ -123,16 +127,20 @@ __device__ __forceinline__ ReqRange load_range(const VerifyArgs& a, int i) {
 // the emitted tokens. `word(r)` returns row r's word; `first` holds the range
 // of request tid.
 template <int NT, typename Word>
-__device__ __forceinline__ void scan_requests(const VerifyArgs& a, TailScratch& t, ReqRange first, Word word) {
+__device__ __forceinline__ void scan_requests(const VerifyArgs& a, TailScratch& t, Word word) {
   const int tid = threadIdx.x;
   int carry = 0;
-  for (int base = 0; base < a.B; base += NT) {
-    const int i = base + tid;
+  // Requests go to the threads from the top down (request base + k to thread
+  // NT - 1 - k): the rows were handled from thread 0 up, so with R + B <= NT
+  // the scanning waves have no loads or stores of their own in flight, and
+  // none of their waits stalls behind the row outputs just stored. Emitted
+  // positions then come from a suffix scan over the threads.
+  auto block = [&](int base, const ReqRange& rg) {
+    const int i = base + (NT - 1 - tid);
     int acc = 0, r0 = 0, len = 0;
     uint32_t nxt = 0;
     bool ok = false;
     if (i < a.B) {
-      const ReqRange rg = base == 0 ? first : load_range(a, i);
       r0 = rg.r0;
       const int r1 = rg.r1;
       ok = r0 >= 0 && r1 > r0 && r1 <= a.R && (i != 0 || r0 == 0) && (i != a.B - 1 || r1 == a.R);
@@ -146,7 +154,9 @@ __device__ __forceinline__ void scan_requests(const VerifyArgs& a, TailScratch& 
       len = acc + 1;
     }
     int total = 0;
-    const int pos = carry + block_exclusive_scan<NT>(len, t.scan, total);
+    const int before = block_exclusive_scan<NT>(len, t.scan, total);
+    // lengths of this block's requests below i: threads above this one
+    const int pos = carry + total - before - len;
     if (i < a.B) {
       const int nt = static_cast<int>(nxt & kTokenMask);
       a.accepted_len[i] = acc;
@@ -157,7 +167,11 @@ __device__ __forceinline__ void scan_requests(const VerifyArgs& a, TailScratch& 
       if (pos + acc < a.R) a.out_tokens[pos + acc] = nt;
     }
     carry += total;
-  }
+  };
+  // the first NT requests use the ranges staged in LDS; the block is peeled
+  // so that no load of a later block shares its path
+  block(0, t.first[NT - 1 - tid]);
+  for (int base = NT; base < a.B; base += NT) block(base, load_range(a, base + (NT - 1 - tid)));
   if (tid == 0) a.out_offsets[a.B] = carry;
 }
 
@@ -167,14 +181,17 @@ __device__ __forceinline__ void scan_requests(const VerifyArgs& a, TailScratch& 
 template <int NT>
 __device__ __forceinline__ void words_tail(const VerifyArgs& a, uint32_t tag, TailScratch& t) {
   const int tid = threadIdx.x;
-  const ReqRange first = load_range(a, tid);
+  t.first[tid] = load_range(a, tid);
   int stalled = 0, budget = kPollBudget;
   const int staged = min(a.R, kTailStage);
   for (int k = tid; k < staged; k += NT) t.words[k] = poll_tagged(a.ws_row + k, tag, budget, stalled);
-  __syncthreads();
-  scan_requests<NT>(a, t, first, [&](int row) -> uint32_t {
-    return row < staged ? t.words[row] : poll_tagged(a.ws_row + row, tag, budget, stalled);
-  });
+  lds_barrier();
+  if (a.R <= kTailStage)
+    scan_requests<NT>(a, t, [&](int row) -> uint32_t { return t.words[row]; });
+  else
+    scan_requests<NT>(a, t, [&](int row) -> uint32_t {
+      return row < staged ? t.words[row] : poll_tagged(a.ws_row + row, tag, budget, stalled);
+    });
   if (stalled) set_flag(a, VSV_FLAG_STALLED);
   end_call(a, tag);
 }

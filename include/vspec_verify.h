@@ -63,7 +63,7 @@ typedef enum { VSV_F32 = 0, VSV_BF16 = 1 } vsv_dtype;
 typedef struct {
   const void* logits;          /* [num_rows, ld] vocab-wide target logits             */
   int32_t dtype;               /* vsv_dtype                                           */
-  int32_t vocab;               /* 1 <= V < 2^30                                       */
+  int32_t vocab;               /* 1 <= V < 2^30, and a row of V logits < 2 GiB        */
   int64_t ld;                  /* row stride in elements, >= vocab                    */
   int32_t num_requests;        /* B >= 0                                              */
   int32_t num_rows;            /* R = sum_i (K_i + 1) >= B                            */

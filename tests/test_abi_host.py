@@ -75,6 +75,8 @@ def _greedy(L, batch, outs, ws=0x100000, ws_bytes=1 << 20, k=1):
     dict(logits=None), dict(dtype=7), dict(vocab=0), dict(ld=1000), dict(num_rows=3),
     dict(num_requests=-1), dict(row_offsets=None), dict(row_owner=None), dict(draft_tokens=None),
     dict(logits=0x10001), dict(dtype=0, logits=0x10002), dict(num_requests=0, num_rows=5),
+    # a row of 2 GiB or more (fp32 and bf16)
+    dict(dtype=0, vocab=1 << 29, ld=1 << 29), dict(vocab=(1 << 30) - 1, ld=(1 << 30) - 1),
 ])
 def test_invalid_batch_is_rejected_before_launch(L, bad):
     assert _greedy(L, _batch(**bad), _outs()) == 1
