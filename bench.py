@@ -133,8 +133,10 @@ def cpu_baseline(wl, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=500)
+    # the GPU needs tens of milliseconds of sustained work before its clocks
+    # settle: with a short warm-up the first timed launches run 5-10 % slow
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
                     help="workload (default: EAGLE greedy B=128 K=4 V=152064)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
