@@ -63,9 +63,10 @@ __device__ __forceinline__ uint32_t queue_take(const VerifyArgs& a) {
 }
 
 template <typename E, int NT, int U>
-__global__ __launch_bounds__(NT) void verify_sampled_kernel(VerifyArgs a) {
+// two workgroups per CU (4 waves per SIMD): at most 128 VGPRs
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void verify_sampled_kernel(VerifyArgs a) {
   __shared__ SampledLds<NT> L;
-  static_assert(sizeof(TailScratch) <= sizeof(L.elem), "tail staging aliases the candidate buffers");
+  static_assert(sizeof(TailScratch) <= sizeof(L.c), "tail staging aliases the candidate buffer");
   const uint32_t tag = call_tag(a);
   if (threadIdx.x == 0) L.row_next = static_cast<int>(min(queue_take(a), static_cast<uint32_t>(a.R)));
   lds_barrier();
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(NT) void verify_sampled_kernel(VerifyArgs a) {
       store_agent(a.ws_queue + kQueueNext, 0u);
       store_agent(a.ws_queue + kQueueDone, 0u);
     }
-    words_tail<NT>(a, tag, *reinterpret_cast<TailScratch*>(&L.elem[0][0]));
+    words_tail<NT>(a, tag, *reinterpret_cast<TailScratch*>(&L.c));
   }
 }
 

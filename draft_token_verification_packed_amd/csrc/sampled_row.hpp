@@ -15,18 +15,20 @@
 // Every decision is "the token at some rank", so it is enough to know the
 // rank order and the cumulative weights near the few ranks that matter.
 //
-// How: while streaming the row once (row_stream.hpp), each wave keeps the
-// candidate tokens above a wave-uniform threshold in LDS. A 16-byte vector
-// whose max clears the threshold is parked in the wave's ring with one
-// ballot; full rings are drained in bulk into the wave's candidate buffer,
-// and a full buffer is compacted with a 64-bin histogram that raises the
-// threshold. Each wave's buffer therefore holds every element of the wave's
-// share of the row above its final threshold, and the union holds every
-// element above the largest of them. Afterwards a 1024-bin histogram of
-// (count, float64 weight) over the union locates each cut; only the bin a
-// cut falls in is gathered and sorted. When the candidates cannot decide
-// (survivor set or draw beyond them, huge tie groups), an exact radix-select
-// over the whole row decides instead, reading the row again.
+// How: the row is streamed once from HBM (row_stream.hpp) for its maximum
+// and exponent sum, and every 16-byte vector leaves a 16-bit code of its
+// maximum (rounded up to bfloat16, so an upper bound) in LDS. With the row
+// maximum known, the capture threshold tau is exact: the maximum minus a
+// window of 10 T (or the min-p cut), or, for a top-k row, the k-th largest
+// vector maximum (a lower bound of the k-th largest element). A second pass
+// over the codes picks the vectors that may hold an element >= tau, reads
+// them again (they are still in the device's caches) and keeps those
+// elements in one candidate buffer. A 1024-bin histogram of (count, float64
+// weight) over the candidates then locates each cut; only the bin a cut
+// falls in is gathered and sorted. When the candidates cannot decide
+// (survivor set or draw beyond them, too many candidates, huge tie groups),
+// an exact radix-select over the whole row decides instead, reading the row
+// again.
 #pragma once
 
 #include "kernels.hpp"
@@ -34,11 +36,13 @@
 
 namespace vsv {
 
-constexpr int kEW = 768;        // candidate slots per wave
-constexpr int kRing = 128;      // parked vectors per wave
+constexpr int kVM = 20480;      // vector-maximum codes per row (an entry covers S vectors when more)
+constexpr int kCand = 4096;     // candidate slots per row
+constexpr int kCapVec = 3072;   // most vectors a window capture reads again (about 1.2 elements each)
+constexpr int kTopBins = 1024;  // top-k threshold: codes within this many of the maximum's
 constexpr int kNB = 1024;       // histogram bins over the candidates
 constexpr int kGather = 256;    // most elements one bin may hold
-constexpr float kZcap = 10.0f;  // capture window below the running max, in units of T
+constexpr float kZcap = 10.0f;  // capture window below the row maximum, in units of T
 
 struct Cand {
   float x;
@@ -56,14 +60,9 @@ __device__ __forceinline__ uint32_t ord_ukey(float x) { return static_cast<uint3
 
 template <int NT> struct SampledLds {
   static constexpr int NW = NT / kWave;
-  static_assert(NT >= kGather && NT <= 1024 && kNB % NT == 0, "one gathered element per thread");
-  static_assert(sizeof(double) * kNB >= sizeof(double) * kGather, "weight views share storage");
-  Cand elem[NW][kEW];
+  static_assert(NT >= kGather && NT <= 1024 && kNB % NT == 0 && kTopBins % NT == 0, "one gathered element per thread");
   union {
-    struct {
-      u32x4 v[NW][kRing];
-      int e0[NW][kRing];
-    } ring;
+    uint16_t vm[kVM];  // pass 1: vector-maximum codes; pass 2: indices of the picked ones
     struct {
       int cnt[kNB + 1];
       double mass[kNB + 1];
@@ -79,11 +78,12 @@ template <int NT> struct SampledLds {
       double mass[256];
     } radix;
   } u;
-  int whist[NW][64];
-  float wtau[NW];
-  int wn[NW];
-  int wovf[NW];
-  int mkey;
+  union {
+    Cand cand[kCand];           // every element >= tau of the row
+    int hist[NW][kTopBins];     // top-k threshold, before the capture
+  } c;
+  int ncand;
+  int ovf;
   int gn;
   int bi[4];
   double bd[4];
@@ -92,17 +92,6 @@ template <int NT> struct SampledLds {
   RowScratch<NT> rs;
   int row_next;  // the workgroup's next row (row queue)
   int last;      // this workgroup finished the call's last row
-};
-
-// Per-wave capture state; every lane holds the same values.
-struct WaveCap {
-  int ring_n;    // parked vectors
-  int elem_n;    // candidates in the buffer
-  float tau_w;   // threshold raised by compaction
-  float tau;     // effective threshold, max(tau_w, running max - window)
-  float dcap;    // capture window (x units)
-  int ovf;       // the buffer could not hold the wave's candidates
-  int kmin;      // compaction never keeps fewer candidates than this
 };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
@@ -116,175 +105,6 @@ __device__ __forceinline__ int mbcnt(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
 }
 
-// Keep only the wave's candidates at or above its current threshold
-// (entries parked before the threshold last rose may lie below it).
-template <int NT>
-__device__ __forceinline__ void wave_filter(SampledLds<NT>& L, WaveCap& s) {
-  const int lane = lane_id();
-  Cand* buf = L.elem[wave_id()];
-  int n = 0;
-  for (int base = 0; base < s.elem_n; base += kWave) {
-    const int q = base + lane;
-    Cand e{-INFINITY, 0};
-    if (q < s.elem_n) e = buf[q];
-    const bool keep = q < s.elem_n && e.x >= s.tau;
-    const uint64_t bal = __ballot(keep);
-    wave_lds_sync();
-    if (keep) buf[n + mbcnt(bal)] = e;   // n + rank <= q: reads of this chunk are done
-    n += __popcll(bal);
-    wave_lds_sync();
-  }
-  s.elem_n = n;
-}
-
-// Make room in the wave's buffer: drop entries below the threshold, and if
-// more than `target` remain, raise the threshold (64 value bins between it
-// and the wave's largest candidate) so that about `target` are kept.
-// Returns false if nothing can be dropped.
-template <int NT>
-__device__ bool wave_compact(SampledLds<NT>& L, WaveCap& s, int target) {
-  const int w = wave_id(), lane = lane_id();
-  Cand* buf = L.elem[w];
-  const int before = s.elem_n;
-  wave_filter<NT>(L, s);
-  if (s.elem_n <= target) return s.elem_n < before;
-  // histogram range: the buffer's own values (the threshold may be far below)
-  float hi = -INFINITY, lo = INFINITY;
-  for (int q = lane; q < s.elem_n; q += kWave) {
-    hi = fmaxf(hi, buf[q].x);
-    lo = fminf(lo, buf[q].x);
-  }
-  hi = uni(wave_reduce(hi, MaxOp()));
-  lo = uni(wave_reduce(lo, MinOp()));
-  if (!(hi > lo) || !(hi - lo < INFINITY)) return s.elem_n < before;
-  const float inv = 64.0f / (hi - lo);
-  L.whist[w][lane] = 0;
-  wave_lds_sync();
-  for (int q = lane; q < s.elem_n; q += kWave) {
-    int b = static_cast<int>((hi - buf[q].x) * inv);
-    b = b < 0 ? 0 : (b > 63 ? 63 : b);
-    atomicAdd(&L.whist[w][b], 1);
-  }
-  wave_lds_sync();
-  const int c1 = L.whist[w][lane];
-  const int incl = wave_inclusive_scan(c1);
-  const uint64_t reach = __ballot(incl >= target);
-  const int b = reach ? __builtin_ctzll(reach) : 63;
-  // entries of bins 0 .. b-1 stay; refine bin b with 64 sub-bins so that the
-  // kept count lands near the target instead of jumping a whole bin
-  const int before_b = read_lane(incl - c1, b);
-  const float bhi = hi - static_cast<float>(b) / inv;
-  const float sinv = inv * 64.0f;
-  L.whist[w][lane] = 0;
-  wave_lds_sync();
-  for (int q = lane; q < s.elem_n; q += kWave) {
-    const float x = buf[q].x;
-    const int bb = static_cast<int>((hi - x) * inv);
-    if ((bb < 0 ? 0 : (bb > 63 ? 63 : bb)) != b) continue;
-    int sb = static_cast<int>((bhi - x) * sinv);
-    sb = sb < 0 ? 0 : (sb > 63 ? 63 : sb);
-    atomicAdd(&L.whist[w][sb], 1);
-  }
-  wave_lds_sync();
-  const int incl2 = before_b + wave_inclusive_scan(L.whist[w][lane]);
-  const uint64_t reach2 = __ballot(incl2 >= target);
-  int sbk = reach2 ? __builtin_ctzll(reach2) : 63;
-  if (b == 63 && sbk == 63) sbk = 62;  // something must go
-  // keep values >= lower edge of sub-bin sbk of bin b
-  const float nt = bhi - static_cast<float>(sbk + 1) / sinv;
-  if (nt > s.tau) {
-    s.tau_w = fmaxf(s.tau_w, nt);
-    s.tau = nt;
-    wave_filter<NT>(L, s);
-  }
-  return s.elem_n < before;
-}
-
-// Move the parked vectors' elements at or above the threshold into the
-// buffer. Lane l reads 32-bit word l % 4 of parked vector l / 4 (one or two
-// elements), so a step covers 16 vectors with one compare, ballot and write
-// per element; the words of four steps (64 vectors) are read together, so a
-// batch costs a single LDS round trip. When a batch does not fit, the buffer
-// is compacted first (which raises the threshold) and the batch re-tested.
-template <typename E, int NT>
-__device__ __forceinline__ void wave_drain(SampledLds<NT>& L, WaveCap& s) {
-  constexpr int EPW = 4 / sizeof(E);   // elements per 32-bit word
-  constexpr int kStep = kWave / 4;     // vectors per step
-  constexpr int kBatch = 4;            // steps per batch
-  constexpr int M = kBatch * EPW;      // elements per lane per batch
-  const int w = wave_id(), lane = lane_id();
-  if (s.ring_n == 0) return;
-  wave_lds_sync();
-  const int q = lane & 3, jl = lane >> 2;
-  const uint32_t* ring = reinterpret_cast<const uint32_t*>(&L.u.ring.v[w][0]);
-  for (int j0 = 0; j0 < s.ring_n; j0 += kStep * kBatch) {
-    float x[M];
-    int e[M];
-    bool have[kBatch];
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int jj = j0 + b * kStep + jl;
-      have[b] = jj < s.ring_n;
-      const int j = min(jj, kRing - 1);
-      const uint32_t word = ring[j * 4 + q];
-      const int e0 = L.u.ring.e0[w][j] + q * EPW;
-#pragma unroll
-      for (int h = 0; h < EPW; ++h) {
-        x[b * EPW + h] = EPW == 1 ? __uint_as_float(word)
-                                  : __uint_as_float(h == 0 ? (word << 16) : (word & 0xFFFF0000u));
-        e[b * EPW + h] = e0 + h;
-      }
-    }
-    // steps past the ring's fill level hold nothing: skip them (uniform)
-    const int steps = min(kBatch, (s.ring_n - j0 + kStep - 1) / kStep);
-    auto count = [&]() {
-      int n = 0;
-#pragma unroll
-      for (int i = 0; i < M; ++i)
-        if (i / EPW < steps) n += __popcll(__ballot(have[i / EPW] && x[i] >= s.tau));
-      return n;
-    };
-    if (s.elem_n + count() > kEW) {
-      // A top-k row keeps only its top_k + 32: the k-th largest of the
-      // elements seen so far can only rise, so it is a safe threshold, and
-      // a high one parks far fewer vectors later. Other rows keep half.
-      if (!wave_compact<NT>(L, s, s.kmin > 0 ? s.kmin : kEW / 2) || s.elem_n + count() > kEW) {
-        s.ovf = 1;
-        s.tau = INFINITY;  // stop capturing: this row goes to the exact path
-        break;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < M; ++i) {
-      if (i / EPW >= steps) break;
-      const bool take = have[i / EPW] && x[i] >= s.tau;
-      const uint64_t bal = __ballot(take);
-      if (take) L.elem[w][s.elem_n + mbcnt(bal)] = Cand{x[i], e[i]};
-      s.elem_n += __popcll(bal);
-    }
-  }
-  s.ring_n = 0;
-  wave_lds_sync();
-}
-
-// Park without draining; returns true when the ring needs a drain before
-// the next park.
-template <int NT>
-__device__ __forceinline__ bool wave_park_only(SampledLds<NT>& L, WaveCap& s, const u32x4& v, int e0, float vmax,
-                                               bool valid) {
-  const bool take = valid && vmax >= s.tau;
-  const uint64_t bal = __ballot(take);
-  if (bal == 0) return false;
-  const int w = wave_id();
-  if (take) {
-    const int pos = s.ring_n + mbcnt(bal);
-    L.u.ring.v[w][pos] = v;
-    L.u.ring.e0[w][pos] = e0;
-  }
-  s.ring_n += __popcll(bal);
-  return s.ring_n > kRing - kWave;
-}
-
 // Row statistics of one decoded vector: running max and exponent sum (a
 // sampled row needs no argmax position).
 template <int N>
@@ -296,53 +116,6 @@ __device__ __forceinline__ void take_floats(RowPartial& p, const float* f, float
 #pragma unroll
   for (int k = 0; k < N; ++k) e[k] = fast_exp2(fmaf(f[k], c, nmc));
   p.s += static_cast<double>(tree_sum<N>(e));
-}
-
-// Append single elements (row head / tail) directly to the buffer.
-template <int NT>
-__device__ __forceinline__ void wave_take_scalar(SampledLds<NT>& L, WaveCap& s, float x, int e, bool valid) {
-  const bool take = valid && x >= s.tau;
-  const uint64_t bal = __ballot(take);
-  if (bal == 0) return;
-  const int n = __popcll(bal);
-  if (s.elem_n + n > kEW && !wave_compact<NT>(L, s, s.kmin > 0 ? s.kmin : kEW / 2)) {
-    s.ovf = 1;
-    s.tau = INFINITY;
-    return;
-  }
-  const bool take2 = valid && x >= s.tau;
-  const uint64_t bal2 = __ballot(take2);
-  if (s.elem_n + __popcll(bal2) > kEW) {
-    s.ovf = 1;
-    s.tau = INFINITY;
-    return;
-  }
-  if (take2) L.elem[wave_id()][s.elem_n + mbcnt(bal2)] = Cand{x, e};
-  s.elem_n += __popcll(bal2);
-  wave_lds_sync();
-}
-
-// Starting threshold from the whole block's first group: every wave
-// publishes its max before any reads it back.
-template <int NT>
-__device__ __forceinline__ void block_start_max(SampledLds<NT>& L, WaveCap& s, float lane_best) {
-  const float wm = wave_reduce(lane_best, MaxOp());
-  if (lane_id() == 0 && wm > -INFINITY) atomicMax(&L.mkey, ord_key(wm));
-  lds_barrier();
-  const float m = key_float(uni(L.mkey));
-  const float t = m - s.dcap;
-  if (t > s.tau) s.tau = t;
-}
-
-// Share the wave's running max and pull in the block's.
-template <int NT>
-__device__ __forceinline__ void wave_sync_max(SampledLds<NT>& L, WaveCap& s, float lane_best) {
-  const float wm = wave_reduce(lane_best, MaxOp());
-  if (lane_id() == 0 && wm > -INFINITY) atomicMax(&L.mkey, ord_key(wm));
-  wave_lds_sync();
-  const float m = key_float(uni(L.mkey));
-  const float t = m - s.dcap;
-  if (t > s.tau && !s.ovf) s.tau = t;
 }
 
 // ---------------------------------------------------------------- deciding
@@ -436,18 +209,16 @@ struct CandLocator {
     // the stream summed every element with the rounded scale c; the
     // candidates' share is replaced by their exact weights
     double corr = 0.0;
-    for (int w = 0; w < NW; ++w) {
-      const int n = L.wn[w];
-      for (int j = threadIdx.x; j < n; j += NT) {
-        const float x = L.elem[w][j].x;
-        if (!in_bins(x)) continue;
-        const int b = bin_of(x);
-        atomicAdd(&L.u.post.cnt[b], 1);
-        if (!kCode) {
-          const double we = weight(x, m, T);
-          atomicAdd(&L.u.post.mass[b], we);
-          corr += we - exp2((static_cast<double>(x) - static_cast<double>(m)) * c);
-        }
+    const int n = L.ncand;
+    for (int j = threadIdx.x; j < n; j += NT) {
+      const float x = L.c.cand[j].x;
+      if (!in_bins(x)) continue;
+      const int b = bin_of(x);
+      atomicAdd(&L.u.post.cnt[b], 1);
+      if (!kCode) {
+        const double we = weight(x, m, T);
+        atomicAdd(&L.u.post.mass[b], we);
+        corr += we - exp2((static_cast<double>(x) - static_cast<double>(m)) * c);
       }
     }
     lds_barrier();
@@ -532,14 +303,12 @@ struct CandLocator {
   __device__ int gather(int b) {
     if (threadIdx.x == 0) L.gn = 0;
     lds_barrier();
-    for (int w = 0; w < NW; ++w) {
-      const int n = L.wn[w];
-      for (int j = threadIdx.x; j < n; j += NT) {
-        const Cand e = L.elem[w][j];
-        if (!in_bins(e.x) || bin_of(e.x) != b) continue;
-        const int pos = atomicAdd(&L.gn, 1);
-        if (pos < kGather) L.u.post.g[pos] = e;
-      }
+    const int n = L.ncand;
+    for (int j = threadIdx.x; j < n; j += NT) {
+      const Cand e = L.c.cand[j];
+      if (!in_bins(e.x) || bin_of(e.x) != b) continue;
+      const int pos = atomicAdd(&L.gn, 1);
+      if (pos < kGather) L.u.post.g[pos] = e;
     }
     lds_barrier();
     const int cb = L.gn;
@@ -643,12 +412,10 @@ struct CandLocator {
   // Candidates with (x - m) / T >= lnmp; exact unless every candidate passes.
   __device__ int count_minp(double lnmp, bool& exact) {
     int cnt = 0;
-    for (int w = 0; w < NW; ++w) {
-      const int n = L.wn[w];
-      for (int j = threadIdx.x; j < n; j += NT) {
-        const float x = L.elem[w][j].x;
-        if (in_bins(x) && (static_cast<double>(x) - static_cast<double>(m)) / T >= lnmp) ++cnt;
-      }
+    const int n = L.ncand;
+    for (int j = threadIdx.x; j < n; j += NT) {
+      const float x = L.c.cand[j].x;
+      if (in_bins(x) && (static_cast<double>(x) - static_cast<double>(m)) / T >= lnmp) ++cnt;
     }
     cnt = block_reduce<NT>(cnt, SumOp(), L.red_i);
     exact = cnt < nc;
@@ -882,11 +649,35 @@ __device__ bool decide(Loc& loc, int V, int top_k, double top_p, double min_p, d
 
 namespace vsv {
 
-// Stream one sampled row: the statistics of stream_row plus candidate capture.
+// ---------------------------------------------------------------- capture
+
+// Order-preserving 16-bit code of x rounded up to bfloat16: an upper bound
+// of x in code order (exact for bfloat16 values; -0 counts as +0).
+__device__ __forceinline__ int up_code(float x) {
+  const uint32_t u = __float_as_uint(x == 0.0f ? 0.0f : x);
+  uint32_t h = u >> 16;
+  // a positive value with bits below bfloat16 rounds its magnitude up; a
+  // negative one truncates toward zero, which is up as well
+  if ((u & 0xFFFFu) && !(u & 0x80000000u)) h += 1;
+  return (h & 0x8000u) ? static_cast<int>(~h & 0xFFFFu) : static_cast<int>(h | 0x8000u);
+}
+
+// Entries of the vector-maximum codes: entry (r, t) = r * NT + t covers the
+// vectors of thread t's slot steps r * S .. r * S + S - 1 (vector k * NT + t
+// for step k). S = 1 while a row has at most kVM vectors.
+struct VmPlan {
+  int S;      // slot steps per entry
+  int rows;   // entry rows written (entries = rows * NT)
+};
+
+// Pass 1: stream one sampled row for the statistics of stream_row, and leave
+// the code of every vector's maximum in L.u.vm. Loads use the caches' normal
+// policy so that pass 2's reads of a few vectors find them there.
 template <typename E, int NT, int U>
-__device__ __forceinline__ void stream_sampled(const E* __restrict__ row, int V, float c, RowPartial& p,
-                                               SampledLds<NT>& L, WaveCap& s) {
+__device__ __forceinline__ VmPlan stream_sampled(const E* __restrict__ row, int V, float c, RowPartial& p,
+                                                 SampledLds<NT>& L) {
   constexpr int N = Elem<E>::kVec;
+  constexpr int kRowsVM = kVM / NT;
   const int tid = threadIdx.x;
   const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
   int head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(E));
@@ -895,37 +686,36 @@ __device__ __forceinline__ void stream_sampled(const E* __restrict__ row, int V,
   const int body_end = head + nvec * N;
   const u32x4* __restrict__ vp = reinterpret_cast<const u32x4*>(row + head);
   // Rolling slots: slot u holds vector g*G + u*NT + tid of group g; it is
-  // decoded and parked, then reloaded at once with the same vector of group
-  // g+1, so U-1 vectors per lane are always in flight and the loop carries
-  // no register copies (a copy at the latch would wait for every load).
-  // Loads are unconditional (clamped as in load_group, row_stream.hpp).
+  // decoded, then reloaded at once with the same vector of group g+1, so
+  // U-1 vectors per lane are always in flight and the loop carries no
+  // register copies (a copy at the latch would wait for every load). Loads
+  // are unconditional (clamped to the row's last vector).
   constexpr int G = U * NT;
   const int nfull = nvec / G;
+  const int steps = nvec > 0 ? (nvec > nfull * G ? nfull + 1 : nfull) * U : 0;
+  VmPlan plan{max(1, (steps + kRowsVM - 1) / kRowsVM), 0};
 
-  // head elements first: a load issued after the slots' would make the
-  // first wait cover them too
   const bool has_head = tid < head;
   const float xh = has_head ? Elem<E>::at(row, tid) : -INFINITY;
   u32x4 slot[U];
-  if (nvec > 0) load_group<NT, U>(slot, vp, 0, nvec);
-
-  // Starting threshold: the block's max over its first group (and head).
-  {
-    float m0 = xh;
-    if (nvec > 0) {
+  if (nvec > 0) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (tid + u * NT < nvec) {
-          float f[N];
-          m0 = fmaxf(m0, vec_max<E>(slot[u], f));
-        }
-      }
-    }
-    block_start_max<NT>(L, s, m0);
+    for (int u = 0; u < U; ++u) slot[u] = vp[min(tid + u * NT, nvec - 1)];
   }
   if (has_head) take_scalar<false>(p, xh, tid, c, INFINITY, 0);
-  wave_take_scalar<NT>(L, s, xh, tid, has_head);
 
+  // the running maximum of the current entry (uniform countdown of steps)
+  float run = -INFINITY;
+  int left = plan.S;
+  auto note = [&](float vmax) {
+    run = fmaxf(run, vmax);
+    if (--left == 0) {
+      L.u.vm[plan.rows * NT + tid] = static_cast<uint16_t>(up_code(run));
+      run = -INFINITY;
+      left = plan.S;
+      ++plan.rows;
+    }
+  };
   if (nvec > 0) {
     for (int g = 0; g < nfull; ++g) {
       const int v = g * G + tid;
@@ -933,35 +723,327 @@ __device__ __forceinline__ void stream_sampled(const E* __restrict__ row, int V,
       for (int u = 0; u < U; ++u) {
         float f[N];
         const float vmax = vec_max<E>(slot[u], f);
-        const int e0 = head + (v + u * NT) * N;
-        const bool full = wave_park_only<NT>(L, s, slot[u], e0, vmax, true);
-        slot[u] = load_stream(vp + min(v + G + u * NT, nvec - 1));
+        slot[u] = vp[min(v + G + u * NT, nvec - 1)];
         take_floats<N>(p, f, vmax, c);
-        if (full) wave_drain<E, NT>(L, s);
+        note(vmax);
       }
-      wave_sync_max<NT>(L, s, p.best);
     }
-    // the slots now hold group nfull, the partial last one
+    if (nvec > nfull * G) {
+      // the slots hold group nfull, the partial last one
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int q = nfull * G + tid + u * NT;
-      const bool valid = q < nvec;
-      float f[N];
-      float vmax = -INFINITY;
-      if (valid) {
-        vmax = vec_max<E>(slot[u], f);
-        take_floats<N>(p, f, vmax, c);
+      for (int u = 0; u < U; ++u) {
+        const int q = nfull * G + tid + u * NT;
+        float f[N];
+        float vmax = -INFINITY;
+        if (q < nvec) {
+          vmax = vec_max<E>(slot[u], f);
+          take_floats<N>(p, f, vmax, c);
+        }
+        note(vmax);
       }
-      if (wave_park_only<NT>(L, s, slot[u], head + q * N, vmax, valid)) wave_drain<E, NT>(L, s);
+    }
+    if (left != plan.S) {
+      L.u.vm[plan.rows * NT + tid] = static_cast<uint16_t>(up_code(run));
+      ++plan.rows;
+    }
+  }
+  const int tail = V - body_end;
+  if (tid < tail) take_scalar<false>(p, Elem<E>::at(row, body_end + tid), body_end + tid, c, INFINITY, 0);
+  return plan;
+}
+
+// Counts of vector-maximum codes >= each of the codes ct[0 .. C-1], over the
+// row's entries (every thread reads eight codes at a time).
+template <int NT, int C>
+__device__ __forceinline__ void count_codes(SampledLds<NT>& L, const VmPlan& plan, const int* ct, int* out) {
+  constexpr int NW = NT / kWave;
+  const int ne = plan.rows * NT;   // a multiple of 8: NT is
+  int n[C];
+#pragma unroll
+  for (int i = 0; i < C; ++i) n[i] = 0;
+  for (int g = threadIdx.x; g * 8 < ne; g += NT) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(&L.u.vm[g * 8]);
+    const uint32_t h[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int code = static_cast<int>((h[q / 2] >> (16 * (q & 1))) & 0xFFFFu);
+#pragma unroll
+      for (int i = 0; i < C; ++i) n[i] += code >= ct[i] ? 1 : 0;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < C; ++i) n[i] = wave_all(n[i], SumOp());
+  lds_barrier();
+  if (lane_id() == 0) {
+#pragma unroll
+    for (int i = 0; i < C; ++i) L.c.hist[0][wave_id() * C + i] = n[i];
+  }
+  lds_barrier();
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    int t = 0;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) t += L.c.hist[0][ww * C + i];
+    out[i] = t;
+  }
+  lds_barrier();
+}
+
+// The k-th largest vector-maximum code among those within `span` of the
+// row maximum's, as a value: a lower bound of the row's k-th largest element
+// (k vectors have a maximum at least that large; float32 codes are rounded
+// up, so the bound steps down one code). `have` codes lie in range (at
+// least k). Few of them (at most kGather): they are gathered and ranked;
+// otherwise a histogram over the range finds the code.
+template <typename E, int NT>
+__device__ float kth_code_value(SampledLds<NT>& L, const VmPlan& plan, int k, int mc, int span, int have) {
+  constexpr int NW = NT / kWave;
+  constexpr int PER = kTopBins / NT;
+  const int tid = threadIdx.x, w = wave_id(), lane = lane_id();
+  const int ne = plan.rows * NT;
+  const int lo = mc - span + 1;
+  int code = 0;
+  if (have <= kGather) {
+    // gather the codes >= lo (indices irrelevant) and rank them
+    if (tid == 0) L.gn = 0;
+    lds_barrier();
+    for (int g = tid; g * 8 < ne; g += NT) {
+      const u32x4 cw = *reinterpret_cast<const u32x4*>(&L.u.vm[g * 8]);
+      const uint32_t hw[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int c = static_cast<int>((hw[q / 2] >> (16 * (q & 1))) & 0xFFFFu);
+        if (c >= lo) {
+          const int pos = atomicAdd(&L.gn, 1);
+          if (pos < kGather) L.c.hist[0][pos] = c;
+        }
+      }
+    }
+    lds_barrier();
+    const int n = min(L.gn, kGather);
+    if (tid == 0) L.bi[0] = -1;
+    lds_barrier();
+    if (tid < n) {
+      // the code with exactly k - 1 codes above it, or the last of a tie
+      // group that straddles rank k - 1
+      const int mine = L.c.hist[0][tid];
+      int above = 0, equal_before = 0;
+      for (int o = 0; o < n; ++o) {
+        const int c = L.c.hist[0][o];
+        above += c > mine ? 1 : 0;
+        equal_before += (c == mine && o < tid) ? 1 : 0;
+      }
+      if (above + equal_before == k - 1) L.bi[0] = mine;
+    }
+    lds_barrier();
+    code = L.bi[0];
+    lds_barrier();
+    if (code < 0) return -INFINITY;
+  } else {
+    int* h = L.c.hist[w];
+    for (int b = lane; b < kTopBins; b += kWave) h[b] = 0;
+    wave_lds_sync();
+    for (int g = tid; g * 8 < ne; g += NT) {
+      const u32x4 cw = *reinterpret_cast<const u32x4*>(&L.u.vm[g * 8]);
+      const uint32_t hw[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int d = mc - static_cast<int>((hw[q / 2] >> (16 * (q & 1))) & 0xFFFFu);
+        if (d >= 0 && d < span) atomicAdd(&h[d], 1);
+      }
+    }
+    lds_barrier();
+    int cnt[PER];
+    int sc = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      int v = 0;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) v += L.c.hist[ww][tid * PER + q];
+      cnt[q] = v;
+      sc += v;
+    }
+    if (tid == 0) L.bi[0] = kTopBins;
+    int tot;
+    const int incl = block_scan_incl<NT, int>(sc, L.red_i, tot);
+    int run = incl - sc, found = kTopBins;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      run += cnt[q];
+      if (run >= k && found == kTopBins) found = tid * PER + q;
+    }
+    if (found < kTopBins) atomicMin(&L.bi[0], found);
+    lds_barrier();
+    const int b = L.bi[0];
+    lds_barrier();
+    if (b >= kTopBins) return -INFINITY;
+    code = mc - b;
+  }
+  return bf16_of_code(code - (sizeof(E) == 2 ? 0 : 1));
+}
+
+// The capture threshold: at least `floor_tau`, and high enough that at most
+// `cap` vectors (top-k rows: exactly the k-th largest) qualify. Counting
+// passes decide whether the floor suffices and, if not, which range of
+// codes holds the cut.
+template <typename E, int NT>
+__device__ float capture_threshold(SampledLds<NT>& L, const VmPlan& plan, float m, float floor_tau, int k, bool topk) {
+  const int mc = up_code(m);
+  const int spans[3] = {16, 128, kTopBins};
+  if (!topk) {
+    // the window fits as it is (the usual case): one count decides
+    const int c0 = up_code(floor_tau);
+    int n0;
+    count_codes<NT, 1>(L, plan, &c0, &n0);
+    if (n0 <= k) return floor_tau;
+  }
+  const int ct[3] = {mc - spans[0] + 1, mc - spans[1] + 1, mc - spans[2] + 1};
+  int n[3];
+  count_codes<NT, 3>(L, plan, ct, n);
+  // the narrowest range holding k codes
+  int span = -1, have = 0;
+  for (int i = 0; i < 3 && span < 0; ++i)
+    if (n[i] >= k) {
+      span = spans[i];
+      have = n[i];
+    }
+  if (span < 0) return topk ? -INFINITY : floor_tau;
+  const float t = kth_code_value<E, NT>(L, plan, k, mc, span, have);
+  return fmaxf(t, floor_tau);
+}
+
+// Pass 2: every element >= tau of the row into L.c.cand (L.ncand of them).
+// Each wave picks the entries of its share whose code reaches tau's (their
+// indices overwrite the front of the share), reads their vectors again in
+// batches (every load in a batch issued before any is used) and appends the
+// elements >= tau, reserving room with one LDS atomic per step. Returns
+// false if the row has more than kCand such elements.
+template <typename E, int NT>
+__device__ bool capture_row(const E* __restrict__ row, int V, float tau, const VmPlan& plan, SampledLds<NT>& L) {
+  constexpr int N = Elem<E>::kVec;
+  constexpr int NW = NT / kWave;
+  constexpr int kB = 8;        // entries per lane per batch
+  const int w = wave_id(), lane = lane_id();
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
+  int head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(E));
+  if (head > V) head = V;
+  const int nvec = (V - head) / N;
+  const int body_end = head + nvec * N;
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<E*>(row + head), 0, nvec * 16, 0x00020000);
+  if (threadIdx.x == 0) {
+    L.ncand = 0;
+    L.ovf = 0;
+  }
+  lds_barrier();
+  const int ct = up_code(tau);
+
+  // A: pick the share's entries whose code reaches tau's, eight codes per
+  // lane per step (a share is a multiple of 8 entries); their indices
+  // overwrite the front of the share (a step writes below what it read)
+  const int ne = plan.rows * NT;
+  const int per = ((ne + NW - 1) / NW + 7) / 8 * 8;
+  const int s0 = w * per, s1 = min(ne, s0 + per);
+  int np = 0;
+  for (int base = s0; base < s1; base += kWave * 8) {
+    const int e8 = base + lane * 8;
+    u32x4 cw = {0u, 0u, 0u, 0u};
+    if (e8 < s1) cw = *reinterpret_cast<const u32x4*>(&L.u.vm[e8]);
+    const uint32_t hw[4] = {cw.x, cw.y, cw.z, cw.w};
+    bool any = false;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) any |= static_cast<int>((hw[q / 2] >> (16 * (q & 1))) & 0xFFFFu) >= ct;
+    if (__ballot(any) == 0) continue;   // nothing picked: nothing written
+    wave_lds_sync();  // this step's reads come before its writes
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int code = static_cast<int>((hw[q / 2] >> (16 * (q & 1))) & 0xFFFFu);
+      const bool pick = e8 < s1 && code >= ct;   // s1 is a multiple of 8
+      const uint64_t bal = __ballot(pick);
+      if (pick) L.u.vm[s0 + np + mbcnt(bal)] = static_cast<uint16_t>(e8 + q);
+      np += __popcll(bal);
+    }
+    wave_lds_sync();
+  }
+
+  // B: their vectors, kB entries per lane at a time; a lane past the list
+  // (or a vector past the row) loads through an out-of-range offset, which
+  // returns zero without touching memory, and its elements are ignored. A
+  // lane counts its elements >= tau, a wave scan places them, and one LDS
+  // atomic per batch reserves the wave's room.
+  for (int j0 = 0; j0 < np; j0 += kWave * kB) {
+    for (int sstep = 0; sstep < plan.S; ++sstep) {
+      u32x4 v[kB];
+      int vi[kB];
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
+        const int j = j0 + b * kWave + lane;
+        int q = -1;
+        if (j < np) {
+          const int e = L.u.vm[s0 + j];
+          q = ((e / NT) * plan.S + sstep) * NT + (e % NT);
+          if (q >= nvec) q = -1;
+        }
+        vi[b] = q;
+        const uint32_t off = q >= 0 ? static_cast<uint32_t>(q) * 16u : 0xFFFFFFF0u;
+        v[b] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
+      }
+      int mine = 0;
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
+        float f[N];
+        Elem<E>::decode(v[b], f);
+#pragma unroll
+        for (int k = 0; k < N; ++k) mine += (vi[b] >= 0 && f[k] >= tau) ? 1 : 0;
+      }
+      // the write pass decodes again rather than keeping every element live
+#pragma unroll
+      for (int b = 0; b < kB; ++b) asm volatile("" : "+v"(v[b]));
+      const int incl = wave_scan_incl(mine);
+      const int total = read_lane(incl, kWave - 1);
+      if (total == 0) continue;
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&L.ncand, total);
+      base = __builtin_amdgcn_readfirstlane(base);
+      int pos = base + incl - mine;
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
+        if (vi[b] < 0) continue;
+        float f[N];
+        Elem<E>::decode(v[b], f);
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+          if (f[k] >= tau) {
+            if (pos < kCand) L.c.cand[pos] = Cand{f[k], head + vi[b] * N + k};
+            ++pos;
+          }
+        }
+      }
     }
   }
 
-  const int tail = V - body_end;
-  const bool has_tail = tid < tail;
-  const float xt = has_tail ? Elem<E>::at(row, body_end + tid) : -INFINITY;
-  if (has_tail) take_scalar<false>(p, xt, body_end + tid, c, INFINITY, 0);
-  wave_take_scalar<NT>(L, s, xt, body_end + tid, has_tail);
-  wave_drain<E, NT>(L, s);
+  // C: elements outside the 16-byte body (wave 0: lanes 0 .. 7 the head,
+  // lanes 8 .. 15 the tail)
+  if (w == 0) {
+    const int te = body_end + (lane - 8);
+    const bool hv = lane < head;
+    const bool tv = lane >= 8 && lane < 16 && te < V;
+    const int e = hv ? lane : te;
+    const float x = (hv || tv) ? Elem<E>::at(row, e) : -INFINITY;
+    const bool take = (hv || tv) && x >= tau;
+    const uint64_t bal = __ballot(take);
+    if (bal) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&L.ncand, __popcll(bal));
+      base = __builtin_amdgcn_readfirstlane(base);
+      const int pos = base + mbcnt(bal);
+      if (take && pos < kCand) L.c.cand[pos] = Cand{x, e};
+    }
+  }
+  lds_barrier();
+  const bool ok = L.ncand <= kCand;
+  lds_barrier();
+  return ok;
 }
 
 // Outcome of one sampled row.
@@ -989,49 +1071,37 @@ __device__ __forceinline__ SampledOut sampled_row(const VerifyArgs& a, const E* 
   const double Td = static_cast<double>(T);
   const float c = 1.4426950408889634f / T;
 
-  // Capture window below the running max: T * kZcap (weights under e^-kZcap
-  // of the max's), or exactly the min-p cut when min-p alone filters. A
-  // top-k cut is a count, which an outlying max can push below any window,
-  // so top-k rows use no window: compaction alone raises their threshold and
-  // always keeps top_k + 32 candidates per wave (the union then holds the
-  // whole top-k set whenever top_k + 32 fits a wave's buffer).
-  const bool tk = top_k > 0 && top_k < a.V;
-  float dcap = tk ? FLT_MAX : T * kZcap;
-  if (min_p > 0.f && top_p >= 1.f && !tk) {
-    const float dm = static_cast<float>(-Td * log(static_cast<double>(min_p))) * 1.0001f + 1e-6f;
-    dcap = fminf(dcap, dm);
-  }
-  if (!(dcap < INFINITY)) dcap = FLT_MAX;
-  const int kmin = tk ? min(top_k + 32, kEW - 2 * kWave) : 0;
-
-  const int w = wave_id();
-  if (threadIdx.x == 0) L.mkey = INT32_MIN;
-  lds_barrier();
-  WaveCap s{0, 0, -INFINITY, -INFINITY, dcap, 0, kmin};
-
   RowPartial p;
   partial_init(p);
-  stream_sampled<E, NT, U>(row, a.V, c, p, L, s);
+  const VmPlan plan = stream_sampled<E, NT, U>(row, a.V, c, p, L);
   after_stream();
-  if (lane_id() == 0) {
-    L.wtau[w] = s.ovf ? INFINITY : s.tau;
-    L.wn[w] = s.elem_n;
-    L.wovf[w] = s.ovf;
-  }
   const NoKeep nokeep;
   const RowResult res = finish_row<E, NT, U, false, false>(p, L.rs, nokeep, row, a.V);
   out.lse = res.lse;
   if (!(res.max < INFINITY) || !(res.max > -INFINITY) || !isfinite(res.lse)) out.bits |= VSV_FLAG_LOGITS;
-
-  constexpr int NW = NT / kWave;
-  float tau = -INFINITY;
-  int ovf = 0;
-#pragma unroll
-  for (int k = 0; k < NW; ++k) {
-    tau = fmaxf(tau, L.wtau[k]);
-    ovf |= L.wovf[k];
-  }
   const float m = res.max;
+
+  // Capture threshold: T * kZcap below the maximum (weights under e^-kZcap
+  // of the max's), or exactly the min-p cut when min-p alone filters, but
+  // no lower than the kCapVec-th largest vector maximum, so the candidates
+  // fit. A top-k cut is a count, which an outlying maximum can push below
+  // any window, so a top-k row captures down to its k-th largest vector
+  // maximum instead. Whether the candidates suffice is decided from exact
+  // mass accounting afterwards.
+  const bool tk = top_k > 0 && top_k < a.V;
+  float tau = -INFINITY;
+  if (!out.bits) {
+    if (tk) {
+      tau = capture_threshold<E, NT>(L, plan, m, -INFINITY, top_k, true);
+    } else {
+      float dcap = T * kZcap;
+      if (min_p > 0.f && top_p >= 1.f) {
+        const float dm = static_cast<float>(-Td * log(static_cast<double>(min_p))) * 1.0001f + 1e-6f;
+        dcap = fminf(dcap, dm);
+      }
+      tau = capture_threshold<E, NT>(L, plan, m, (dcap < INFINITY) ? m - dcap : -INFINITY, kCapVec, false);
+    }
+  }
   const double u = row_uniform(a.seed, a.offset, req, j);
   // whole-row weight relative to the maximum, with the stream's exponents
   // (x * c with c = log2(e) / T rounded to float); CandLocator::build swaps
@@ -1040,7 +1110,7 @@ __device__ __forceinline__ SampledOut sampled_row(const VerifyArgs& a, const E* 
                                      static_cast<double>(m) * static_cast<double>(c));
   int token = 0;
   bool done = false;
-  if (!ovf && !out.bits) {
+  if (!out.bits && tau > -INFINITY && capture_row<E, NT>(row, a.V, tau, plan, L)) {
     CandLocator<E, NT> loc(L, m, Td, tau, wtot, static_cast<double>(c));
     loc.build();
     int t = 0;
