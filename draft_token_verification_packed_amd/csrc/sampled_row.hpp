@@ -62,7 +62,10 @@ template <int NT> struct SampledLds {
   static constexpr int NW = NT / kWave;
   static_assert(NT >= kGather && NT <= 1024 && kNB % NT == 0 && kTopBins % NT == 0, "one gathered element per thread");
   union {
-    uint16_t vm[kVM];  // pass 1: vector-maximum codes; pass 2: indices of the picked ones
+    struct {
+      alignas(16) uint16_t l1[kVM];  // pass 1: entry codes; pass 2: indices of the picked entries
+      uint16_t l2[kVM / 8];          // block codes (top-k rows)
+    } vm;
     struct {
       int cnt[kNB + 1];
       double mass[kNB + 1];
@@ -662,12 +665,14 @@ __device__ __forceinline__ int up_code(float x) {
   return (h & 0x8000u) ? static_cast<int>(~h & 0xFFFFu) : static_cast<int>(h | 0x8000u);
 }
 
-// Entries of the vector-maximum codes: entry (r, t) = r * NT + t covers the
-// vectors of thread t's slot steps r * S .. r * S + S - 1 (vector k * NT + t
-// for step k). S = 1 while a row has at most kVM vectors.
+// Entries of the vector-maximum codes: entry (r, t) = l1[r * NT + t] covers
+// the vectors of thread t's slot steps r * S .. r * S + S - 1 (vector
+// k * NT + t for step k). S = 1 while a row has at most kVM vectors. Block
+// (b, t) = l2[b * NT + t] is the largest code of entries (8b .. 8b + 7, t).
 struct VmPlan {
-  int S;      // slot steps per entry
-  int rows;   // entry rows written (entries = rows * NT)
+  int S;       // slot steps per entry
+  int rows;    // entry rows written (entries = rows * NT)
+  int blocks;  // blocks of eight entry rows (blocks * NT of them)
 };
 
 // Pass 1: stream one sampled row for the statistics of stream_row, and leave
@@ -693,7 +698,7 @@ __device__ __forceinline__ VmPlan stream_sampled(const E* __restrict__ row, int 
   constexpr int G = U * NT;
   const int nfull = nvec / G;
   const int steps = nvec > 0 ? (nvec > nfull * G ? nfull + 1 : nfull) * U : 0;
-  VmPlan plan{max(1, (steps + kRowsVM - 1) / kRowsVM), 0};
+  VmPlan plan{max(1, (steps + kRowsVM - 1) / kRowsVM), 0, 0};
 
   const bool has_head = tid < head;
   const float xh = has_head ? Elem<E>::at(row, tid) : -INFINITY;
@@ -707,13 +712,22 @@ __device__ __forceinline__ VmPlan stream_sampled(const E* __restrict__ row, int 
   // the running maximum of the current entry (uniform countdown of steps)
   float run = -INFINITY;
   int left = plan.S;
+  int bmax = 0;   // the largest code of the current block
+  auto push = [&](int code) {
+    L.u.vm.l1[plan.rows * NT + tid] = static_cast<uint16_t>(code);
+    bmax = max(bmax, code);
+    if ((++plan.rows & 7) == 0) {
+      L.u.vm.l2[plan.blocks * NT + tid] = static_cast<uint16_t>(bmax);
+      ++plan.blocks;
+      bmax = 0;
+    }
+  };
   auto note = [&](float vmax) {
     run = fmaxf(run, vmax);
     if (--left == 0) {
-      L.u.vm[plan.rows * NT + tid] = static_cast<uint16_t>(up_code(run));
+      push(up_code(run));
       run = -INFINITY;
       left = plan.S;
-      ++plan.rows;
     }
   };
   if (nvec > 0) {
@@ -742,9 +756,10 @@ __device__ __forceinline__ VmPlan stream_sampled(const E* __restrict__ row, int 
         note(vmax);
       }
     }
-    if (left != plan.S) {
-      L.u.vm[plan.rows * NT + tid] = static_cast<uint16_t>(up_code(run));
-      ++plan.rows;
+    if (left != plan.S) push(up_code(run));
+    if (plan.rows & 7) {
+      L.u.vm.l2[plan.blocks * NT + tid] = static_cast<uint16_t>(bmax);
+      ++plan.blocks;
     }
   }
   const int tail = V - body_end;
@@ -762,7 +777,7 @@ __device__ __forceinline__ void count_codes(SampledLds<NT>& L, const VmPlan& pla
 #pragma unroll
   for (int i = 0; i < C; ++i) n[i] = 0;
   for (int g = threadIdx.x; g * 8 < ne; g += NT) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(&L.u.vm[g * 8]);
+    const u32x4 w = *reinterpret_cast<const u32x4*>(&L.u.vm.l1[g * 8]);
     const uint32_t h[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -789,6 +804,45 @@ __device__ __forceinline__ void count_codes(SampledLds<NT>& L, const VmPlan& pla
   lds_barrier();
 }
 
+// The k-th largest block code (l2) within kTopBins codes of mc, or -1 when
+// fewer than k lie there. k blocks hold an entry code at least that large,
+// so it bounds the k-th largest entry code from below.
+template <int NT>
+__device__ int kth_block_code(SampledLds<NT>& L, const VmPlan& plan, int k, int mc) {
+  constexpr int PER = kTopBins / NT;
+  const int tid = threadIdx.x;
+  int* h = L.c.hist[0];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) h[tid * PER + q] = 0;
+  if (tid == 0) L.bi[0] = kTopBins;
+  lds_barrier();
+  for (int g = tid; g < plan.blocks * NT; g += NT) {
+    const int d = mc - static_cast<int>(L.u.vm.l2[g]);
+    if (d >= 0 && d < kTopBins) atomicAdd(&h[d], 1);
+  }
+  lds_barrier();
+  int cnt[PER];
+  int sc = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    cnt[q] = h[tid * PER + q];
+    sc += cnt[q];
+  }
+  int tot;
+  const int incl = block_scan_incl<NT, int>(sc, L.red_i, tot);
+  int run = incl - sc, found = kTopBins;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    run += cnt[q];
+    if (run >= k && found == kTopBins) found = tid * PER + q;
+  }
+  if (found < kTopBins) atomicMin(&L.bi[0], found);
+  lds_barrier();
+  const int b = L.bi[0];
+  lds_barrier();
+  return b < kTopBins ? mc - b : -1;
+}
+
 // The k-th largest vector-maximum code among those within `span` of the
 // row maximum's, as a value: a lower bound of the row's k-th largest element
 // (k vectors have a maximum at least that large; float32 codes are rounded
@@ -808,7 +862,7 @@ __device__ float kth_code_value(SampledLds<NT>& L, const VmPlan& plan, int k, in
     if (tid == 0) L.gn = 0;
     lds_barrier();
     for (int g = tid; g * 8 < ne; g += NT) {
-      const u32x4 cw = *reinterpret_cast<const u32x4*>(&L.u.vm[g * 8]);
+      const u32x4 cw = *reinterpret_cast<const u32x4*>(&L.u.vm.l1[g * 8]);
       const uint32_t hw[4] = {cw.x, cw.y, cw.z, cw.w};
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -844,7 +898,7 @@ __device__ float kth_code_value(SampledLds<NT>& L, const VmPlan& plan, int k, in
     for (int b = lane; b < kTopBins; b += kWave) h[b] = 0;
     wave_lds_sync();
     for (int g = tid; g * 8 < ne; g += NT) {
-      const u32x4 cw = *reinterpret_cast<const u32x4*>(&L.u.vm[g * 8]);
+      const u32x4 cw = *reinterpret_cast<const u32x4*>(&L.u.vm.l1[g * 8]);
       const uint32_t hw[4] = {cw.x, cw.y, cw.z, cw.w};
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -890,6 +944,12 @@ template <typename E, int NT>
 __device__ float capture_threshold(SampledLds<NT>& L, const VmPlan& plan, float m, float floor_tau, int k, bool topk) {
   const int mc = up_code(m);
   const int spans[3] = {16, 128, kTopBins};
+  if (topk && k <= plan.blocks * NT) {
+    // the k-th largest block code: a lower bound of the k-th largest entry
+    // code, close to it when the top entries lie in distinct blocks
+    const int cb = kth_block_code<NT>(L, plan, k, mc);
+    if (cb >= 0) return bf16_of_code(cb - (sizeof(E) == 2 ? 0 : 1));
+  }
   if (!topk) {
     // the window fits as it is (the usual case): one count decides
     const int c0 = up_code(floor_tau);
@@ -948,7 +1008,7 @@ __device__ bool capture_row(const E* __restrict__ row, int V, float tau, const V
   for (int base = s0; base < s1; base += kWave * 8) {
     const int e8 = base + lane * 8;
     u32x4 cw = {0u, 0u, 0u, 0u};
-    if (e8 < s1) cw = *reinterpret_cast<const u32x4*>(&L.u.vm[e8]);
+    if (e8 < s1) cw = *reinterpret_cast<const u32x4*>(&L.u.vm.l1[e8]);
     const uint32_t hw[4] = {cw.x, cw.y, cw.z, cw.w};
     bool any = false;
 #pragma unroll
@@ -960,7 +1020,7 @@ __device__ bool capture_row(const E* __restrict__ row, int V, float tau, const V
       const int code = static_cast<int>((hw[q / 2] >> (16 * (q & 1))) & 0xFFFFu);
       const bool pick = e8 < s1 && code >= ct;   // s1 is a multiple of 8
       const uint64_t bal = __ballot(pick);
-      if (pick) L.u.vm[s0 + np + mbcnt(bal)] = static_cast<uint16_t>(e8 + q);
+      if (pick) L.u.vm.l1[s0 + np + mbcnt(bal)] = static_cast<uint16_t>(e8 + q);
       np += __popcll(bal);
     }
     wave_lds_sync();
@@ -980,7 +1040,7 @@ __device__ bool capture_row(const E* __restrict__ row, int V, float tau, const V
         const int j = j0 + b * kWave + lane;
         int q = -1;
         if (j < np) {
-          const int e = L.u.vm[s0 + j];
+          const int e = L.u.vm.l1[s0 + j];
           q = ((e / NT) * plan.S + sstep) * NT + (e % NT);
           if (q >= nvec) q = -1;
         }
