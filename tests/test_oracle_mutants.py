@@ -2,10 +2,11 @@
 
 Each mutant plants one plausible mistake in a copy of `oracle/` (a dropped
 term, a wrong tie rule or boundary, an off-by-one index, a swapped filter
-order, a wrong Philox constant). The pin suite `test_oracle_pins.py` then
-runs against the mutant in a subprocess and must fail: a mistake that no
-pin catches would also slip past parity, since parity compares the HIP path
-with this oracle.
+order, a wrong Philox constant). The pin suite of the mutated module
+(`test_oracle_pins.py`, or `test_oracle_allocate.py` for the verify
+allocation) then runs against the mutant in a subprocess and must fail: a
+mistake that no pin catches would also slip past parity, since parity
+compares the HIP path with this oracle.
 """
 import concurrent.futures
 import os
@@ -18,6 +19,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")
+PINS_BY_FILE = {"allocate.py": os.path.join(ROOT, "tests", "test_oracle_allocate.py")}
 
 # (name, file, original text, mutated text); the original must occur once.
 MUTANTS = [
@@ -86,6 +88,21 @@ MUTANTS = [
     ("uniform_drops_a_bit", "philox.py",
      "return (w[0] >> 8) * (1.0 / 16777216.0)",
      "return (w[0] >> 9) * (1.0 / 16777216.0)"),
+    ("allocation_scores_not_products", "allocate.py",
+     "run = np.float32(run * c[i, j])",
+     "run = np.float32(c[i, j])"),
+    ("allocation_ties_request_desc", "allocate.py",
+     "np.lexsort((jj.ravel(), ii.ravel(), -P.ravel().astype(np.float64)))",
+     "np.lexsort((jj.ravel(), -ii.ravel(), -P.ravel().astype(np.float64)))"),
+    ("allocation_budget_without_bonus_rows", "allocate.py",
+     "    M = G - B\n",
+     "    M = G - B + 1\n"),
+    ("allocation_drafts_shifted", "allocate.py",
+     "packed[off[i] - i + j] = d[i, j]",
+     "packed[off[i] - i + j] = d[i, min(j + 1, K - 1)]"),
+    ("allocation_source_stride", "allocate.py",
+     "source[off[i] + j] = i * (K + 1) + j",
+     "source[off[i] + j] = i * K + j"),
 ]
 
 
@@ -103,7 +120,7 @@ def _run_pins_on(name, fname, old, new):
         # the mutant package comes first; the repository (synth, tests) after it
         env["PYTHONPATH"] = os.pathsep.join([tmp, ROOT])
         env["PYTHONDONTWRITEBYTECODE"] = "1"
-        cmd = [sys.executable, "-m", "pytest", PINS, "-x", "-q", "-p", "no:cacheprovider",
+        cmd = [sys.executable, "-m", "pytest", PINS_BY_FILE.get(fname, PINS), "-x", "-q", "-p", "no:cacheprovider",
                "--import-mode=append", "--rootdir", ROOT]
         if fname != "philox.py":
             cmd += ["-k", "not rocrand"]
