@@ -130,6 +130,55 @@ def cpu_baseline(wl, budget_s=12.0):
                        % (passes, wl.R, "plus its draft rows" if wl.D else "verify rows only", dt))
 
 
+def bench_allocate(args, vsv, torch):
+    """Adaptive verify allocation at the large mixed batch's shape (B=512,
+    K=7, budget G = B + B * K / 2 rows), scores from the seeded generator.
+    One workgroup; the kernel is latency-bound, so the line reports its
+    launch time, with its algorithmic bytes against HBM for reference."""
+    import numpy as np
+    import synth
+    from oracle.allocate import allocate_verify
+    B, K = 512, 7
+    G = B + (B * K) // 2
+    conf, drafts = synth.scores(B, K, 1006, "confidence")
+    c, d = upload(torch, conf), upload(torch, drafts)
+    call, out = vsv.prepare_allocate(c, d, B, K, G)
+    for _ in range(args.warmup):
+        call.run()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(args.steps):
+        call.run()
+    ev[1].record()
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / args.steps
+    ref = allocate_verify(conf, drafts, B, K, G)
+    assert np.array_equal(out["verify_len"].cpu().numpy(), ref["verify_len"]), "allocation differs from the oracle"
+    # scores and drafts read; lengths, offsets, owners, sources, packed drafts, products written
+    nbytes = 4 * (2 * B * K + B + (B + 1) + 2 * G + (G - B) + B * K)
+    achieved = nbytes / (us * 1e-6) / 1e9
+    line = dict(metric="adaptive verify allocation latency, B=512 K=7 G=2304", value=us, unit="us",
+                n_gpus=1, steps=args.steps, warmup=args.warmup, ms_per_step=us * 1e-3, higher_is_better=False,
+                scaling="weak", vs_baseline=None, dtype="f32", data="synthetic",
+                config=dict(workload="adaptive verify allocation, B=512 K=7 G=2304, confidence-shaped scores",
+                            B=B, K=K, G=G, score_seed=1006),
+                roofline=dict(bound="hbm", kernel="allocate_kernel", achieved=achieved, peak=HBM_PEAK_GBPS,
+                              unit="GB/s", frac=achieved / HBM_PEAK_GBPS, traffic=None, bytes_per_launch=nbytes,
+                              launch_us=us, note="one workgroup: bound by latency, not bandwidth"))
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < 10.0:
+            allocate_verify(conf, drafts, B, K, G)
+            n += 1
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = dict(value=dt / n * 1e6, unit="us", cores=1, kind="oracle",
+                                    sample="%d allocations of the same batch, %.1f s, single process" % (n, dt))
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +189,8 @@ def main():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
                     help="workload (default: EAGLE greedy B=128 K=4 V=152064)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--allocate", action="store_true",
+                    help="time adaptive verify allocation (B=512, K=7) instead of verification")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB --steps times (calibrates "
                          "the profiler's FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
@@ -171,6 +222,8 @@ def main():
         print(json.dumps(dict(copy_probe_bytes=n, launches=args.steps)), flush=True)
         return 0
     vsv.lib()
+    if args.allocate:
+        return bench_allocate(args, vsv, torch)
     print("[bench] generating workload %d" % args.config, file=sys.stderr, flush=True)
     wl = synth.make(args.config)
     steps, kernels, ncopy, step_bytes = build_steps(vsv, torch, wl)

@@ -10,6 +10,7 @@ Entry points mirror the C ABI in include/vspec_verify.h:
     verify_sampled(logits, row_offsets, row_owner, draft_tokens,
                    temperature, top_k, top_p, min_p, seed, offset=0)
     draft_confidence(draft_logits, selected=None)
+    allocate_verify(confidence, draft_tokens, num_requests, num_drafts, row_budget)
 """
 import ctypes
 import os
@@ -50,7 +51,7 @@ class Outputs(ctypes.Structure):
 
 
 SYMBOLS = ("vsv_workspace_bytes", "vsv_workspace_init", "vsv_verify_greedy", "vsv_verify_sampled",
-           "vsv_draft_confidence", "vsv_status_string", "vsv_version")
+           "vsv_draft_confidence", "vsv_allocate_verify", "vsv_status_string", "vsv_version")
 
 _lib = None
 
@@ -76,6 +77,8 @@ def lib():
     L.vsv_verify_sampled.restype = ctypes.c_int
     L.vsv_draft_confidence.argtypes = [vp, i32, i32, i64, i32, vp, vp, vp, vp, vp]
     L.vsv_draft_confidence.restype = ctypes.c_int
+    L.vsv_allocate_verify.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    L.vsv_allocate_verify.restype = ctypes.c_int
     L.vsv_status_string.argtypes = [ctypes.c_int]
     L.vsv_status_string.restype = ctypes.c_char_p
     L.vsv_version.argtypes = []
@@ -208,6 +211,40 @@ def draft_confidence(draft_logits, selected=None, vocab=None, stream=None):
     return conf, lse, flag
 
 
+def _alloc_outputs(B, K, G, dev, with_drafts):
+    return dict(verify_len=torch.empty(B, dtype=torch.int32, device=dev),
+                row_offsets=torch.empty(B + 1, dtype=torch.int32, device=dev),
+                row_owner=torch.empty(max(G, 1), dtype=torch.int32, device=dev),
+                row_source=torch.empty(max(G, 1), dtype=torch.int32, device=dev),
+                packed_drafts=(torch.empty(max(G - B, 1), dtype=torch.int32, device=dev) if with_drafts else None),
+                prefix=torch.empty(max(B * K, 1), dtype=torch.float32, device=dev))
+
+
+def _alloc_args(confidence, draft_tokens, B, K, G, out, stream):
+    if B * K > 0:
+        _vec(confidence, B * K, torch.float32, "confidence")
+        if draft_tokens is not None:
+            _vec(draft_tokens, B * K, torch.int32, "draft_tokens")
+    pd = out["packed_drafts"] if draft_tokens is not None and G > B else None
+    return (_ptr(confidence) if B * K > 0 else None, (_ptr(draft_tokens) if pd is not None else None), int(B), int(K), int(G),
+            _ptr(out["verify_len"]), _ptr(out["row_offsets"]), _ptr(out["row_owner"]),
+            _ptr(out["row_source"]), _ptr(pd), _ptr(out["prefix"]), _stream(stream))
+
+
+def allocate_verify(confidence, draft_tokens, num_requests, num_drafts, row_budget, stream=None):
+    """Verify lengths and packed verify layout for a row budget; returns a dict of device tensors.
+
+    `confidence` and `draft_tokens` are [B * K] request-major device vectors
+    (`draft_tokens` may be None). The result's row_offsets, row_owner and
+    packed_drafts are the batch layout the verify entry points take.
+    """
+    B, K, G = int(num_requests), int(num_drafts), int(row_budget)
+    dev = confidence.device if confidence is not None else torch.device("cuda", torch.cuda.current_device())
+    out = _alloc_outputs(B, K, G, dev, draft_tokens is not None)
+    _check(lib().vsv_allocate_verify(*_alloc_args(confidence, draft_tokens, B, K, G, out, stream)))
+    return out
+
+
 class PreparedCall:
     """One entry-point call with every argument marshalled once.
 
@@ -253,6 +290,14 @@ def prepare_sampled(logits, row_offsets, row_owner, draft_tokens, temperature, t
             _stream(stream))
     return PreparedCall(lib().vsv_verify_sampled, args,
                         (batch, outs, res, ws, logits, temperature, top_k, top_p, min_p)), res
+
+
+def prepare_allocate(confidence, draft_tokens, num_requests, num_drafts, row_budget, out=None, stream=None):
+    B, K, G = int(num_requests), int(num_drafts), int(row_budget)
+    if out is None:
+        out = _alloc_outputs(B, K, G, confidence.device, draft_tokens is not None)
+    args = _alloc_args(confidence, draft_tokens, B, K, G, out, stream)
+    return PreparedCall(lib().vsv_allocate_verify, args, (confidence, draft_tokens, out)), out
 
 
 def prepare_confidence(draft_logits, selected=None, vocab=None, out=None, stream=None):

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "allocate.hpp"
 #include "kernels.hpp"
 
 using vsv::VerifyArgs;
@@ -136,6 +137,23 @@ vsv_status vsv_draft_confidence(const void* draft_logits, int32_t dtype, int32_t
   return vsv::launch_confidence(a, stream) == hipSuccess ? VSV_OK : VSV_EHIP;
 }
 
+vsv_status vsv_allocate_verify(const float* confidence, const int32_t* draft_tokens, int32_t num_requests,
+                               int32_t num_drafts, int32_t row_budget, int32_t* verify_len, int32_t* row_offsets,
+                               int32_t* row_owner, int32_t* row_source, int32_t* packed_drafts, float* prefix,
+                               hipStream_t stream) {
+  const int32_t B = num_requests, K = num_drafts, G = row_budget;
+  if (B < 0 || K < 0 || G < B) return VSV_EINVAL;
+  if (static_cast<int64_t>(G) > static_cast<int64_t>(B) * (K + 1)) return VSV_EINVAL;
+  if (B == 0) return VSV_OK;
+  if (B > vsv::kMaxAllocRequests || static_cast<int64_t>(B) * K > vsv::kMaxAllocPositions) return VSV_EINVAL;
+  if (K > 0 && !confidence) return VSV_EINVAL;
+  if (!verify_len || !row_offsets || !row_owner) return VSV_EINVAL;
+  if ((draft_tokens == nullptr) != (packed_drafts == nullptr)) return VSV_EINVAL;
+  vsv::AllocArgs a{confidence, draft_tokens, B, K, G, verify_len, row_offsets, row_owner, row_source,
+                   G > B ? packed_drafts : nullptr, prefix};
+  return vsv::launch_allocate(a, stream) == hipSuccess ? VSV_OK : VSV_EHIP;
+}
+
 const char* vsv_status_string(vsv_status status) {
   switch (status) {
     case VSV_OK: return "ok";
@@ -147,6 +165,6 @@ const char* vsv_status_string(vsv_status status) {
   return "unknown status";
 }
 
-int32_t vsv_version(void) { return 100; }
+int32_t vsv_version(void) { return 101; }
 
 }  // extern "C"

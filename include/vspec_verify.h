@@ -155,6 +155,49 @@ vsv_status vsv_draft_confidence(const void* draft_logits, int32_t dtype,
                                 float* lse, int32_t* error_flag,
                                 hipStream_t stream);
 
+/* Adaptive target-verify allocation: how many leading drafts of each request
+ * the target verifies under a padded row budget, and the packed layout of
+ * those verify rows (xLLM docs, "Adaptive speculative inference": the
+ * enable_adaptive_target_verify switch, and section "Adaptive target
+ * verification from MTP logits": every draft step still runs, the host fixes
+ * the padded target-row budget ahead of the round, and the round's draft
+ * confidence scores stay on the device to decide the prefix allocation and
+ * the packing).
+ *
+ * Inputs (device, request-major, B requests of K drafts each):
+ *   confidence [B * K]  score of draft j of request i at i * K + j, e.g. the
+ *                       output of vsv_draft_confidence; clamped to [0, 1],
+ *                       NaN counts as 0; may be NULL when K == 0
+ *   draft_tokens [B*K]  the drafts in the same layout, or NULL
+ *   row_budget G        host value, B <= G <= B * (K + 1): packed target rows
+ *                       including every request's bonus row
+ * The predicted acceptance of draft j is the float32 running product of its
+ * request's clamped scores through j (left to right). The G - B rows beyond
+ * the bonus rows go to the positions with the largest products, ties broken
+ * by request, then position, ascending; this maximises the expected number
+ * of accepted drafts, and each request receives a prefix of its drafts.
+ *
+ * Outputs (device, caller-allocated):
+ *   verify_len [B]      k_i, the number of drafts request i verifies
+ *   row_offsets [B+1]   exclusive scan of (k_i + 1); row_offsets[B] = G
+ *   row_owner [G]       request of every packed row
+ *   row_source [G]      or NULL: full-width row i * (K + 1) + j that packed
+ *                       row off[i] + j stands for (j = k_i is the bonus row)
+ *   packed_drafts [G-B] or NULL (exactly when draft_tokens is NULL): draft j
+ *                       of request i at off[i] - i + j, the layout that
+ *                       vsv_verify_greedy / vsv_verify_sampled read
+ *   prefix [B * K]      or NULL: the running products
+ * The outputs feed vsv_batch directly (num_rows = G).
+ * Errors: VSV_EINVAL (B < 0, K < 0, G outside [B, B * (K + 1)],
+ * B > 8192 or B * K > 16384, NULL confidence with K > 0, NULL verify_len /
+ * row_offsets / row_owner, exactly one of draft_tokens and packed_drafts
+ * NULL), VSV_EHIP. B = 0 (with G = 0) is a no-op. */
+vsv_status vsv_allocate_verify(const float* confidence, const int32_t* draft_tokens,
+                               int32_t num_requests, int32_t num_drafts, int32_t row_budget,
+                               int32_t* verify_len, int32_t* row_offsets, int32_t* row_owner,
+                               int32_t* row_source, int32_t* packed_drafts, float* prefix,
+                               hipStream_t stream);
+
 /* Static description of a status code. */
 const char* vsv_status_string(vsv_status status);
 

@@ -265,3 +265,38 @@ def redraw_rows(wl, rows):
         wl.attempts[int(r)] = wl.attempts.get(int(r), 0) + 1
         _fill_row(wl, int(r))
     return wl
+
+
+def scores(B, K, seed, kind="confidence", V=VOCAB):
+    """Per-draft scores and draft tokens for adaptive verify allocation.
+
+    Returns (scores float32 [B * K], drafts int32 [B * K]), request-major.
+    Kinds:
+      confidence  half the positions U(0.05, 0.95) (a draft near the top of
+                  its distribution), half 10^U(-9, -1) (a draft far down it)
+      uniform     U(0, 1)
+      ties        drawn from {0, 0.25, 0.5, 1}, so products tie often
+      special     U(-0.5, 1.5) with a few NaN and +-inf (outside [0, 1])
+      tiny        U(0, 1e-12), so long products reach subnormals and 0
+    """
+    g = np.random.default_rng([seed, 7, B, K])
+    n = B * K
+    if kind == "confidence":
+        near = g.uniform(0.05, 0.95, n)
+        far = 10.0 ** g.uniform(-9.0, -1.0, n)
+        s = np.where(g.uniform(size=n) < 0.5, near, far)
+    elif kind == "uniform":
+        s = g.uniform(0.0, 1.0, n)
+    elif kind == "ties":
+        s = g.choice(np.array([0.0, 0.25, 0.5, 1.0]), n)
+    elif kind == "special":
+        s = g.uniform(-0.5, 1.5, n)
+        if n:
+            for v in (np.nan, np.inf, -np.inf):
+                s[g.integers(0, n, max(1, n // 50))] = v
+    elif kind == "tiny":
+        s = g.uniform(0.0, 1e-12, n)
+    else:
+        raise ValueError(kind)
+    drafts = g.integers(0, V, n).astype(np.int32)
+    return s.astype(np.float32), drafts

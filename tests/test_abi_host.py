@@ -128,3 +128,22 @@ def test_confidence_validation(L):
 def test_workspace_init_validation(L):
     assert L.vsv_workspace_init(None, 256, None) == 1
     assert L.vsv_workspace_init(ctypes.c_void_p(0x1000), 6, None) == 1
+
+
+def test_allocate_validation(L):
+    f = L.vsv_allocate_verify
+    p = ctypes.c_void_p(0x1000)
+
+    def call(B, K, G, conf=p, drafts=None, vl=p, off=p, own=p, packed=None):
+        return f(conf, drafts, B, K, G, vl, off, own, None, packed, None, None)
+
+    assert call(0, 4, 0) == 0                      # empty batch: no-op
+    assert call(0, 4, 1) == 1                      # G outside [B, B * (K + 1)]
+    assert call(3, 4, 2) == 1 and call(3, 4, 16) == 1
+    assert call(-1, 4, 0) == 1 and call(3, -1, 3) == 1
+    assert call(8193, 1, 8193) == 1                # more requests than one workgroup holds
+    assert call(2049, 8, 2049) == 1                # more positions than one workgroup holds
+    assert call(3, 4, 5, conf=None) == 1           # scores needed when K > 0
+    assert call(3, 4, 5, vl=None) == 1 and call(3, 4, 5, off=None) == 1 and call(3, 4, 5, own=None) == 1
+    assert call(3, 4, 5, drafts=p) == 1            # drafts without packed output
+    assert call(3, 4, 5, packed=p) == 1            # packed output without drafts
