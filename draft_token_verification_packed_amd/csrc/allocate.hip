@@ -36,6 +36,7 @@ namespace {
 constexpr int kAllocThreads = 1024;
 constexpr int kAllocBins = 2048;
 constexpr int kAllocWaves = kAllocThreads / kWave;
+static_assert(kMaxAllocPositions < (1 << 15), "two counts share one 32-bit scan");
 
 struct AllocScratch {
   uint32_t key[kMaxAllocPositions];    // products as bit patterns
@@ -45,6 +46,7 @@ struct AllocScratch {
   int digit, above;
 };
 
+// Multiply the running product by the clamped score c; returns its pattern.
 __device__ __forceinline__ uint32_t clamp_bits(float c, float& run) {
   const float s = (c >= 0.f) ? fminf(c, 1.f) : 0.f;   // NaN and negatives give 0
   run = run * s;
@@ -76,16 +78,18 @@ __global__ __launch_bounds__(kAllocThreads) void allocate_kernel(AllocArgs a) {
   const int t = threadIdx.x;
   const int B = a.B, K = a.K, N = a.B * a.K, M = a.G - a.B;
 
-  // 1. running products of the clamped scores
+  // 1. running products of the clamped scores. The scores come in with one
+  //    coalesced load per position and the products are formed in LDS, so
+  //    the whole step costs one global round trip.
+  for (int q = t; q < N; q += kAllocThreads) s.key[q] = __float_as_uint(a.conf[q]);
+  lds_barrier();
   for (int i = t; i < B; i += kAllocThreads) {
     float run = 1.f;
-    for (int j = 0; j < K; ++j) {
-      const uint32_t bits = clamp_bits(a.conf[i * K + j], run);
-      s.key[i * K + j] = bits;
-      if (a.prefix) a.prefix[i * K + j] = __uint_as_float(bits);
-    }
+    for (int j = 0; j < K; ++j) s.key[i * K + j] = clamp_bits(__uint_as_float(s.key[i * K + j]), run);
   }
   lds_barrier();
+  if (a.prefix)
+    for (int q = t; q < N; q += kAllocThreads) a.prefix[q] = __uint_as_float(s.key[q]);
 
   // 2. tau = the M-th largest pattern (M >= 1); with M = 0 no position is
   //    taken, which a threshold above every pattern expresses.
@@ -135,10 +139,12 @@ __global__ __launch_bounds__(kAllocThreads) void allocate_kernel(AllocArgs a) {
       gt_sum += k > tau;
       eq_sum += k == tau;
     }
-  int gt_total, eq_total;
-  (void)block_exclusive_scan<kAllocThreads>(gt_sum, s.scan, gt_total);
-  const int ties_before = block_exclusive_scan<kAllocThreads>(eq_sum, s.scan, eq_total);
-  const int need = M - gt_total;   // tied positions to take, in request order
+  // one scan of both counts, packed as gt * 2^16 + eq (each at most
+  // kMaxAllocPositions < 2^16, so neither half carries into the other)
+  int both_total;
+  const int both_before = block_exclusive_scan<kAllocThreads>((gt_sum << 16) | eq_sum, s.scan, both_total);
+  const int ties_before = both_before & 0xFFFF;
+  const int need = M - (both_total >> 16);   // tied positions to take, in request order
   int rows = 0;
   walk_requests(s, K, i0, i1, tau, need, ties_before, [&](int, int k) { rows += k + 1; });
   int rows_total;
