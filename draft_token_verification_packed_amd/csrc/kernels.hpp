@@ -24,14 +24,27 @@ namespace vsv {
 #ifndef VSV_UNROLL
 #define VSV_UNROLL 2
 #endif
-#ifndef VSV_UNROLL_SAMPLED
-#define VSV_UNROLL_SAMPLED 3
-#endif
 constexpr int kVerifyThreads = VSV_VERIFY_THREADS;
 constexpr int kGreedyThreads = VSV_GREEDY_THREADS;
 constexpr int kRowThreads = VSV_ROW_THREADS;
 constexpr int kUnroll = VSV_UNROLL;
-constexpr int kUnrollSampled = VSV_UNROLL_SAMPLED;
+
+// Load depth of a sampled launch, by element type. Pass 1 of a sampled row
+// keeps kPass1 rolling 16-byte vectors per lane (kPass1 - 1 loads in flight);
+// greedy rows stream in groups of kGreedy vectors, two groups in turn. Each
+// workgroup takes rows one after another, so a launch is paced by its rows'
+// latencies. fp32 sampled rows (608 KB each) gain from a deeper pass 1: on
+// the ragged fp32 batch (B=128, 586 rows) eight slots cut the launch from
+// 118 to 112 us. bf16 gained nothing from deeper loads on the large mixed
+// batch (B=512, 4096 rows), whose sampled rows are paced by their selection
+// work, and deeper greedy groups there spill registers.
+template <typename E> struct SampledDepth;
+template <> struct SampledDepth<float> {
+  static constexpr int kPass1 = 8, kGreedy = 2;
+};
+template <> struct SampledDepth<uint16_t> {
+  static constexpr int kPass1 = 3, kGreedy = 2;
+};
 
 // Everything a verify launch needs, passed by value as the kernel argument.
 struct VerifyArgs {

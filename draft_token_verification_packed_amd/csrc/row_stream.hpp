@@ -85,14 +85,25 @@ __device__ __forceinline__ void partial_rebase(RowPartial& p, float vmax, float 
   }
 }
 
-// Pairwise sum of n (a power of two) floats.
+// Largest power of two not above n (n >= 1).
+constexpr int pow2_floor(int n) { return n < 2 ? 1 : 2 * pow2_floor(n / 2); }
+
+// Pairwise sum of n floats: a power of two folds its upper half onto its
+// lower half until one value is left; any other n sums its largest
+// power-of-two prefix and the rest separately.
 template <int n>
 __device__ __forceinline__ float tree_sum(float* e) {
+  static_assert(n >= 1, "at least one term");
+  constexpr int p = pow2_floor(n);
+  if constexpr (p != n) {
+    return tree_sum<p>(e) + tree_sum<n - p>(e + p);
+  } else {
 #pragma unroll
-  for (int w = n / 2; w >= 1; w /= 2)
+    for (int w = n / 2; w >= 1; w /= 2)
 #pragma unroll
-    for (int k = 0; k < w; ++k) e[k] = e[k] + e[k + w];
-  return e[0];
+      for (int k = 0; k < w; ++k) e[k] = e[k] + e[k + w];
+    return e[0];
+  }
 }
 
 template <bool kRank>

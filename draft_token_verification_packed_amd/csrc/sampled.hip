@@ -29,7 +29,7 @@ __device__ __forceinline__ void sampled_kernel_row(const VerifyArgs& a, uint32_t
   int token = 0, bits = 0, slow = 0;
   double lse = 0.0;
   if (m.req >= 0 && T > 0.f) {
-    const SampledOut o = sampled_row<E, NT, kUnrollSampled>(a, row, m.req, m.j, T, L, after_stream);
+    const SampledOut o = sampled_row<E, NT, SampledDepth<E>::kPass1>(a, row, m.req, m.j, T, L, after_stream);
     token = o.token;
     lse = o.lse;
     bits = o.bits;
@@ -108,7 +108,7 @@ static int sampled_resident(int cus) {
   if (cus <= 0 || hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
   if (dev < 64 && cached[dev] > 0) return cached[dev];
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, verify_sampled_kernel<E, kVerifyThreads, kUnroll>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, verify_sampled_kernel<E, kVerifyThreads, SampledDepth<E>::kGreedy>,
                                                    kVerifyThreads, 0) != hipSuccess ||
       per_cu <= 0)
     return 0;
@@ -122,7 +122,7 @@ static hipError_t launch_sampled_t(const VerifyArgs& a, hipStream_t s) {
   int grid = sampled_resident<E>(a.groups);
   if (grid <= 0) grid = 256;
   if (grid > a.R) grid = a.R;
-  verify_sampled_kernel<E, kVerifyThreads, kUnroll><<<dim3(grid), dim3(kVerifyThreads), 0, s>>>(a);
+  verify_sampled_kernel<E, kVerifyThreads, SampledDepth<E>::kGreedy><<<dim3(grid), dim3(kVerifyThreads), 0, s>>>(a);
   return hipGetLastError();
 }
 
