@@ -33,14 +33,15 @@ constexpr int kUnroll = VSV_UNROLL;
 // keeps kPass1 rolling 16-byte vectors per lane (kPass1 - 1 loads in flight);
 // greedy rows stream in groups of kGreedy vectors, two groups in turn. Each
 // workgroup takes rows one after another, so a launch is paced by its rows'
-// latencies. fp32 sampled rows (608 KB each) gain from a deeper pass 1: on
-// the ragged fp32 batch (B=128, 586 rows) eight slots cut the launch from
-// 118 to 112 us. bf16 gained nothing from deeper loads on the large mixed
+// latencies. fp32 rows (608 KB each) gain from deeper loads: on the ragged
+// fp32 batch (B=128, 586 rows) eight pass-1 slots cut the launch from 118 to
+// 112 us, and greedy groups of four shorten the greedy rows that the queue
+// hands out last. bf16 gained nothing from deeper loads on the large mixed
 // batch (B=512, 4096 rows), whose sampled rows are paced by their selection
 // work, and deeper greedy groups there spill registers.
 template <typename E> struct SampledDepth;
 template <> struct SampledDepth<float> {
-  static constexpr int kPass1 = 8, kGreedy = 2;
+  static constexpr int kPass1 = 8, kGreedy = 4;
 };
 template <> struct SampledDepth<uint16_t> {
   static constexpr int kPass1 = 3, kGreedy = 2;
@@ -85,10 +86,14 @@ struct VerifyArgs {
   //  ws_part  [kPartWords][R + kMaxGroups] 64-bit words, field-major; slot
   //           r + p holds the partial statistics persistent workgroup p
   //           gathered for row r
+  //  ws_perm  [R] (sampled launches) the order in which the row queue hands
+  //           out rows, written by the ordering kernel before the launch
   uint32_t* ws_epoch;
   uint32_t* ws_queue;
   uint64_t* ws_row;
   uint64_t* ws_part;
+  int32_t* ws_perm;
+  int32_t ordered;      // sampled: the queue hands out rows in ws_perm order
 };
 
 struct ConfidenceArgs {
@@ -125,9 +130,13 @@ constexpr int kQueueDone = 16;
 constexpr int kQueueWords = 17;
 inline size_t ws_align(size_t b) { return (b + kWsAlign - 1) / kWsAlign * kWsAlign; }
 inline size_t ws_row_bytes(int32_t R) { return ws_align(static_cast<size_t>(R > 0 ? R : 1) * 8); }
-inline size_t ws_bytes(int32_t B, int32_t R, int32_t /*sampled*/) {
+inline size_t ws_part_bytes(int32_t R) {
+  return ws_align((static_cast<size_t>(R > 0 ? R : 0) + kMaxGroups) * kPartWords * 8);
+}
+inline size_t ws_bytes(int32_t B, int32_t R, int32_t sampled) {
   (void)B;
-  return kWsAlign + ws_row_bytes(R) + ws_align((static_cast<size_t>(R > 0 ? R : 0) + kMaxGroups) * kPartWords * 8);
+  const size_t perm = sampled ? ws_align(static_cast<size_t>(R > 0 ? R : 1) * 4) : 0;
+  return kWsAlign + ws_row_bytes(R) + ws_part_bytes(R) + perm;
 }
 // Tokens travel in the low 30 bits of a row word.
 constexpr int32_t kMaxVocab = 0x3FFFFFFF;
