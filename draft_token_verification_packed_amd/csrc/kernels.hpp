@@ -24,10 +24,14 @@ namespace vsv {
 #ifndef VSV_UNROLL
 #define VSV_UNROLL 2
 #endif
+#ifndef VSV_UNROLL_ROWS
+#define VSV_UNROLL_ROWS 2
+#endif
 constexpr int kVerifyThreads = VSV_VERIFY_THREADS;
 constexpr int kGreedyThreads = VSV_GREEDY_THREADS;
 constexpr int kRowThreads = VSV_ROW_THREADS;
 constexpr int kUnroll = VSV_UNROLL;
+constexpr int kUnrollRows = VSV_UNROLL_ROWS;
 
 // Load depth of a sampled launch, by element type. Pass 1 of a sampled row
 // keeps kPass1 rolling 16-byte vectors per lane (kPass1 - 1 loads in flight);
@@ -106,19 +110,20 @@ struct ConfidenceArgs {
   int32_t* error_flag;
 };
 
-// Greedy verification runs one persistent workgroup per CU (at most
-// kMaxGroups). The batch's rows are cut into chunks of 64 * kUnroll 16-byte
-// vectors; each workgroup takes an equal contiguous range of the chunk list
-// and its waves pull chunks from it one at a time, so every CU and every wave
-// finishes at about the same moment however unevenly the memory system serves
-// them. A workgroup's range touches at most kMaxLocalRows rows; batches with
-// more rows per CU than that use one workgroup per row, which is then
-// balanced by itself.
+// Greedy verification of a batch with at most as many rows as CUs runs one
+// persistent workgroup per CU (at most kMaxGroups): the batch's rows are cut
+// into chunks of 64 * kUnroll 16-byte vectors, each workgroup takes an equal
+// contiguous range of the chunk list and its waves pull chunks from it one
+// at a time, so every CU streams the same number of bytes however few the
+// rows. Larger batches use one kRowThreads workgroup per row: every row then
+// streams at the same share of the memory system, and no row's statistics
+// cross workgroups, which was faster from 1.25 rows per CU (B=64 EAGLE-shaped
+// batches) up to 12 per CU (B=600) on MI355X.
 constexpr int kMaxGroups = 1024;
 constexpr int kMaxLocalRows = 32;
 constexpr int kPartWords = 6;   // best, index, exponent ref, sum, rank, row info
 inline bool greedy_persistent(int32_t R, int32_t groups) {
-  return groups > 0 && static_cast<int64_t>(R) <= static_cast<int64_t>(kMaxLocalRows - 1) * groups;
+  return groups > 0 && R <= groups && R <= (kMaxLocalRows - 1) * groups;
 }
 
 // Workspace layout (bytes, 256-aligned pieces). The first piece holds the

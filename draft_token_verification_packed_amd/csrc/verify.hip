@@ -8,7 +8,7 @@
 // acceptance, and runs the per-request scan (verify_common.hpp). No atomics
 // on global memory.
 //
-// Batches with many rows per CU: one workgroup per row decides the row and
+// Batches with more rows than CUs: one workgroup per row decides the row and
 // stores its word (emitted token, accept bit); the workgroup of the last row
 // runs the same per-request scan.
 #include "verify_common.hpp"
@@ -494,7 +494,7 @@ static hipError_t launch_greedy_t(VerifyArgs a, hipStream_t s) {
     a.cpr = nvmax > 0 ? (nvmax + CH - 1) / CH : 1;
     verify_greedy_kernel<E, kGreedyThreads, kUnroll, kRelaxed><<<dim3(a.groups), dim3(kGreedyThreads), 0, s>>>(a);
   } else {
-    verify_greedy_rows_kernel<E, kRowThreads, kUnroll, kRelaxed><<<dim3(a.R), dim3(kRowThreads), 0, s>>>(a);
+    verify_greedy_rows_kernel<E, kRowThreads, kUnrollRows, kRelaxed><<<dim3(a.R), dim3(kRowThreads), 0, s>>>(a);
   }
   return hipGetLastError();
 }
