@@ -44,7 +44,7 @@ __global__ __launch_bounds__(NT) void confidence_kernel(ConfidenceArgs a) {
 
 template <typename E>
 static hipError_t launch_t(const ConfidenceArgs& a, hipStream_t s) {
-  confidence_kernel<E, kVerifyThreads, kUnroll><<<dim3(a.D), dim3(kVerifyThreads), 0, s>>>(a);
+  confidence_kernel<E, kConfThreads, kUnroll><<<dim3(a.D), dim3(kConfThreads), 0, s>>>(a);
   return hipGetLastError();
 }
 

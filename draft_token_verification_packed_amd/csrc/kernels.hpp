@@ -21,6 +21,12 @@ namespace vsv {
 #ifndef VSV_ROW_THREADS
 #define VSV_ROW_THREADS 256
 #endif
+#ifndef VSV_CONF_THREADS
+#define VSV_CONF_THREADS 512
+#endif
+#ifndef VSV_ORDER_THREADS
+#define VSV_ORDER_THREADS 128
+#endif
 #ifndef VSV_UNROLL
 #define VSV_UNROLL 2
 #endif
@@ -30,6 +36,8 @@ namespace vsv {
 constexpr int kVerifyThreads = VSV_VERIFY_THREADS;
 constexpr int kGreedyThreads = VSV_GREEDY_THREADS;
 constexpr int kRowThreads = VSV_ROW_THREADS;
+constexpr int kConfThreads = VSV_CONF_THREADS;     // draft-confidence rows
+constexpr int kOrderThreads = VSV_ORDER_THREADS;   // sampled row order
 constexpr int kUnroll = VSV_UNROLL;
 constexpr int kUnrollRows = VSV_UNROLL_ROWS;
 

@@ -161,8 +161,6 @@ static int sampled_resident(int cus) {
   return n;
 }
 
-constexpr int kOrderThreads = 1024;
-
 template <typename E>
 static hipError_t launch_sampled_t(const VerifyArgs& a, hipStream_t s) {
   int grid = sampled_resident<E>(a.groups);
