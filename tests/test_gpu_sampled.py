@@ -169,3 +169,39 @@ def test_c5_draft_confidence(vsv):
     rc, rl = oracle.draft_confidence(wl.draft_logits, wl.dtype, wl.V, wl.selected)
     assert_lse_close(host(lse), rl)
     np.testing.assert_allclose(host(conf), rc, rtol=1e-5, atol=0)
+
+
+def test_many_requests_in_longest_first_order(vsv):
+    """A batch with at most two rows per workgroup slot goes out longest
+    first (sampled requests' rows, then greedy ones); here with more requests
+    than the ordering workgroup has threads, and a third of them greedy."""
+    rng = np.random.default_rng(4242)
+    params = lambda i: [(0.0, 0, 1.0, 0.0), (0.8, 40, 0.9, 0.0), (1.0, 0, 0.95, 0.05)][i % 3]
+    b = custom_sampled(rng, 300, 2, 4099, oracle.BF16, params, seed=17, offset=3)
+    assert int(b["offsets"][-1]) <= 1024
+    out = run_custom(vsv, b)
+    assert_same(out, oracle_custom(b))
+    assert int(host(out["error_flag"])[0]) == 0
+
+
+def test_layout_errors_are_flagged(vsv):
+    """Inconsistent owner maps and offsets set the layout flag; the launch
+    (with its row-order pass) still completes and writes inside the buffers."""
+    import torch
+    wl = synth.make(3, B=12, V=1000)
+    d = upload(wl)
+    own = d["owner"].clone()
+    own[3] = (own[3] + 1) % wl.B
+    out = vsv.verify_sampled(d["logits"], d["offsets"], own, d["drafts"], d["temperature"], d["top_k"],
+                             d["top_p"], d["min_p"], wl.seed)
+    torch.cuda.synchronize()
+    assert int(host(out["error_flag"])[0]) & vsv.FLAG_LAYOUT
+    off = d["offsets"].clone()
+    off[5] = off[4]                       # request 4 owns no rows: offsets not increasing
+    out = vsv.verify_sampled(d["logits"], off, d["owner"], d["drafts"], d["temperature"], d["top_k"],
+                             d["top_p"], d["min_p"], wl.seed)
+    torch.cuda.synchronize()
+    assert int(host(out["error_flag"])[0]) & vsv.FLAG_LAYOUT
+    # the next well-formed call on the same workspace is unaffected
+    good = run_sampled(vsv, with_margins(wl))
+    assert_same(good, oracle_of(wl))
