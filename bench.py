@@ -183,6 +183,59 @@ def bench_allocate(args, vsv, torch):
     return 0
 
 
+def bench_goodput(args, vsv):
+    """Goodput step selection per completed batch (host code): observe one
+    batch of B=512 requests with up to 7 verified drafts, then pick the next
+    step count, on a drifting synthetic acceptance history; the oracle is
+    timed beside it on the same history."""
+    import numpy as np
+    from oracle.goodput import GoodputController
+    rng = np.random.default_rng(1007)
+    S, B, n = 7, 512, 2000
+    hist = []
+    for t in range(n):
+        k = rng.integers(1, S + 1, B)
+        p = 0.55 + 0.35 * np.sin(t / 50.0)
+        a = np.minimum(rng.geometric(1.0 - p, B) - 1, k)
+        hist.append((a.astype(np.int32), k.astype(np.int32)))
+    cost = 10.0 + 1.5 * np.arange(1, S + 1)
+    import ctypes
+    g = vsv.Goodput(S)
+    L = vsv.lib()
+    st = ctypes.byref(g.state)
+    ptrs = [(a.ctypes.data_as(ctypes.c_void_p), k.ctypes.data_as(ctypes.c_void_p)) for a, k in hist]
+    cost = np.ascontiguousarray(cost, dtype=np.float64)
+    pc = cost.ctypes.data_as(ctypes.c_void_p)
+    out = ctypes.c_int32(0)
+    po = ctypes.byref(out)
+    steps = []
+    t0 = time.perf_counter()
+    for pa, pk in ptrs:
+        if L.vsv_goodput_observe(st, pa, pk, B) != 0 or L.vsv_goodput_step(st, pc, B, po) != 0:
+            raise RuntimeError("goodput call failed")
+        steps.append(out.value)
+    dt = time.perf_counter() - t0
+    line = dict(metric="goodput step selection per batch (host), B=512 S=7", value=dt / n * 1e6, unit="us",
+                n_gpus=0, steps=n, warmup=0, ms_per_step=dt / n * 1e3, higher_is_better=False, scaling="weak",
+                vs_baseline=None, dtype="f64", data="synthetic",
+                config=dict(workload="goodput step selection, B=512 max_steps=7, window 20, re-score every 5",
+                            B=B, max_steps=S, batches=n, switches=int(np.count_nonzero(np.diff(steps)))),
+                note="host code: the two C calls per batch through ctypes with arguments prepared beforehand")
+    if not args.no_cpu_baseline:
+        ref = GoodputController(S)
+        t0 = time.perf_counter()
+        ref_steps = []
+        for a, k in hist:
+            ref.observe(a, k)
+            ref_steps.append(ref.step(cost, B))
+        rdt = time.perf_counter() - t0
+        assert ref_steps == steps, "goodput decisions differ from the oracle"
+        line["cpu_baseline"] = dict(value=rdt / n * 1e6, unit="us", cores=1, kind="oracle",
+                                    sample="the same %d batches, %.1f s, single process" % (n, rdt))
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,6 +246,8 @@ def main():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
                     help="workload (default: EAGLE greedy B=128 K=4 V=152064)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--goodput", action="store_true",
+                    help="time goodput step selection (host code, B=512, 7 steps) instead of verification")
     ap.add_argument("--allocate", action="store_true",
                     help="time adaptive verify allocation (B=512, K=7) instead of verification")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -212,6 +267,9 @@ def main():
     import synth
     import draft_token_verification_packed_amd as vsv
 
+    if args.goodput:
+        vsv.lib()
+        return bench_goodput(args, vsv)
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1

@@ -11,6 +11,9 @@ Entry points mirror the C ABI in include/vspec_verify.h:
                    temperature, top_k, top_p, min_p, seed, offset=0)
     draft_confidence(draft_logits, selected=None)
     allocate_verify(confidence, draft_tokens, num_requests, num_drafts, row_budget)
+    Goodput(max_steps, window_size=20, update_interval=5, switch_min_gain=0.05)
+        .observe(accepted_len, verify_len), .step(cost_ms, batch_size)   (host)
+    goodput_select(prefix_acceptance, cost_ms, batch_size, current, switch_min_gain)
 """
 import ctypes
 import os
@@ -51,7 +54,20 @@ class Outputs(ctypes.Structure):
 
 
 SYMBOLS = ("vsv_workspace_bytes", "vsv_workspace_init", "vsv_verify_greedy", "vsv_verify_sampled",
-           "vsv_draft_confidence", "vsv_allocate_verify", "vsv_status_string", "vsv_version")
+           "vsv_draft_confidence", "vsv_allocate_verify", "vsv_goodput_init", "vsv_goodput_observe",
+           "vsv_goodput_step", "vsv_goodput_select", "vsv_status_string", "vsv_version")
+
+GOODPUT_MAX_STEPS = 32
+GOODPUT_MAX_WINDOW = 64
+
+
+class GoodputState(ctypes.Structure):
+    _fields_ = [("max_steps", ctypes.c_int32), ("window_size", ctypes.c_int32), ("update_interval", ctypes.c_int32),
+                ("switch_min_gain", ctypes.c_double), ("current", ctypes.c_int32), ("since", ctypes.c_int32),
+                ("filled", ctypes.c_int32), ("head", ctypes.c_int32),
+                ("reached", (ctypes.c_int32 * GOODPUT_MAX_STEPS) * GOODPUT_MAX_WINDOW),
+                ("accepted", (ctypes.c_int32 * GOODPUT_MAX_STEPS) * GOODPUT_MAX_WINDOW),
+                ("estimate", ctypes.c_double * GOODPUT_MAX_STEPS)]
 
 _lib = None
 
@@ -79,6 +95,15 @@ def lib():
     L.vsv_draft_confidence.restype = ctypes.c_int
     L.vsv_allocate_verify.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     L.vsv_allocate_verify.restype = ctypes.c_int
+    gp = ctypes.POINTER(GoodputState)
+    L.vsv_goodput_init.argtypes = [gp, i32, i32, i32, ctypes.c_double]
+    L.vsv_goodput_init.restype = ctypes.c_int
+    L.vsv_goodput_observe.argtypes = [gp, vp, vp, i32]
+    L.vsv_goodput_observe.restype = ctypes.c_int
+    L.vsv_goodput_step.argtypes = [gp, vp, i32, ctypes.POINTER(i32)]
+    L.vsv_goodput_step.restype = ctypes.c_int
+    L.vsv_goodput_select.argtypes = [vp, vp, i32, i32, i32, ctypes.c_double]
+    L.vsv_goodput_select.restype = i32
     L.vsv_status_string.argtypes = [ctypes.c_int]
     L.vsv_status_string.restype = ctypes.c_char_p
     L.vsv_version.argtypes = []
@@ -243,6 +268,55 @@ def allocate_verify(confidence, draft_tokens, num_requests, num_drafts, row_budg
     out = _alloc_outputs(B, K, G, dev, draft_tokens is not None)
     _check(lib().vsv_allocate_verify(*_alloc_args(confidence, draft_tokens, B, K, G, out, stream)))
     return out
+
+
+def _host_array(x, ctype, np_dtype):
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(x, dtype=np_dtype))
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Goodput:
+    """Goodput step selection over completed batches (host code; see
+    vsv_goodput_* in the header). `observe` takes a batch's accepted and
+    verified draft counts, `step` the full-round cost of every candidate
+    step count 1 .. max_steps and returns the step count for the next batch."""
+
+    def __init__(self, max_steps, window_size=20, update_interval=5, switch_min_gain=0.05):
+        self.state = GoodputState()
+        _check(lib().vsv_goodput_init(ctypes.byref(self.state), int(max_steps), int(window_size),
+                                      int(update_interval), float(switch_min_gain)))
+
+    def observe(self, accepted_len, verify_len):
+        import numpy as np
+        a, pa = _host_array(accepted_len, ctypes.c_int32, np.int32)
+        k, pk = _host_array(verify_len, ctypes.c_int32, np.int32)
+        if a.shape != k.shape or a.ndim != 1:
+            raise ValueError("accepted_len and verify_len must be matching vectors")
+        _check(lib().vsv_goodput_observe(ctypes.byref(self.state), pa, pk, int(a.size)))
+
+    def step(self, cost_ms, batch_size):
+        import numpy as np
+        c, pc = _host_array(cost_ms, ctypes.c_double, np.float64)
+        if c.size != self.state.max_steps:
+            raise ValueError("cost_ms needs one cost per step count 1 .. max_steps")
+        out = ctypes.c_int32(0)
+        _check(lib().vsv_goodput_step(ctypes.byref(self.state), pc, int(batch_size), ctypes.byref(out)))
+        return int(out.value)
+
+    @property
+    def estimate(self):
+        return [self.state.estimate[j] for j in range(self.state.max_steps)]
+
+
+def goodput_select(prefix_acceptance, cost_ms, batch_size, current, switch_min_gain=0.05):
+    """One stateless scoring (vsv_goodput_select); -1 for invalid arguments."""
+    import numpy as np
+    p, pp = _host_array(prefix_acceptance, ctypes.c_double, np.float64)
+    c, pc = _host_array(cost_ms, ctypes.c_double, np.float64)
+    if p.size != c.size:
+        raise ValueError("one prefix acceptance and one cost per step count")
+    return int(lib().vsv_goodput_select(pp, pc, int(c.size), int(batch_size), int(current), float(switch_min_gain)))
 
 
 class PreparedCall:

@@ -198,6 +198,69 @@ vsv_status vsv_allocate_verify(const float* confidence, const int32_t* draft_tok
                                int32_t* row_source, int32_t* packed_drafts, float* prefix,
                                hipStream_t stream);
 
+/* Goodput step selection: the step count of the next decode batch from
+ * completed verification results (xLLM docs, "Adaptive speculative
+ * inference", section "Adaptive draft step (MTP)" and its policy options:
+ * one step count s for the whole batch, the one maximising
+ * B * (1 + sum(prefix_acceptance[:s])) / cost_ms(s); prefix acceptance
+ * counted over a window of completed batches (default 20); candidates
+ * re-scored every update_interval batches (default 5); the step changes only
+ * when the predicted relative gain is strictly above switch_min_gain
+ * (default 0.05)).
+ * HOST code and HOST pointers: the caller reads accepted lengths back with
+ * its normal results and passes the full-round cost of every candidate.
+ * Rules the page leaves open: candidates are 1 .. max_steps and the
+ * controller starts at max_steps; prefix acceptance j is the share, among
+ * the window's requests that verified at least j + 1 drafts, of those that
+ * accepted at least j + 1 (a position no request in the window verified
+ * keeps its last estimate, 0 before any); equal scores go to the smaller
+ * step count. The caller owns the state; one state per controller, not
+ * thread-safe. */
+#define VSV_GOODPUT_MAX_STEPS 32
+#define VSV_GOODPUT_MAX_WINDOW 64
+typedef struct {
+  int32_t max_steps;        /* S: largest step count                           */
+  int32_t window_size;      /* completed batches counted                       */
+  int32_t update_interval;  /* batches between re-scorings                     */
+  double switch_min_gain;   /* strict relative gain needed to switch           */
+  int32_t current;          /* step count in force                             */
+  int32_t since;            /* batches observed since the last re-scoring      */
+  int32_t filled;           /* batches in the window                           */
+  int32_t head;             /* window slot of the next batch                   */
+  int32_t reached[VSV_GOODPUT_MAX_WINDOW][VSV_GOODPUT_MAX_STEPS];   /* per batch: */
+  int32_t accepted[VSV_GOODPUT_MAX_WINDOW][VSV_GOODPUT_MAX_STEPS];  /* requests that verified / accepted > j drafts */
+  double estimate[VSV_GOODPUT_MAX_STEPS];  /* prefix acceptance per position */
+} vsv_goodput;
+
+/* Reset `state`. Errors: VSV_EINVAL (NULL state, max_steps outside
+ * [1, VSV_GOODPUT_MAX_STEPS], window_size outside [1, VSV_GOODPUT_MAX_WINDOW],
+ * update_interval < 1, non-finite switch_min_gain). */
+vsv_status vsv_goodput_init(vsv_goodput* state, int32_t max_steps, int32_t window_size,
+                            int32_t update_interval, double switch_min_gain);
+
+/* Record one completed batch: accepted_len[i] and verify_len[i] (drafts the
+ * target verified) of its num_requests requests, host arrays. Positions at or
+ * beyond max_steps are not counted. Errors: VSV_EINVAL (NULL state or arrays,
+ * num_requests < 0, an entry with accepted_len < 0 or > verify_len); the batch
+ * is then not recorded. */
+vsv_status vsv_goodput_observe(vsv_goodput* state, const int32_t* accepted_len,
+                               const int32_t* verify_len, int32_t num_requests);
+
+/* The step count for the next batch of batch_size requests. cost_ms[s - 1] is
+ * the full-round cost of s steps (host array of max_steps positive values);
+ * re-scores when update_interval batches were observed since the last
+ * re-scoring. Errors: VSV_EINVAL (NULL state, cost_ms or step, a cost that is
+ * not positive and finite, batch_size < 0). */
+vsv_status vsv_goodput_step(vsv_goodput* state, const double* cost_ms, int32_t batch_size,
+                            int32_t* step);
+
+/* One scoring without state: the step count among 1 .. max_steps that the
+ * rule above picks from `current`, given prefix_acceptance[max_steps] and
+ * cost_ms[max_steps] (host arrays). Returns -1 for invalid arguments. */
+int32_t vsv_goodput_select(const double* prefix_acceptance, const double* cost_ms,
+                           int32_t max_steps, int32_t batch_size, int32_t current,
+                           double switch_min_gain);
+
 /* Static description of a status code. */
 const char* vsv_status_string(vsv_status status);
 
