@@ -3,8 +3,8 @@
 Each mutant plants one plausible mistake in a copy of `oracle/` (a dropped
 term, a wrong tie rule or boundary, an off-by-one index, a swapped filter
 order, a wrong Philox constant). The pin suite of the mutated module
-(`test_oracle_pins.py`, or `test_oracle_allocate.py` for the verify
-allocation) then runs against the mutant in a subprocess and must fail: a
+(`test_oracle_pins.py`, `test_oracle_allocate.py` for the verify
+allocation, `test_oracle_goodput.py` for goodput step selection) then runs against the mutant in a subprocess and must fail: a
 mistake that no pin catches would also slip past parity, since parity
 compares the HIP path with this oracle.
 """
@@ -19,7 +19,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")
-PINS_BY_FILE = {"allocate.py": os.path.join(ROOT, "tests", "test_oracle_allocate.py")}
+PINS_BY_FILE = {"allocate.py": os.path.join(ROOT, "tests", "test_oracle_allocate.py"),
+                "goodput.py": os.path.join(ROOT, "tests", "test_oracle_goodput.py")}
 
 # (name, file, original text, mutated text); the original must occur once.
 MUTANTS = [
@@ -103,6 +104,27 @@ MUTANTS = [
     ("allocation_source_stride", "allocate.py",
      "source[off[i] + j] = i * (K + 1) + j",
      "source[off[i] + j] = i * K + j"),
+    ("goodput_margin_inclusive", "goodput.py",
+     "best_score > (1.0 + min_gain) * score(",
+     "best_score >= (1.0 + min_gain) * score("),
+    ("goodput_ties_to_larger_step", "goodput.py",
+     "        if v > best_score:\n",
+     "        if v >= best_score:\n"),
+    ("goodput_score_without_one", "goodput.py",
+     "    total = 1.0\n",
+     "    total = 0.0\n"),
+    ("goodput_unreached_positions_reset", "goodput.py",
+     "            if reached[j] > 0:\n                self.estimate[j] = float(accepted[j]) / float(reached[j])",
+     "            self.estimate[j] = float(accepted[j]) / float(max(reached[j], 1))"),
+    ("goodput_window_one_longer", "goodput.py",
+     "self.batches = self.batches[-self.window:]",
+     "self.batches = self.batches[-self.window - 1:]"),
+    ("goodput_rescore_early", "goodput.py",
+     "if self.since >= self.interval:",
+     "if self.since >= self.interval - 1:"),
+    ("goodput_counts_inclusive", "goodput.py",
+     "accepted = np.array([int((a > j).sum())",
+     "accepted = np.array([int((a >= j).sum())"),
 ]
 
 
