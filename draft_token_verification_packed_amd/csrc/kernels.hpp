@@ -70,6 +70,7 @@ struct VerifyArgs {
   int32_t relaxed_k;
   int32_t groups;       // greedy: persistent workgroups (one per CU)
   int32_t cpr;          // greedy: chunks per row (set at launch)
+  int32_t parts;        // greedy, one workgroup per row part: 1 or 2 parts per row
   // sampled only
   const float* temperature;
   const int32_t* top_k;

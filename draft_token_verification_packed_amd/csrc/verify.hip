@@ -444,15 +444,38 @@ __global__ __launch_bounds__(NT) void verify_greedy_kernel(VerifyArgs a) {
   if (p == plan.P - 1) greedy_tail<NT, kRelaxed>(a, plan, tag, tail, s_lo);
 }
 
-// One workgroup per row (batches with many rows per CU): the row's word is
-// decided here and handed to the scan like a sampled row's.
+// Words of a first half's statistics (row-major, kHalfWords per row in the
+// workspace's partials area): max, its lowest index, exponent reference,
+// the float64 sum as two halves, rank count.
+constexpr int kHalfWords = 6;
+
+// One workgroup per row, or per half row (a.parts = 2), for batches with
+// more rows than CUs. Halves are used where they give the CUs a more even
+// number of parts. The first half stores its statistics as tagged words;
+// the second half, dispatched after it, waits for them (so the wait always
+// ends), merges, and decides the row. The row's word goes to the scan like a
+// sampled row's.
 template <typename E, int NT, int U, bool kRelaxed>
 __global__ __launch_bounds__(NT) void verify_greedy_rows_kernel(VerifyArgs a) {
   __shared__ RowScratch<NT> scr;
   __shared__ TailScratch tail;
-  const int r = blockIdx.x;
+  constexpr int N = Elem<E>::kVec;
+  const bool halves = a.parts == 2;
+  const int r = halves ? static_cast<int>(blockIdx.x >> 1) : static_cast<int>(blockIdx.x);
+  const int part = halves ? static_cast<int>(blockIdx.x & 1) : 0;
   const uint32_t tag = call_tag(a);
   const E* __restrict__ row = static_cast<const E*>(a.logits) + static_cast<int64_t>(r) * a.ld;
+  // the part's elements [e0, e1): the halves split the row's 16-byte body;
+  // the first also holds the elements before it, the second those after it
+  int e0 = 0, e1 = a.V;
+  if (halves) {
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
+    int head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(E));
+    if (head > a.V) head = a.V;
+    const int mid = head + ((a.V - head) / N / 2) * N;
+    e0 = part == 0 ? 0 : mid;
+    e1 = part == 0 ? mid : a.V;
+  }
   const int owner = a.owner[r];
   RowMeta m{-1, 0, 0, -1};
   float xd = INFINITY;
@@ -464,25 +487,67 @@ __global__ __launch_bounds__(NT) void verify_greedy_rows_kernel(VerifyArgs a) {
   partial_init(p);
   GroupKeep<U> keep{};
   constexpr float kLog2e = 1.4426950408889634f;
-  stream_row<E, NT, U, kRelaxed>(row, a.V, kLog2e, xd, kRelaxed ? m.draft : 0, p, keep, [&]() {
+  // element indices inside the part are relative to e0, so the draft's is too
+  stream_row<E, NT, U, kRelaxed>(row + e0, e1 - e0, kLog2e, xd, kRelaxed ? m.draft - e0 : 0, p, keep, [&]() {
     if (!kRelaxed) m = load_meta(a, r, owner);
   });
-  const RowResult res = finish_row<E, NT, U, kRelaxed, true>(p, scr, keep, row, a.V);
+  const RowResult res = finish_row<E, NT, U, kRelaxed, true>(p, scr, keep, row + e0, e1 - e0);
   if (threadIdx.x == 0) {
-    int token = res.argmax;
-    int bits = 0;
-    if (!(res.max < INFINITY) || token == INT32_MAX || !isfinite(res.lse)) {
-      bits |= VSV_FLAG_LOGITS;
-      if (token == INT32_MAX) token = 0;
+    const int idx = res.argmax == INT32_MAX ? INT32_MAX : e0 + res.argmax;
+    uint64_t* hw = a.ws_part + static_cast<size_t>(r) * kHalfWords;
+    if (halves && part == 0) {
+      const uint64_t sb = __builtin_bit_cast(uint64_t, res.sum);
+      store_agent64(hw + 0, tagged(tag, __float_as_uint(res.max)));
+      store_agent64(hw + 1, tagged(tag, static_cast<uint32_t>(idx)));
+      store_agent64(hw + 2, tagged(tag, __float_as_uint(res.mref)));
+      store_agent64(hw + 3, tagged(tag, static_cast<uint32_t>(sb)));
+      store_agent64(hw + 4, tagged(tag, static_cast<uint32_t>(sb >> 32)));
+      store_agent64(hw + 5, tagged(tag, static_cast<uint32_t>(res.rank)));
+    } else {
+      RowRed red{res.sum, res.max, idx, res.mref, res.rank};
+      int stalled = 0;
+      if (halves) {
+        uint64_t w[kHalfWords];
+        auto load_all = [&]() {
+#pragma unroll
+          for (int f = 0; f < kHalfWords; ++f) w[f] = load_agent64(hw + f);
+        };
+        auto complete = [&]() {
+          bool ok = true;
+#pragma unroll
+          for (int f = 0; f < kHalfWords; ++f) ok = ok && static_cast<uint32_t>(w[f] >> 32) == tag;
+          return ok;
+        };
+        int budget = kPollBudget;
+        load_all();
+        while (!complete() && budget > 0) {
+          --budget;
+          __builtin_amdgcn_s_sleep(2);
+          load_all();
+        }
+        stalled = complete() ? 0 : 1;
+        const uint64_t sb = (static_cast<uint64_t>(static_cast<uint32_t>(w[4])) << 32) | static_cast<uint32_t>(w[3]);
+        const RowRed first{__builtin_bit_cast(double, sb), __uint_as_float(static_cast<uint32_t>(w[0])),
+                           static_cast<int>(static_cast<uint32_t>(w[1])), __uint_as_float(static_cast<uint32_t>(w[2])),
+                           static_cast<int>(static_cast<uint32_t>(w[5]))};
+        red = combine(first, red);
+      }
+      const double lse = 0.69314718055994530942 * (static_cast<double>(red.mc) + log2(red.s));
+      int token = red.idx;
+      int bits = stalled ? VSV_FLAG_STALLED : 0;
+      if (!(red.best < INFINITY) || token == INT32_MAX || !isfinite(lse)) {
+        bits |= VSV_FLAG_LOGITS;
+        if (token == INT32_MAX) token = 0;
+      }
+      const bool ok = kRelaxed ? (red.rank < a.relaxed_k) : (m.draft == token);
+      const uint32_t word = row_word(a, m, token, ok, bits);
+      if (bits) set_flag(a, bits);
+      if (a.row_token) a.row_token[r] = token;
+      if (a.row_lse) a.row_lse[r] = static_cast<float>(lse);
+      store_agent64(a.ws_row + r, tagged(tag, word));
     }
-    const bool ok = kRelaxed ? (res.rank < a.relaxed_k) : (m.draft == token);
-    const uint32_t word = row_word(a, m, token, ok, bits);
-    if (bits) set_flag(a, bits);
-    if (a.row_token) a.row_token[r] = token;
-    if (a.row_lse) a.row_lse[r] = static_cast<float>(res.lse);
-    store_agent64(a.ws_row + r, tagged(tag, word));
   }
-  if (r == a.R - 1) words_tail<NT>(a, tag, tail);
+  if (blockIdx.x == gridDim.x - 1) words_tail<NT>(a, tag, tail);
 }
 
 template <typename E, bool kRelaxed>
@@ -494,7 +559,17 @@ static hipError_t launch_greedy_t(VerifyArgs a, hipStream_t s) {
     a.cpr = nvmax > 0 ? (nvmax + CH - 1) / CH : 1;
     verify_greedy_kernel<E, kGreedyThreads, kUnroll, kRelaxed><<<dim3(a.groups), dim3(kGreedyThreads), 0, s>>>(a);
   } else {
-    verify_greedy_rows_kernel<E, kRowThreads, kUnrollRows, kRelaxed><<<dim3(a.R), dim3(kRowThreads), 0, s>>>(a);
+    // halves where they even out the parts per CU, i.e. where
+    // ceil(R S / CUs) / (R S / CUs) is closer to 1 with S = 2 than with S = 1
+    // (320 EAGLE-shaped rows on 256 CUs: 25.4 -> 22.5 us)
+    a.parts = 1;
+    if (a.groups > 0 && a.R <= (1 << 29)) {
+      const int64_t c = a.groups, r1 = a.R, r2 = 2 * static_cast<int64_t>(a.R);
+      const int64_t w1 = (r1 + c - 1) / c, w2 = (r2 + c - 1) / c;
+      if (w2 * r1 < w1 * r2) a.parts = 2;   // w2 / r2 < w1 / r1, exactly
+    }
+    verify_greedy_rows_kernel<E, kRowThreads, kUnrollRows, kRelaxed>
+        <<<dim3(a.R * a.parts), dim3(kRowThreads), 0, s>>>(a);
   }
   return hipGetLastError();
 }
