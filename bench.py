@@ -97,10 +97,11 @@ def build_steps(vsv, torch, wl):
             ccall, _ = vsv.prepare_confidence(dl, sel)
             calls.append(ccall)
         steps.append(calls)
-    # greedy batches with more rows than CUs run one workgroup per row, the
-    # others one persistent workgroup per CU (the library's launch rule)
+    # greedy batches with between half as many rows as CUs and as many run
+    # one persistent workgroup per CU, the others one workgroup per row or
+    # half row (the library's launch rule)
     cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
-    greedy = "verify_greedy_rows_kernel" if wl.R > cus else "verify_greedy_kernel"
+    greedy = "verify_greedy_kernel" if 2 * wl.R >= cus and wl.R <= cus else "verify_greedy_rows_kernel"
     kernels = [("verify_sampled_kernel" if wl.sampled else greedy, verify_bytes)]
     if wl.D:
         kernels.append(("confidence_kernel", conf_bytes))

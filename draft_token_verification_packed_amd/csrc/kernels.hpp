@@ -119,20 +119,23 @@ struct ConfidenceArgs {
   int32_t* error_flag;
 };
 
-// Greedy verification of a batch with at most as many rows as CUs runs one
-// persistent workgroup per CU (at most kMaxGroups): the batch's rows are cut
-// into chunks of 64 * kUnroll 16-byte vectors, each workgroup takes an equal
-// contiguous range of the chunk list and its waves pull chunks from it one
-// at a time, so every CU streams the same number of bytes however few the
-// rows. Larger batches use one kRowThreads workgroup per row: every row then
-// streams at the same share of the memory system, and no row's statistics
-// cross workgroups, which was faster from 1.25 rows per CU (B=64 EAGLE-shaped
-// batches) up to 12 per CU (B=600) on MI355X.
+// Greedy verification of a batch with between half as many rows as CUs and
+// as many runs one persistent workgroup per CU (at most kMaxGroups): the
+// batch's rows are cut into chunks of 64 * kUnroll 16-byte vectors, each
+// workgroup takes an equal contiguous range of the chunk list and its waves
+// pull chunks from it one at a time, so every CU streams the same number of
+// bytes however few the rows. Other batches use one kRowThreads workgroup
+// per row (or per half row): each row then streams at the same share of the
+// memory system and no row's statistics cross more than two workgroups.
+// Timed on EAGLE-shaped bf16 batches on MI355X (256 CUs), the persistent
+// kernel won only from about 128 to 256 rows; below, its fixed cost of 256
+// large workgroups and the merge across them dominates (20 rows: 20.7 us
+// against 14.1), and above, the row kernel wins up to 3000 rows.
 constexpr int kMaxGroups = 1024;
 constexpr int kMaxLocalRows = 32;
 constexpr int kPartWords = 6;   // best, index, exponent ref, sum, rank, row info
 inline bool greedy_persistent(int32_t R, int32_t groups) {
-  return groups > 0 && R <= groups && R <= (kMaxLocalRows - 1) * groups;
+  return groups > 0 && 2 * static_cast<int64_t>(R) >= groups && R <= groups;
 }
 
 // Workspace layout (bytes, 256-aligned pieces). The first piece holds the

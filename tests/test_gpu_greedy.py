@@ -36,13 +36,15 @@ def test_c1_tiny_closed_form(vsv):
     assert_same(out, oracle_of(wl))
 
 
-@pytest.mark.parametrize("B", [16, 128])
+# 16 and 128 requests (80, 640 rows) run one workgroup per row or half row,
+# 32 (160 rows) the persistent kernel
+@pytest.mark.parametrize("B", [16, 32, 128])
 def test_c2_eagle_greedy(vsv, B):
     wl = synth.make(2, B=B)
     assert_same(run_greedy(vsv, wl), oracle_of(wl))
 
 
-@pytest.mark.parametrize("B", [8, 128])
+@pytest.mark.parametrize("B", [8, 40, 128])
 def test_c4_relaxed_top4(vsv, B):
     wl = synth.make(4, B=B)
     ref = oracle_of(wl)
