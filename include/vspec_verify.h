@@ -91,11 +91,11 @@ typedef struct {
 /* Bytes of device workspace a verify call needs (B requests, R rows): the
  * words through which rows and workgroups hand their results to the
  * batch-wide scan, a call counter, and the row queue of sampled
- * verification with the order in which it hands out rows. The workspace must be zero-filled
- * before its first use (vsv_workspace_init or any zeroed allocation); after
- * that every call leaves it ready for the next one, so one workspace serves
- * any later call on the same stream. Two calls that may overlap in time
- * need two workspaces. */
+ * verification with the order in which it hands out rows. The workspace
+ * must be zero-filled before its first use (vsv_workspace_init or any
+ * zeroed allocation); after that every call leaves it ready for the next
+ * one, so one workspace serves any later call on the same stream. Two calls
+ * that may overlap in time need two workspaces. */
 size_t vsv_workspace_bytes(int32_t num_requests, int32_t num_rows, int32_t sampled);
 
 /* Zero-fill `bytes` of workspace on `stream` with a kernel (no memset node,
