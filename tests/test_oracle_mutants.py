@@ -4,7 +4,8 @@ Each mutant plants one plausible mistake in a copy of `oracle/` (a dropped
 term, a wrong tie rule or boundary, an off-by-one index, a swapped filter
 order, a wrong Philox constant). The pin suite of the mutated module
 (`test_oracle_pins.py`, `test_oracle_allocate.py` for the verify
-allocation, `test_oracle_goodput.py` for goodput step selection) then runs against the mutant in a subprocess and must fail: a
+allocation, `test_oracle_goodput.py` for goodput step selection,
+`test_oracle_probabilistic.py` for probabilistic drafts) then runs against the mutant in a subprocess and must fail: a
 mistake that no pin catches would also slip past parity, since parity
 compares the HIP path with this oracle.
 """
@@ -20,7 +21,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")
 PINS_BY_FILE = {"allocate.py": os.path.join(ROOT, "tests", "test_oracle_allocate.py"),
-                "goodput.py": os.path.join(ROOT, "tests", "test_oracle_goodput.py")}
+                "goodput.py": os.path.join(ROOT, "tests", "test_oracle_goodput.py"),
+                "probabilistic.py": os.path.join(ROOT, "tests", "test_oracle_probabilistic.py")}
 
 # (name, file, original text, mutated text); the original must occur once.
 MUTANTS = [
@@ -122,6 +124,24 @@ MUTANTS = [
     ("goodput_rescore_early", "goodput.py",
      "if self.since >= self.interval:",
      "if self.since >= self.interval - 1:"),
+    ("prob_ratio_inverted", "probabilistic.py",
+     "return bool(u_acc * q[d] < p[d])",
+     "return bool(u_acc * p[d] < q[d])"),
+    ("prob_accept_inclusive", "probabilistic.py",
+     "return bool(u_acc * q[d] < p[d])",
+     "return bool(u_acc * q[d] <= p[d])"),
+    ("prob_residual_q_minus_p", "probabilistic.py",
+     "r = np.maximum(p - q, 0.0)",
+     "r = np.maximum(q - p, 0.0)"),
+    ("prob_residual_not_clipped", "probabilistic.py",
+     "r = np.maximum(p - q, 0.0)",
+     "r = np.abs(p - q)"),
+    ("prob_draft_without_temperature", "probabilistic.py",
+     "z = (y - np.max(y)) / draft_temperature",
+     "z = (y - np.max(y))"),
+    ("prob_acceptance_word", "probabilistic.py",
+     "(w[1] >> 8) * (1.0 / 16777216.0)",
+     "(w[2] >> 8) * (1.0 / 16777216.0)"),
     ("goodput_counts_inclusive", "goodput.py",
      "accepted = np.array([int((a > j).sum())",
      "accepted = np.array([int((a >= j).sum())"),
