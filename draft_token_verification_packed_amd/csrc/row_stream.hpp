@@ -106,9 +106,13 @@ __device__ __forceinline__ float tree_sum(float* e) {
   }
 }
 
-template <bool kRank>
+// One element outside the row's 16-byte body. A head element (before the
+// body, kHead) has a lower index than every body element, so it also takes
+// the thread's best when it only ties it: it may be reduced after the body
+// and still keep the lowest index of the maximum.
+template <bool kRank, bool kHead = false>
 __device__ __forceinline__ void take_scalar(RowPartial& p, float x, int e, float c, float xd, int d) {
-  if (x > p.best) {
+  if (kHead ? (x >= p.best) : (x > p.best)) {
     p.best = x;
     p.bpos = e;
     p.bvec = 0;
@@ -276,7 +280,7 @@ __device__ __forceinline__ void stream_row(const E* __restrict__ row, int V, flo
     hook();
   }
 
-  if (tid < head) take_scalar<kRank>(p, Elem<E>::at(row, tid), tid, c, xd, d);
+  if (tid < head) take_scalar<kRank, true>(p, Elem<E>::at(row, tid), tid, c, xd, d);
   const int tail = V - body_end;
   if (tid < tail) take_scalar<kRank>(p, Elem<E>::at(row, body_end + tid), body_end + tid, c, xd, d);
 }

@@ -399,7 +399,7 @@ __global__ __launch_bounds__(NT) void verify_greedy_kernel(VerifyArgs a) {
     if (!live) return;
     // elements outside the row's 16-byte body (misaligned rows or a vocab
     // that is not a multiple of the vector), loaded with the chunk
-    if (sl.k == 0 && lane < sl.g.head) take_scalar<kRelaxed>(pt, edge_value<E>(edge), lane, kLog2e, xd, d);
+    if (sl.k == 0 && lane < sl.g.head) take_scalar<kRelaxed, true>(pt, edge_value<E>(edge), lane, kLog2e, xd, d);
     if (sl.k == a.cpr - 1) {
       const int e = sl.g.head + sl.g.nvec * Elem<E>::kVec + (lane - 8);
       if (lane >= 8 && lane < 16 && e < a.V) take_scalar<kRelaxed>(pt, edge_value<E>(edge), e, kLog2e, xd, d);

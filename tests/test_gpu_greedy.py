@@ -194,3 +194,33 @@ def test_confidence_edge_rows(vsv):
     assert int(host(flag)[0]) & vsv.FLAG_TOKEN
     rc, rl = oracle.draft_confidence(y[:3], oracle.F32, 777, sel[:3])
     np.testing.assert_allclose(c[:3], rc, rtol=1e-5)
+
+
+@pytest.mark.parametrize("dtype", [oracle.F32, oracle.BF16])
+@pytest.mark.parametrize("B", [6, 60, 300])
+def test_max_tied_between_head_and_body(vsv, dtype, B):
+    """Rows misaligned by one element start with elements outside the 16-byte
+    body; the row maximum is planted in one of them and again deep in the
+    body, so the lowest index is a head element. 6, 60 and 300 requests take
+    the row kernel with halves, the persistent kernel and the row kernel;
+    the sampled entry point with T = 0 streams the same rows as greedy rows."""
+    import torch
+    rng = np.random.default_rng(600 + B + dtype)
+    V = 5000
+    store, off, owner, drafts = _custom(rng, B, 4, V, dtype, ld=V + 3, ties=True, pad_nan=False, shift=1)
+    top = synth.f32_to_bf16_bits(np.array([5.0], dtype=np.float32))[0] if dtype == oracle.BF16 else np.float32(5.0)
+    store[:, 1 + 1] = top            # element 1 of every row: inside the misaligned head
+    store[:, 1 + 3000] = top         # and the same value in the body
+    R = int(off[-1])
+    print("head tie B=%d R=%d dtype=%d" % (B, R, dtype), flush=True)
+    t = to_dev(store)[:, 1:]
+    out = vsv.verify_greedy(t, to_dev(off), to_dev(owner), to_dev(drafts), vocab=V)
+    torch.cuda.synchronize()
+    ref = oracle.verify_greedy(store[:, 1:], dtype, V, off, owner, drafts)
+    assert (ref["row_token"] == 1).all()
+    assert_same(out, ref)
+    z = torch.zeros(B, dtype=torch.float32, device="cuda")
+    s = vsv.verify_sampled(t, to_dev(off), to_dev(owner), to_dev(drafts), z, torch.zeros(B, dtype=torch.int32,
+                           device="cuda"), torch.ones(B, device="cuda"), z, 1, vocab=V)
+    torch.cuda.synchronize()
+    assert_same(s, ref)
