@@ -244,8 +244,10 @@ def main():
     # the GPU needs tens of milliseconds of sustained work before its clocks
     # settle: with a short warm-up the first timed launches run 5-10 % slow
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5],
-                    help="workload (default: EAGLE greedy B=128 K=4 V=152064)")
+    ap.add_argument("--workload", default="eagle", choices=["tiny", "eagle", "ragged", "relaxed", "mixed"],
+                    help="synthetic batch: tiny greedy B=4 K=4 V=1024 fp32; eagle greedy B=128 K=4 "
+                         "V=152064 bf16 (default); ragged sampled B=128 K~U{0..7} fp32; relaxed top-4 + "
+                         "confidence B=128 K=4 bf16; mixed sampled + confidence B=512 K=7 bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--goodput", action="store_true",
                     help="time goodput step selection (host code, B=512, 7 steps) instead of verification")
@@ -287,8 +289,8 @@ def main():
     vsv.lib()
     if args.allocate:
         return bench_allocate(args, vsv, torch)
-    print("[bench] generating workload %d" % args.config, file=sys.stderr, flush=True)
-    wl = synth.make(args.config)
+    print("[bench] generating workload %s" % args.workload, file=sys.stderr, flush=True)
+    wl = synth.make(args.workload)
     steps, kernels, ncopy, step_bytes = build_steps(vsv, torch, wl)
     torch.cuda.synchronize()
     print("[bench] %d input copies, %.1f MB per step" % (ncopy, step_bytes / 1e6), file=sys.stderr, flush=True)
@@ -324,18 +326,17 @@ def main():
     kname, kbytes = kernels[dom]
     kms = per_kernel_ms[dom]
     achieved = kbytes / (kms * 1e-3) / 1e9
-    tag = "config%d" % args.config
-    traffic = measured_traffic(kname, tag)
+    traffic = measured_traffic(kname, args.workload)
     line = dict(
         metric="verified rows/sec and achieved HBM GB/s (% of peak), B=128 K=4 V=152064",
         value=wl.R / (ms * 1e-3), unit="rows/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
         ms_per_step=ms, higher_is_better=True, scaling="weak", vs_baseline=None,
         dtype="bf16" if wl.dtype == 1 else "f32", data="synthetic",
         hbm_gbps=step_bytes / (ms * 1e-3) / 1e9, hbm_frac=step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        config=dict(workload=wl.name, config=args.config, B=wl.B, R=wl.R, D=wl.D, V=wl.V,
-                    K=None if wl.config == 3 else int((wl.R - wl.B) // wl.B),
+        config=dict(workload=wl.name, key=args.workload, B=wl.B, R=wl.R, D=wl.D, V=wl.V,
+                    K=None if wl._spec["K"] is None else int(wl._spec["K"]),
                     relaxed_topk=wl.relaxed_topk, sampled=bool(wl.sampled), input_copies=ncopy,
-                    bytes_per_step=step_bytes, data_seed=1000 + args.config, philox_seed=wl.seed,
+                    bytes_per_step=step_bytes, data_seed=wl._spec["data_seed"], philox_seed=wl.seed,
                     slow_rows_first_copy=slow),
         roofline=dict(bound="hbm", kernel=kname, achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s",
                       frac=achieved / HBM_PEAK_GBPS, traffic=traffic, bytes_per_launch=kbytes,

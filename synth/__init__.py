@@ -11,8 +11,8 @@ Every row is drawn from its own NumPy stream keyed by (seed, row, attempt),
 so a single row can be re-drawn (attempt + 1) without touching the rest; the
 tests use that to keep sampled rows away from rounding-sensitive thresholds.
 
-The five workloads follow the shapes and distributions of the benchmark
-configurations: B requests of K draft tokens (K + 1 verify rows each, the
+The five workloads (tiny, eagle, ragged, relaxed, mixed) follow the shapes
+and distributions of the verification batches being measured: B requests of K draft tokens (K + 1 verify rows each, the
 bonus row last), a 152064-token vocabulary, N(0, sigma^2) logits in float32
 or bfloat16 (round-to-nearest-even from float32), and drafts that hit the
 target's arg-max with fixed per-position rates.
@@ -38,7 +38,7 @@ def f32_to_bf16_bits(a):
 @dataclass
 class Workload:
     name: str
-    config: int
+    key: str
     B: int
     V: int
     ld: int
@@ -57,7 +57,7 @@ class Workload:
     relaxed_topk: int = 1
     draft_logits: Optional[np.ndarray] = None  # [D, ld] same dtype as logits
     selected: Optional[np.ndarray] = None      # int32 [D]
-    planted: Optional[np.ndarray] = None       # per request, C1 only
+    planted: Optional[np.ndarray] = None       # per request, tiny greedy batch only
     attempts: Dict[int, int] = field(default_factory=dict)
     _spec: dict = field(default_factory=dict, repr=False)
 
@@ -75,23 +75,28 @@ class Workload:
         return (self.R + self.D) * self.V * es
 
 
-# Per-config recipes. sigma: logits standard deviation; boost: added to the
-# row's largest float32 draw before rounding; hit: per-position probability
-# that a draft equals the row's arg-max.
+# Workload recipes by key. sigma: logits standard deviation; boost: added to
+# the row's largest float32 draw before rounding; hit: per-position
+# probability that a draft equals the row's arg-max; data_seed and
+# philox_seed: the default seeds of the logits and of the sampler.
 SPECS = {
-    1: dict(name="tiny greedy verify, B=4 K=4 V=1024 fp32", B=4, K=4, V=1024,
-            dtype=F32, sigma=2.0, boost=0.0, mode="planted"),
-    2: dict(name="EAGLE greedy verify, B=128 K=4 V=152064 bf16", B=128, K=4, V=VOCAB,
+    "tiny": dict(name="tiny greedy verify, B=4 K=4 V=1024 fp32", B=4, K=4, V=1024,
+            dtype=F32, sigma=2.0, boost=0.0, mode="planted", data_seed=1001, philox_seed=2001),
+    "eagle": dict(name="EAGLE greedy verify, B=128 K=4 V=152064 bf16", B=128, K=4, V=VOCAB,
+            data_seed=1002, philox_seed=2002,
             dtype=BF16, sigma=3.0, boost=4.0, mode="hit",
             hit=(0.8, 0.7, 0.6, 0.5), miss="uniform"),
-    3: dict(name="ragged sampled verify, B=128 K~U{0..7} V=152064 fp32", B=128, K=None,
+    "ragged": dict(name="ragged sampled verify, B=128 K~U{0..7} V=152064 fp32", B=128, K=None,
+            data_seed=1003, philox_seed=2003,
             Kmax=7, V=VOCAB, dtype=F32, sigma=2.5, boost=0.0, mode="hit",
             hit=(0.75,), miss="rank", temps=(0.0, 0.5, 1.0), top_k=50, top_p=0.9,
             min_p=0.05, sampled=True),
-    4: dict(name="relaxed top-4 verify + draft confidence, B=128 K=4 V=152064 bf16",
+    "relaxed": dict(name="relaxed top-4 verify + draft confidence, B=128 K=4 V=152064 bf16",
+            data_seed=1004, philox_seed=2004,
             B=128, K=4, V=VOCAB, dtype=BF16, sigma=3.0, boost=0.0, mode="geometric",
             relaxed_topk=4, confidence=True),
-    5: dict(name="large mixed verify + draft confidence, B=512 K=7 V=152064 bf16",
+    "mixed": dict(name="large mixed verify + draft confidence, B=512 K=7 V=152064 bf16",
+            data_seed=1005, philox_seed=2005,
             B=512, K=7, V=VOCAB, dtype=BF16, sigma=3.0, boost=0.0, mode="hit",
             hit=(0.8, 0.7, 0.6, 0.5, 0.5, 0.5, 0.5), miss="rank", temps="alternate",
             alt_temp=0.7, top_k=0, top_p=0.95, min_p=0.0, sampled=True, confidence=True),
@@ -164,10 +169,10 @@ def _token_at_rank(x, rank):
     return int(cand[rank])
 
 
-def make(config, *, B=None, V=None, K=None, ld=None, seed=None, pad=False,
+def make(key, *, B=None, V=None, K=None, ld=None, seed=None, pad=False,
          attempts=None):
-    """Build workload `config` (1..5); B, V, K and ld override the recipe."""
-    spec = dict(SPECS[config])
+    """Build workload `key` (a key of SPECS); B, V, K and ld override the recipe."""
+    spec = dict(SPECS[key])
     if B is not None:
         spec["B"] = B
     if V is not None:
@@ -177,7 +182,7 @@ def make(config, *, B=None, V=None, K=None, ld=None, seed=None, pad=False,
         spec["Kmax"] = K
     Bn, Vn = spec["B"], spec["V"]
     ld = Vn if ld is None else ld
-    seed = 1000 + config if seed is None else seed
+    seed = spec["data_seed"] if seed is None else seed
     attempts = dict(attempts or {})
     g = np.random.default_rng([seed, 0])
 
@@ -190,11 +195,11 @@ def make(config, *, B=None, V=None, K=None, ld=None, seed=None, pad=False,
     R = int(offsets[-1])
     owner = np.repeat(np.arange(Bn, dtype=np.int32), (Ks + 1).astype(np.int64))
 
-    wl = Workload(name=spec["name"], config=config, B=Bn, V=Vn, ld=ld,
+    wl = Workload(name=spec["name"], key=key, B=Bn, V=Vn, ld=ld,
                   dtype=spec["dtype"], offsets=offsets, owner=owner,
                   drafts=np.zeros(R - Bn, dtype=np.int32),
                   logits=np.empty((R, ld), dtype=np.uint16 if spec["dtype"] == BF16 else np.float32),
-                  seed=2000 + config, offset=0,
+                  seed=spec["philox_seed"], offset=0,
                   relaxed_topk=spec.get("relaxed_topk", 1), attempts=attempts)
     wl._spec = dict(spec, pad=pad, data_seed=seed)
 

@@ -29,8 +29,8 @@ def run_greedy(vsv, wl, d=None, **kw):
     return out
 
 
-def test_c1_tiny_closed_form(vsv):
-    wl = synth.make(1)
+def test_tiny_greedy_closed_form(vsv):
+    wl = synth.make("tiny")
     out = run_greedy(vsv, wl)
     assert host(out["accepted_len"]).tolist() == wl.planted.tolist()
     assert_same(out, oracle_of(wl))
@@ -39,14 +39,14 @@ def test_c1_tiny_closed_form(vsv):
 # 16 and 128 requests (80, 640 rows) run one workgroup per row or half row,
 # 32 (160 rows) the persistent kernel
 @pytest.mark.parametrize("B", [16, 32, 128])
-def test_c2_eagle_greedy(vsv, B):
-    wl = synth.make(2, B=B)
+def test_eagle_greedy_k4(vsv, B):
+    wl = synth.make("eagle", B=B)
     assert_same(run_greedy(vsv, wl), oracle_of(wl))
 
 
 @pytest.mark.parametrize("B", [8, 40, 128])
-def test_c4_relaxed_top4(vsv, B):
-    wl = synth.make(4, B=B)
+def test_relaxed_top4_k4(vsv, B):
+    wl = synth.make("relaxed", B=B)
     ref = oracle_of(wl)
     assert_same(run_greedy(vsv, wl), ref)
     assert ref["accepted_len"].mean() > 1.0      # the relaxed rule accepts beyond arg-max hits
@@ -135,7 +135,7 @@ def test_single_row_requests_and_empty_batch(vsv):
 
 
 def test_repeated_calls_reuse_workspace(vsv):
-    wl = synth.make(2, B=32)
+    wl = synth.make("eagle", B=32)
     d = upload(wl)
     a = run_greedy(vsv, wl, d)
     b = run_greedy(vsv, wl, d)
@@ -163,9 +163,9 @@ def test_device_error_flags(vsv):
 
 
 @pytest.mark.parametrize("B", [8, 128])
-def test_c4_draft_confidence(vsv, B):
+def test_relaxed_batch_draft_confidence(vsv, B):
     import torch
-    wl = synth.make(4, B=B)
+    wl = synth.make("relaxed", B=B)
     d = upload(wl)
     conf, lse, flag = vsv.draft_confidence(d["draft_logits"], d["selected"])
     torch.cuda.synchronize()

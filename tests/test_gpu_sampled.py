@@ -42,15 +42,15 @@ def run_custom(vsv, b):
 
 
 @pytest.mark.parametrize("B", [16, 128])
-def test_c3_ragged_sampled(vsv, B):
-    wl = with_margins(synth.make(3, B=B))
+def test_ragged_sampled(vsv, B):
+    wl = with_margins(synth.make("ragged", B=B))
     out = run_sampled(vsv, wl)
     assert_same(out, oracle_of(wl))
 
 
 @pytest.mark.parametrize("B", [8, 48])
-def test_c5_large_mixed(vsv, B):
-    wl = with_margins(synth.make(5, B=B))
+def test_large_mixed_batch(vsv, B):
+    wl = with_margins(synth.make("mixed", B=B))
     out = run_sampled(vsv, wl)
     ref = oracle_of(wl)
     assert_same(out, ref)
@@ -59,9 +59,10 @@ def test_c5_large_mixed(vsv, B):
     assert int(host(out["slow_rows"])[0]) <= max(1, sampled_rows // 20)
 
 
-def test_c5_full_size_sampled_requests(vsv):
-    """Full C5 batch on the GPU; 24 requests re-checked one by one."""
-    wl = synth.make(5)
+def test_large_mixed_full_size_sampled_requests(vsv):
+    """The full mixed batch (B=512, K=7, V=152064 bf16) on the GPU; 24 requests
+    re-checked one by one against the oracle."""
+    wl = synth.make("mixed")
     rng = np.random.default_rng(55)
     check = sorted(rng.choice(wl.B, size=24, replace=False).tolist())
     rows = [r for i in check for r in range(int(wl.offsets[i]), int(wl.offsets[i + 1]))]
@@ -93,7 +94,7 @@ def test_c5_full_size_sampled_requests(vsv):
 
 def test_temperature_zero_is_greedy(vsv):
     import torch
-    wl = synth.make(5, B=16)
+    wl = synth.make("mixed", B=16)
     d = upload(wl)
     z = torch.zeros_like(d["temperature"])
     s = vsv.verify_sampled(d["logits"], d["offsets"], d["owner"], d["drafts"], z, d["top_k"], d["top_p"],
@@ -148,7 +149,7 @@ def test_exact_whole_row_path(vsv):
 
 def test_invalid_parameters_are_flagged(vsv):
     import torch
-    wl = synth.make(5, B=4, V=1000)
+    wl = synth.make("mixed", B=4, V=1000)
     d = upload(wl)
     T = d["temperature"].clone()
     T[1] = -1.0
@@ -160,9 +161,9 @@ def test_invalid_parameters_are_flagged(vsv):
     assert int(host(out["error_flag"])[0]) & vsv.FLAG_PARAMS
 
 
-def test_c5_draft_confidence(vsv):
+def test_large_mixed_draft_confidence(vsv):
     import torch
-    wl = synth.make(5, B=16)
+    wl = synth.make("mixed", B=16)
     d = upload(wl)
     conf, lse, flag = vsv.draft_confidence(d["draft_logits"], d["selected"])
     torch.cuda.synchronize()
@@ -188,7 +189,7 @@ def test_layout_errors_are_flagged(vsv):
     """Inconsistent owner maps and offsets set the layout flag; the launch
     (with its row-order pass) still completes and writes inside the buffers."""
     import torch
-    wl = synth.make(3, B=12, V=1000)
+    wl = synth.make("ragged", B=12, V=1000)
     d = upload(wl)
     own = d["owner"].clone()
     own[3] = (own[3] + 1) % wl.B

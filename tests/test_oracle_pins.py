@@ -123,10 +123,10 @@ def test_rank_matches_brute_force():
         assert [tiny.rank(list(x), int(t)) for t in order] == list(range(23))
 
 
-# ---------------------------------------------------------------- C1 closed form
+# ------------------------------------------------ tiny greedy batch: closed form
 
-def test_c1_closed_form_from_planted_mismatches():
-    w = synth.make(1)
+def test_tiny_closed_form_from_planted_mismatches():
+    w = synth.make("tiny")
     res = oracle.verify_greedy(w.logits, w.dtype, w.V, w.offsets, w.owner, w.drafts)
     assert w.planted.tolist().count(4) == 1
     expect_toks = []
@@ -144,7 +144,7 @@ def test_c1_closed_form_from_planted_mismatches():
 @pytest.mark.parametrize("seed", [11, 12, 13])
 def test_first_mismatch_replacement_and_bonus(seed):
     """top_k = 1 makes every sample the arg-max, so acceptance is closed form."""
-    w = synth.make(1, seed=seed)
+    w = synth.make("tiny", seed=seed)
     B = w.B
     ones = np.ones(B, dtype=np.float32)
     res = oracle.verify_sampled(w.logits, w.dtype, w.V, w.offsets, w.owner, w.drafts,
@@ -208,7 +208,7 @@ def test_out_of_range_draft_is_a_mismatch():
 # ---------------------------------------------------------------- T = 0
 
 def test_temperature_zero_equals_greedy():
-    w = synth.make(5, B=6, V=4096)
+    w = synth.make("mixed", B=6, V=4096)
     B = w.B
     z = np.zeros(B, dtype=np.float32)
     s = oracle.verify_sampled(w.logits, w.dtype, w.V, w.offsets, w.owner, w.drafts,
@@ -221,7 +221,7 @@ def test_temperature_zero_equals_greedy():
 
 def test_sampled_row_lse_is_logsumexp_of_x_over_t():
     # reading c12: a sampled row reports the log-sum-exp of x / T
-    w = synth.make(3, B=5, V=2048)
+    w = synth.make("ragged", B=5, V=2048)
     T = np.full(w.B, 0.5, dtype=np.float32)
     res = oracle.verify_sampled(w.logits, w.dtype, w.V, w.offsets, w.owner, w.drafts,
                                 T, w.top_k, w.top_p, w.min_p, w.seed, 0)
