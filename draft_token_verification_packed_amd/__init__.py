@@ -54,7 +54,7 @@ class Outputs(ctypes.Structure):
 
 
 SYMBOLS = ("vsv_workspace_bytes", "vsv_workspace_init", "vsv_verify_greedy", "vsv_verify_sampled",
-           "vsv_draft_confidence", "vsv_allocate_verify", "vsv_goodput_init", "vsv_goodput_observe",
+           "vsv_verify_probabilistic", "vsv_draft_confidence", "vsv_allocate_verify", "vsv_goodput_init", "vsv_goodput_observe",
            "vsv_goodput_step", "vsv_goodput_select", "vsv_status_string", "vsv_version")
 
 GOODPUT_MAX_STEPS = 32
@@ -91,6 +91,9 @@ def lib():
     L.vsv_verify_sampled.argtypes = [ctypes.POINTER(Batch), vp, vp, vp, vp, u64, u64,
                                      ctypes.POINTER(Outputs), vp, sz, vp]
     L.vsv_verify_sampled.restype = ctypes.c_int
+    L.vsv_verify_probabilistic.argtypes = [ctypes.POINTER(Batch), vp, i64, vp, vp, vp, vp, vp, u64, u64,
+                                           ctypes.POINTER(Outputs), vp, sz, vp]
+    L.vsv_verify_probabilistic.restype = ctypes.c_int
     L.vsv_draft_confidence.argtypes = [vp, i32, i32, i64, i32, vp, vp, vp, vp, vp]
     L.vsv_draft_confidence.restype = ctypes.c_int
     L.vsv_allocate_verify.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
@@ -218,6 +221,32 @@ def verify_sampled(logits, row_offsets, row_owner, draft_tokens, temperature, to
     _check(lib().vsv_verify_sampled(ctypes.byref(batch), _ptr(temperature), _ptr(top_k), _ptr(top_p),
                                     _ptr(min_p), int(seed) & (2**64 - 1), int(offset) & (2**64 - 1),
                                     ctypes.byref(outs), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def verify_probabilistic(logits, row_offsets, row_owner, draft_tokens, draft_logits, temperature, top_k, top_p,
+                         min_p, draft_temperature, seed, offset=0, vocab=None, ws=None, stream=None):
+    """Rejection-sampling verification with probabilistic drafts; draft_logits
+    holds the R - B draft rows in the draft tokens' layout. Returns a dict of
+    device tensors (row_lse and slow_rows are not written)."""
+    batch, outs, out, B, R = _prepare(logits, row_offsets, row_owner, draft_tokens, vocab)
+    for t, n in ((temperature, "temperature"), (top_p, "top_p"), (min_p, "min_p"),
+                 (draft_temperature, "draft_temperature")):
+        _vec(t, B, torch.float32, n)
+    _vec(top_k, B, torch.int32, "top_k")
+    dld = 0
+    if R - B > 0:
+        dtype, V, _ = _logits(logits, vocab)
+        ddt, _, dld = _logits(draft_logits, vocab if vocab is not None else logits.shape[1])
+        if ddt != dtype or draft_logits.shape[0] != R - B or draft_logits.shape[1] < V:
+            raise ValueError("draft_logits must be [R - B, >= vocab] of the logits' dtype")
+        dld = draft_logits.stride(0) if draft_logits.shape[0] > 1 else max(draft_logits.shape[1], 1)
+    ws = workspace(B, R, False, logits.device, stream) if ws is None else ws
+    _check(lib().vsv_verify_probabilistic(ctypes.byref(batch), _ptr(draft_logits) if R - B > 0 else None, int(dld),
+                                          _ptr(temperature), _ptr(top_k), _ptr(top_p), _ptr(min_p),
+                                          _ptr(draft_temperature), int(seed) & (2**64 - 1),
+                                          int(offset) & (2**64 - 1), ctypes.byref(outs), _ptr(ws), ws.numel(),
+                                          _stream(stream)))
     return out
 
 

@@ -5,6 +5,7 @@
 
 #include "allocate.hpp"
 #include "kernels.hpp"
+#include "probabilistic.hpp"
 
 using vsv::VerifyArgs;
 
@@ -128,6 +129,31 @@ vsv_status vsv_verify_sampled(const vsv_batch* batch, const float* temperature, 
   return vsv::launch_verify_sampled(a, stream) == hipSuccess ? VSV_OK : VSV_EHIP;
 }
 
+vsv_status vsv_verify_probabilistic(const vsv_batch* batch, const void* draft_logits, int64_t draft_ld,
+                                    const float* temperature, const int32_t* top_k, const float* top_p,
+                                    const float* min_p, const float* draft_temperature, uint64_t seed,
+                                    uint64_t offset, const vsv_outputs* out, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  VerifyArgs a;
+  bool empty = false;
+  const vsv_status st = prepare(batch, out, workspace, workspace_bytes, 0, &a, &empty);
+  if (st != VSV_OK || empty) return st;
+  if (!temperature || !top_k || !top_p || !min_p || !draft_temperature) return VSV_EINVAL;
+  const int32_t D = batch->num_rows - batch->num_requests;
+  if (D > 0) {
+    if (!draft_logits || !aligned(draft_logits, elem_size(batch->dtype))) return VSV_EINVAL;
+    if (draft_ld < batch->vocab || draft_ld > (INT64_MAX / 4) / D) return VSV_EINVAL;
+  }
+  a.temperature = temperature;
+  a.top_k = top_k;
+  a.top_p = top_p;
+  a.min_p = min_p;
+  a.seed = seed;
+  a.offset = offset;
+  const vsv::ProbArgs p{draft_logits, draft_ld, draft_temperature};
+  return vsv::launch_verify_probabilistic(a, p, stream) == hipSuccess ? VSV_OK : VSV_EHIP;
+}
+
 vsv_status vsv_draft_confidence(const void* draft_logits, int32_t dtype, int32_t vocab, int64_t ld,
                                 int32_t num_draft_rows, const int32_t* selected, float* confidence,
                                 float* lse, int32_t* error_flag, hipStream_t stream) {
@@ -168,6 +194,6 @@ const char* vsv_status_string(vsv_status status) {
   return "unknown status";
 }
 
-int32_t vsv_version(void) { return 101; }
+int32_t vsv_version(void) { return 102; }
 
 }  // extern "C"

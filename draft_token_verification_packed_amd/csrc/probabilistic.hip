@@ -1,0 +1,343 @@
+// Verification with probabilistic drafts (gfx950): the rejection sampler of
+// speculative decoding over a packed batch.
+//
+// What is computed, per request i with drafts d_0 .. d_{K-1}: p_j is the
+// target's law at row j (the sampled path's filtered, renormalised softmax
+// of x_j / T_i, or the point mass at the arg-max when T_i = 0) and q_j the
+// draft's (the softmax of the draft row over the request's draft
+// temperature, or the point mass at that row's arg-max when it is 0). Draft
+// j passes when u_acc * q_j(d_j) < p_j(d_j), i.e. with probability
+// min(1, p / q). The first rejected row emits the inverse-CDF draw of
+// max(0, p_j - q_j) in the target's rank order (value descending, index
+// ascending; first cumulative weight strictly above u times the total), and
+// a request whose drafts all pass emits the bonus row's draw from p_K. The
+// pages name this case and leave it unsupported (xLLM docs, "Adaptive
+// speculative inference", DSpark section "Launch example"): their point-mass
+// drafts, which the sampled path verifies, are its special case.
+//
+// How: correctness first, not speed. One workgroup per row streams the
+// target row for its maximum and arg-max. A sampled row then settles its
+// survivor set and own draw with the sampled path's exact whole-row radix
+// locator (several passes over the row, which stays in the caches), reads
+// the draft row for its maximum and exponent sum, and locates the residual
+// draw by a radix descent over the target's keys weighted by max(0, p - q),
+// then by index inside the located key. Each row stores a tagged word; the
+// workgroup that finishes last runs the per-request scan.
+#include "probabilistic.hpp"
+#include "sampled_row.hpp"
+#include "verify_common.hpp"
+
+namespace vsv {
+
+namespace {
+
+// Uniforms of (request, local row): word 0 of the row's Philox block draws
+// the token (the sampled path's u), word 1 tests acceptance.
+__device__ __forceinline__ void prob_uniforms(uint64_t seed, uint64_t offset, int request, int row, double& u,
+                                              double& u_acc) {
+  const Philox4 o = philox4x32_10(
+      Philox4{static_cast<uint32_t>(row), static_cast<uint32_t>(request), static_cast<uint32_t>(offset),
+              static_cast<uint32_t>(offset >> 32)},
+      static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
+  u = static_cast<double>(o.x >> 8) * (1.0 / 16777216.0);
+  u_acc = static_cast<double>(o.y >> 8) * (1.0 / 16777216.0);
+}
+
+// The survivor set, a prefix of the rank order: its size, its total weight
+// and its last token (key and index).
+struct Support {
+  int n;
+  double w;
+  uint32_t key;
+  int idx;
+};
+
+// The filters in the sampled path's order: top-k count, top-p mass over the
+// top-k survivors (the crossing token kept), min-p cut.
+template <typename E, int NT>
+__device__ Support support(FullLocator<E, NT>& loc, int V, int top_k, double top_p, double min_p) {
+  int n = V;
+  double w;
+  if (top_k > 0 && top_k < V) {
+    n = top_k;
+    w = loc.by_count(top_k).cum;
+  } else {
+    w = loc.total_mass();
+  }
+  if (top_p < 1.0) {
+    const Pick p = loc.by_mass(top_p * w, false);
+    n = p.rank + 1;
+    w = p.cum;
+  }
+  if (min_p > 0.0) {
+    bool exact = false;
+    const int lm = loc.count_minp(log(min_p), exact);
+    if (lm < n) {
+      n = lm > 0 ? lm : 1;
+      w = loc.by_count(n).cum;
+    }
+  }
+  const Pick last = loc.by_count(n);
+  return Support{n, w, ord_ukey(loc.at(last.idx)), last.idx};
+}
+
+__device__ __forceinline__ bool in_support(uint32_t k, int e, const Support& s) {
+  return k > s.key || (k == s.key && e <= s.idx);
+}
+
+// The draft's law: softmax of the draft row over Td, or the point mass at
+// its lowest arg-max when Td = 0.
+struct DraftLaw {
+  float my;
+  double Td;
+  double Z;
+  int h;
+  __device__ double q(float y, int e) const {
+    if (Td > 0.0) return exp((static_cast<double>(y) - static_cast<double>(my)) / Td) / Z;
+    return e == h ? 1.0 : 0.0;
+  }
+};
+
+// Returns false when the draft row has a NaN or no finite maximum.
+template <typename E, int NT>
+__device__ bool draft_law(const E* __restrict__ y, int V, double Td, SampledLds<NT>& L, DraftLaw& q) {
+  float mx = -INFINITY;
+  int nan = 0;
+  for (int e = threadIdx.x; e < V; e += NT) {
+    const float v = Elem<E>::at(y, e);
+    nan |= (v != v) ? 1 : 0;
+    mx = fmaxf(mx, v);
+  }
+  nan = block_reduce<NT>(nan, MaxOp(), L.red_i);
+  const double md = block_reduce<NT>(static_cast<double>(mx), MaxOp(), L.red_d);
+  q.my = static_cast<float>(md);
+  q.Td = Td;
+  q.Z = 1.0;
+  q.h = 0;
+  if (nan || !(md > -INFINITY) || !(md < INFINITY)) return false;
+  if (Td > 0.0) {
+    double s = 0.0;
+    for (int e = threadIdx.x; e < V; e += NT)
+      s += exp((static_cast<double>(Elem<E>::at(y, e)) - md) / Td);
+    q.Z = block_reduce<NT>(s, SumOp(), L.red_d);
+  } else {
+    int h = INT32_MAX;
+    for (int e = threadIdx.x; e < V; e += NT)
+      if (Elem<E>::at(y, e) == q.my && e < h) h = e;
+    q.h = block_reduce<NT>(h, MinOp(), L.red_i);
+  }
+  return true;
+}
+
+// The residual draw: the first token in rank order whose cumulative
+// max(0, p - q) exceeds u times the residual's total, or -1 if the residual
+// has no mass.
+template <typename E, int NT>
+__device__ int residual_draw(const E* __restrict__ x, const E* __restrict__ y, int V, float m, double T,
+                             const Support& s, const DraftLaw& q, double u, SampledLds<NT>& L) {
+  auto mass = [&](int e, uint32_t& k) -> double {
+    const float xv = Elem<E>::at(x, e);
+    k = ord_ukey(xv);
+    if (!in_support(k, e, s)) return 0.0;
+    const double r = weight(xv, m, T) / s.w - q.q(Elem<E>::at(y, e), e);
+    return r > 0.0 ? r : 0.0;
+  };
+  // radix descent over the keys (8-bit digits, most significant first),
+  // counting only tokens of positive residual mass
+  uint32_t prefix = 0;
+  for (int d = 0; d < 4; ++d) {
+    const int shift = 24 - 8 * d;
+    for (int b = threadIdx.x; b < 256; b += NT) {
+      L.u.radix.cnt[b] = 0;
+      L.u.radix.mass[b] = 0.0;
+    }
+    lds_barrier();
+    for (int e = threadIdx.x; e < V; e += NT) {
+      uint32_t k;
+      const double r = mass(e, k);
+      if (!(r > 0.0)) continue;
+      if (d > 0 && (k >> (shift + 8)) != prefix) continue;
+      const int dig = static_cast<int>((k >> shift) & 255u);
+      atomicAdd(&L.u.radix.cnt[dig], 1);
+      atomicAdd(&L.u.radix.mass[dig], r);
+    }
+    lds_barrier();
+    if (threadIdx.x == 0) {
+      if (d == 0) {
+        double t = 0.0;
+        for (int b = 255; b >= 0; --b) t += L.u.radix.mass[b];
+        L.bd[2] = u * t;  // the target
+        L.bd[0] = 0.0;    // mass above the located prefix
+      }
+      const double target = L.bd[2];
+      double w = L.bd[0], wl = 0.0;
+      int dsel = -1, dl = -1;
+      for (int dig = 255; dig >= 0; --dig) {
+        if (L.u.radix.cnt[dig] == 0) continue;
+        const double nw = w + L.u.radix.mass[dig];
+        dl = dig;
+        wl = w;
+        if (nw > target) {
+          dsel = dig;
+          break;
+        }
+        w = nw;
+      }
+      // a target at the total (rounding) takes the last token with mass
+      if (dsel < 0) {
+        dsel = dl;
+        w = wl;
+      }
+      L.bi[0] = dsel;
+      L.bd[0] = w;
+    }
+    lds_barrier();
+    const int dsel = L.bi[0];
+    if (dsel < 0) return -1;  // uniform: no mass at all
+    prefix = (prefix << 8) | static_cast<uint32_t>(dsel);
+  }
+  const uint32_t key = prefix;
+  const double target = L.bd[2];
+  double acc = L.bd[0];
+  lds_barrier();
+  // the located key's tokens in index order
+  int mylast = -1;
+  for (int base = 0; base < V; base += NT * 8) {
+    const int lo = base + static_cast<int>(threadIdx.x) * 8;
+    double c = 0.0;
+    for (int e = lo; e < lo + 8 && e < V; ++e) {
+      uint32_t k;
+      const double r = mass(e, k);
+      if (k == key && r > 0.0) {
+        c += r;
+        mylast = e;
+      }
+    }
+    double tot;
+    const double incl = block_scan_incl<NT, double>(c, L.red_d, tot);
+    if (threadIdx.x == 0) L.bi[3] = INT32_MAX;
+    lds_barrier();
+    if (c > 0.0 && acc + (incl - c) <= target && acc + incl > target) {
+      double run = acc + (incl - c);
+      int pick = -1;
+      for (int e = lo; e < lo + 8 && e < V; ++e) {
+        uint32_t k;
+        const double r = mass(e, k);
+        if (k == key && r > 0.0) {
+          pick = e;
+          run += r;
+          if (run > target) break;
+        }
+      }
+      atomicMin(&L.bi[3], pick);
+    }
+    lds_barrier();
+    const int found = L.bi[3];
+    lds_barrier();
+    if (found != INT32_MAX) return found;
+    acc += tot;
+  }
+  return block_reduce<NT>(mylast, MaxOp(), L.red_i);
+}
+
+}  // namespace
+
+template <typename E, int NT, int U>
+__global__ __launch_bounds__(NT) void verify_probabilistic_kernel(VerifyArgs a, ProbArgs pa) {
+  __shared__ SampledLds<NT> L;
+  static_assert(sizeof(TailScratch) <= sizeof(L.c), "tail staging aliases the candidate buffer");
+  const uint32_t tag = call_tag(a);
+  const int r = static_cast<int>(blockIdx.x);
+  const E* __restrict__ row = static_cast<const E*>(a.logits) + static_cast<int64_t>(r) * a.ld;
+  const RowMeta m = load_meta(a, r, a.owner[r]);
+  const int req = m.req < 0 ? 0 : m.req;
+  const float T = a.temperature[req];
+  const float Tq = pa.draft_temperature[req];
+  int top_k = a.top_k[req];
+  float top_p = a.top_p[req];
+  float min_p = a.min_p[req];
+  int bits = 0;
+  if (m.req >= 0) {
+    if (!(T >= 0.f && T < INFINITY) || !(Tq >= 0.f && Tq < INFINITY)) bits |= VSV_FLAG_PARAMS;
+    if (!(top_p > 0.f && top_p <= 1.f)) {
+      bits |= VSV_FLAG_PARAMS;
+      top_p = 1.f;
+    }
+    if (!(min_p >= 0.f && min_p <= 1.f)) {
+      bits |= VSV_FLAG_PARAMS;
+      min_p = 0.f;
+    }
+  }
+
+  // the target row's maximum and lowest arg-max
+  RowPartial p;
+  partial_init(p);
+  GroupKeep<U> keep{};
+  constexpr float kLog2e = 1.4426950408889634f;
+  stream_row<E, NT, U, false>(row, a.V, kLog2e, INFINITY, 0, p, keep);
+  const RowResult res = finish_row<E, NT, U, false, true>(p, L.rs, keep, row, a.V);
+  int token = res.argmax == INT32_MAX ? 0 : res.argmax;
+  if (!(res.max < INFINITY) || res.argmax == INT32_MAX || !isfinite(res.lse)) bits |= VSV_FLAG_LOGITS;
+
+  bool accept = false;
+  const bool live = m.req >= 0 && !(bits & VSV_FLAG_LOGITS);
+  if (live && T > 0.f && T < INFINITY) {
+    const double Td = static_cast<double>(T);
+    lds_barrier();
+    FullLocator<E, NT> fl(L, row, a.V, res.max, Td);
+    const Support s = support(fl, a.V, top_k, static_cast<double>(top_p), static_cast<double>(min_p));
+    double u, ua;
+    prob_uniforms(a.seed, a.offset, m.req, m.j, u, ua);
+    Pick own = fl.by_mass(u * s.w, true);
+    if (own.rank >= s.n) own = fl.by_count(s.n);
+    token = own.idx;
+    if (m.j < m.K) {
+      const E* __restrict__ y = static_cast<const E*>(pa.draft_logits) + static_cast<int64_t>(r - m.req) * pa.dld;
+      const double Tdq = (Tq >= 0.f && Tq < INFINITY) ? static_cast<double>(Tq) : 0.0;
+      DraftLaw q;
+      if (!draft_law<E, NT>(y, a.V, Tdq, L, q)) {
+        bits |= VSV_FLAG_LOGITS;
+      } else {
+        const int d = m.draft;
+        if (d >= 0 && d < a.V) {
+          const float xd = Elem<E>::at(row, d);
+          const double pd = in_support(ord_ukey(xd), d, s) ? weight(xd, res.max, Td) / s.w : 0.0;
+          accept = ua * q.q(Elem<E>::at(y, d), d) < pd;
+        }
+        const int t = residual_draw<E, NT>(row, y, a.V, res.max, Td, s, q, u, L);
+        if (t >= 0) token = t;
+      }
+    }
+  } else if (live) {
+    // a greedy target is the point mass at its arg-max: a draft passes
+    // exactly when it is the arg-max, and the residual is the arg-max too
+    accept = m.j < m.K && m.draft == token;
+  }
+  if (threadIdx.x == 0) {
+    const uint32_t word = row_word(a, m, token, accept, bits);
+    if (bits) set_flag(a, bits);
+    if (a.row_token) a.row_token[r] = token;
+    store_agent64(a.ws_row + r, tagged(tag, word));
+    const uint32_t done = __hip_atomic_fetch_add(a.ws_queue + kQueueDone, 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    L.last = done + 1 == gridDim.x;
+  }
+  lds_barrier();
+  if (L.last) {
+    if (threadIdx.x == 0) store_agent(a.ws_queue + kQueueDone, 0u);
+    words_tail<NT>(a, tag, *reinterpret_cast<TailScratch*>(&L.c));
+  }
+}
+
+template <typename E>
+static hipError_t launch_probabilistic_t(const VerifyArgs& a, const ProbArgs& p, hipStream_t s) {
+  verify_probabilistic_kernel<E, kVerifyThreads, SampledDepth<E>::kGreedy>
+      <<<dim3(a.R), dim3(kVerifyThreads), 0, s>>>(a, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify_probabilistic(const VerifyArgs& a, const ProbArgs& p, hipStream_t s) {
+  return a.dtype == VSV_BF16 ? launch_probabilistic_t<uint16_t>(a, p, s) : launch_probabilistic_t<float>(a, p, s);
+}
+
+}  // namespace vsv

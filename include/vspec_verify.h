@@ -141,6 +141,36 @@ vsv_status vsv_verify_sampled(const vsv_batch* batch, const float* temperature,
                               const vsv_outputs* out, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
+/* Verification with probabilistic drafts: the rejection sampler of
+ * speculative decoding. The pages support only the point-mass drafts of
+ * vsv_verify_sampled and name this general case as unsupported (xLLM docs,
+ * "Adaptive speculative inference", DSpark section "Launch example").
+ * draft_logits: device [R - B, draft_ld] rows of the batch's dtype and
+ * vocabulary; draft j of request i sits at row off[i] - i + j, like its
+ * token. draft_temperature [B]: the temperature the draft was drawn at
+ * (0: the draft row's lowest arg-max). With p the target row's law (as in
+ * vsv_verify_sampled, or the arg-max's point mass when T = 0) and q the
+ * draft row's softmax over its temperature: draft j passes iff
+ * u_acc * q(d_j) < p(d_j), u_acc = (w1 >> 8) * 2^-24 from word 1 of the
+ * same Philox block as u; the first rejected row emits the inverse-CDF draw
+ * of max(0, p - q) in rank order at u (its own draw from p if that residual
+ * has no mass); a request whose drafts all pass emits the bonus row's draw.
+ * row_token holds each row's emitted-if-first-rejected token (the bonus
+ * row's own draw); row_lse and slow_rows are not written. Correctness first:
+ * each sampled row takes several passes over its target and draft rows.
+ * Workspace: vsv_workspace_bytes(B, R, 0) or more.
+ * Errors: as vsv_verify_sampled, plus VSV_EINVAL for NULL draft rows (when
+ * R > B) or draft temperatures, draft_ld < vocab or misaligned draft rows.
+ * NaN in a draft row sets VSV_FLAG_LOGITS; a negative, NaN or infinite
+ * draft temperature sets VSV_FLAG_PARAMS and counts as 0. */
+vsv_status vsv_verify_probabilistic(const vsv_batch* batch, const void* draft_logits,
+                                    int64_t draft_ld, const float* temperature,
+                                    const int32_t* top_k, const float* top_p,
+                                    const float* min_p, const float* draft_temperature,
+                                    uint64_t seed, uint64_t offset, const vsv_outputs* out,
+                                    void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
 /* Draft confidence c_q = exp(y[s_q] - logsumexp(y)) for every draft row q of
  * raw draft logits y (no temperature): the draft probability of the selected
  * token, the score adaptive verification budgets consume (xLLM docs,
