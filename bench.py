@@ -184,6 +184,68 @@ def bench_allocate(args, vsv, torch):
     return 0
 
 
+def bench_probabilistic(args, vsv, torch):
+    """Verification with probabilistic drafts on the large mixed batch (B=512,
+    K=7, V=152064 bf16: even requests greedy, odd ones T = 0.7 and top_p
+    0.95), each draft row the draft law at the request's temperature. The
+    kernel is the exact, multi-pass one, so the line caps the launches at 3
+    warm-up and 20 timed ones."""
+    import numpy as np
+    import synth
+    wl = synth.make("mixed")
+    B, R, V = wl.B, wl.R, wl.V
+    td = wl.temperature.astype(np.float32)
+    dev = [upload(torch, a) for a in (wl.logits, wl.offsets, wl.owner, wl.drafts, wl.draft_logits,
+                                      wl.temperature, wl.top_k, wl.top_p, wl.min_p, td)]
+    x, off, own, dr, y, T, TK, TP, MP, TD = dev
+    warm, steps = min(args.warmup, 3), min(args.steps, 20)
+
+    def call():
+        return vsv.verify_probabilistic(x, off, own, dr, y, T, TK, TP, MP, TD, wl.seed, wl.offset, vocab=V)
+    for _ in range(warm):
+        call()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(steps):
+        out = call()
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    assert int(out["error_flag"].item()) == 0
+    nbytes = (R + wl.D) * V * 2     # every target and draft row read once
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    line = dict(metric="probabilistic-draft verified rows/sec, B=512 K=7 V=152064", value=R / (ms * 1e-3),
+                unit="rows/s", n_gpus=1, steps=steps, warmup=warm, ms_per_step=ms, higher_is_better=True,
+                scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
+                config=dict(workload="probabilistic-draft verify, " + wl.name.split(", ", 1)[1], B=B, R=R, D=wl.D,
+                            V=V, draft_temperature="the request's target temperature", data_seed=wl._spec["data_seed"],
+                            philox_seed=wl.seed),
+                roofline=dict(bound="hbm", kernel="verify_probabilistic_kernel", achieved=achieved,
+                              peak=HBM_PEAK_GBPS, unit="GB/s", frac=achieved / HBM_PEAK_GBPS, traffic=None,
+                              bytes_per_launch=nbytes, launch_us=ms * 1e3,
+                              note="exact multi-pass kernel: bound by its passes over rows held in the caches"))
+    if not args.no_cpu_baseline:
+        from oracle.probabilistic import verify_probabilistic
+        t0 = time.perf_counter()
+        rows, n = 0, 0
+        while time.perf_counter() - t0 < 12.0 and n < B:
+            r0, r1 = int(wl.offsets[n]), int(wl.offsets[n + 1])
+            sub = slice(n, n + 1)
+            verify_probabilistic(wl.logits[r0:r1], wl.dtype, V, np.array([0, r1 - r0], dtype=np.int32),
+                                 np.zeros(r1 - r0, dtype=np.int32), wl.drafts[r0 - n:r1 - n - 1],
+                                 wl.draft_logits[r0 - n:r1 - n - 1], wl.temperature[sub], wl.top_k[sub],
+                                 wl.top_p[sub], wl.min_p[sub], td[sub], wl.seed, wl.offset)
+            rows += r1 - r0
+            n += 1
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = dict(value=rows / dt, unit="rows/s", cores=1, kind="oracle",
+                                    sample="first %d requests (%d rows) one by one, %.1f s, single process"
+                                    % (n, rows, dt))
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def bench_goodput(args, vsv):
     """Goodput step selection per completed batch (host code): observe one
     batch of B=512 requests with up to 7 verified drafts, then pick the next
@@ -251,6 +313,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--goodput", action="store_true",
                     help="time goodput step selection (host code, B=512, 7 steps) instead of verification")
+    ap.add_argument("--probabilistic", action="store_true",
+                    help="time verification with probabilistic drafts on the mixed B=512 K=7 batch instead")
     ap.add_argument("--allocate", action="store_true",
                     help="time adaptive verify allocation (B=512, K=7) instead of verification")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -289,6 +353,8 @@ def main():
     vsv.lib()
     if args.allocate:
         return bench_allocate(args, vsv, torch)
+    if args.probabilistic:
+        return bench_probabilistic(args, vsv, torch)
     print("[bench] generating workload %s" % args.workload, file=sys.stderr, flush=True)
     wl = synth.make(args.workload)
     steps, kernels, ncopy, step_bytes = build_steps(vsv, torch, wl)
