@@ -114,6 +114,25 @@ def test_sampled_rejects_missing_parameters(L):
     assert st == 1
 
 
+def _prob(L, b, o, draft=0x200000, dld=1024, params=(8, 8, 8, 8, 8)):
+    return L.vsv_verify_probabilistic(ctypes.byref(b), ctypes.c_void_p(draft) if draft else None, dld,
+                                      *[ctypes.c_void_p(p) if p else None for p in params], 1, 0, ctypes.byref(o),
+                                      ctypes.c_void_p(0x100000), 1 << 20, None)
+
+
+def test_probabilistic_validation(L):
+    b, o = _batch(), _outs()
+    for k in range(5):                                   # each parameter array, draft temperature last
+        params = [8] * 5
+        params[k] = 0
+        assert _prob(L, b, o, params=params) == 1
+    assert _prob(L, b, o, draft=0) == 1                  # draft rows needed when R > B
+    assert _prob(L, b, o, draft=0x200001) == 1           # misaligned bf16 rows
+    assert _prob(L, b, o, dld=1000) == 1                 # draft_ld < vocab
+    assert _prob(L, _batch(), _outs(out_tokens=None)) == 1
+    assert _prob(L, _batch(num_requests=0, num_rows=0), o, draft=0, params=(0, 0, 0, 0, 0)) == 0
+
+
 def test_confidence_validation(L):
     f = L.vsv_draft_confidence
     assert f(ctypes.c_void_p(0x10000), 1, 100, 100, 0, None, None, None, None, None) == 0   # D = 0: no-op
