@@ -31,6 +31,28 @@ namespace vsv {
 
 namespace {
 
+// Visits every element e = threadIdx.x + k NT of a row as f(e, value),
+// with the loads of kBatch steps issued before any is used. These loops run
+// over rows already in the caches; with one load per iteration each thread
+// would wait out every load's latency in turn.
+template <typename E, int NT, typename F>
+__device__ __forceinline__ void for_each_elem(const E* __restrict__ row, int V, F f) {
+  constexpr int kBatch = 8;
+  for (int base = threadIdx.x; base < V; base += NT * kBatch) {
+    float xs[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int e = base + b * NT;
+      xs[b] = e < V ? Elem<E>::at(row, e) : 0.f;
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int e = base + b * NT;
+      if (e < V) f(e, xs[b]);
+    }
+  }
+}
+
 // Uniforms of (request, local row): word 0 of the row's Philox block draws
 // the token (the sampled path's u), word 1 tests acceptance.
 __device__ __forceinline__ void prob_uniforms(uint64_t seed, uint64_t offset, int request, int row, double& u,
@@ -103,11 +125,10 @@ template <typename E, int NT>
 __device__ bool draft_law(const E* __restrict__ y, int V, double Td, SampledLds<NT>& L, DraftLaw& q) {
   float mx = -INFINITY;
   int nan = 0;
-  for (int e = threadIdx.x; e < V; e += NT) {
-    const float v = Elem<E>::at(y, e);
+  for_each_elem<E, NT>(y, V, [&](int, float v) {
     nan |= (v != v) ? 1 : 0;
     mx = fmaxf(mx, v);
-  }
+  });
   nan = block_reduce<NT>(nan, MaxOp(), L.red_i);
   const double md = block_reduce<NT>(static_cast<double>(mx), MaxOp(), L.red_d);
   q.my = static_cast<float>(md);
@@ -117,13 +138,13 @@ __device__ bool draft_law(const E* __restrict__ y, int V, double Td, SampledLds<
   if (nan || !(md > -INFINITY) || !(md < INFINITY)) return false;
   if (Td > 0.0) {
     double s = 0.0;
-    for (int e = threadIdx.x; e < V; e += NT)
-      s += exp((static_cast<double>(Elem<E>::at(y, e)) - md) / Td);
+    for_each_elem<E, NT>(y, V, [&](int, float v) { s += exp((static_cast<double>(v) - md) / Td); });
     q.Z = block_reduce<NT>(s, SumOp(), L.red_d);
   } else {
     int h = INT32_MAX;
-    for (int e = threadIdx.x; e < V; e += NT)
-      if (Elem<E>::at(y, e) == q.my && e < h) h = e;
+    for_each_elem<E, NT>(y, V, [&](int e, float v) {
+      if (v == q.my && e < h) h = e;
+    });
     q.h = block_reduce<NT>(h, MinOp(), L.red_i);
   }
   return true;
@@ -135,8 +156,8 @@ __device__ bool draft_law(const E* __restrict__ y, int V, double Td, SampledLds<
 template <typename E, int NT>
 __device__ int residual_draw(const E* __restrict__ x, const E* __restrict__ y, int V, float m, double T,
                              const Support& s, const DraftLaw& q, double u, SampledLds<NT>& L) {
-  auto mass = [&](int e, uint32_t& k) -> double {
-    const float xv = Elem<E>::at(x, e);
+  // the draft row is read only at survivors
+  auto mass = [&](int e, float xv, uint32_t& k) -> double {
     k = ord_ukey(xv);
     if (!in_support(k, e, s)) return 0.0;
     const double r = weight(xv, m, T) / s.w - q.q(Elem<E>::at(y, e), e);
@@ -152,15 +173,15 @@ __device__ int residual_draw(const E* __restrict__ x, const E* __restrict__ y, i
       L.u.radix.mass[b] = 0.0;
     }
     lds_barrier();
-    for (int e = threadIdx.x; e < V; e += NT) {
+    for_each_elem<E, NT>(x, V, [&](int e, float xv) {
+      if (d > 0 && (ord_ukey(xv) >> (shift + 8)) != prefix) return;
       uint32_t k;
-      const double r = mass(e, k);
-      if (!(r > 0.0)) continue;
-      if (d > 0 && (k >> (shift + 8)) != prefix) continue;
+      const double r = mass(e, xv, k);
+      if (!(r > 0.0)) return;
       const int dig = static_cast<int>((k >> shift) & 255u);
       atomicAdd(&L.u.radix.cnt[dig], 1);
       atomicAdd(&L.u.radix.mass[dig], r);
-    }
+    });
     lds_barrier();
     if (threadIdx.x == 0) {
       if (d == 0) {
@@ -204,13 +225,17 @@ __device__ int residual_draw(const E* __restrict__ x, const E* __restrict__ y, i
   int mylast = -1;
   for (int base = 0; base < V; base += NT * 8) {
     const int lo = base + static_cast<int>(threadIdx.x) * 8;
+    float xs[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) xs[b] = lo + b < V ? Elem<E>::at(x, lo + b) : 0.f;
     double c = 0.0;
-    for (int e = lo; e < lo + 8 && e < V; ++e) {
+    for (int b = 0; b < 8 && lo + b < V; ++b) {
+      if (ord_ukey(xs[b]) != key) continue;
       uint32_t k;
-      const double r = mass(e, k);
-      if (k == key && r > 0.0) {
+      const double r = mass(lo + b, xs[b], k);
+      if (r > 0.0) {
         c += r;
-        mylast = e;
+        mylast = lo + b;
       }
     }
     double tot;
@@ -220,11 +245,12 @@ __device__ int residual_draw(const E* __restrict__ x, const E* __restrict__ y, i
     if (c > 0.0 && acc + (incl - c) <= target && acc + incl > target) {
       double run = acc + (incl - c);
       int pick = -1;
-      for (int e = lo; e < lo + 8 && e < V; ++e) {
+      for (int b = 0; b < 8 && lo + b < V; ++b) {
+        if (ord_ukey(xs[b]) != key) continue;
         uint32_t k;
-        const double r = mass(e, k);
-        if (k == key && r > 0.0) {
-          pick = e;
+        const double r = mass(lo + b, xs[b], k);
+        if (r > 0.0) {
+          pick = lo + b;
           run += r;
           if (run > target) break;
         }
