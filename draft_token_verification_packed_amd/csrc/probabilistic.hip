@@ -266,6 +266,90 @@ __device__ int residual_draw(const E* __restrict__ x, const E* __restrict__ y, i
   return block_reduce<NT>(mylast, MaxOp(), L.red_i);
 }
 
+// The residual draw when the survivors fit in the candidate buffer (the
+// usual case: top-p keeps a small head of the order). The survivors are
+// gathered into LDS, sorted into rank order (bitonic, key descending, index
+// ascending), and the first one whose cumulative residual mass exceeds u
+// times the total is found by a block scan over contiguous runs of the
+// sorted list. Same result as residual_draw up to summation order.
+template <typename E, int NT>
+__device__ int residual_draw_sorted(const E* __restrict__ x, const E* __restrict__ y, int V, float m, double T,
+                                    const Support& s, const DraftLaw& q, double u, SampledLds<NT>& L) {
+  int P = 1;
+  while (P < s.n) P <<= 1;
+  Cand* c = L.c.cand;
+  if (threadIdx.x == 0) L.ncand = 0;
+  for (int k = threadIdx.x; k < P; k += NT) c[k] = Cand{-INFINITY, INT32_MAX};
+  lds_barrier();
+  for_each_elem<E, NT>(x, V, [&](int e, float xv) {
+    if (!in_support(ord_ukey(xv), e, s)) return;
+    const int slot = atomicAdd(&L.ncand, 1);
+    if (slot < P) c[slot] = Cand{xv, e};
+  });
+  lds_barrier();
+  // rank order; the padding (index INT32_MAX, lowest key) sorts last
+  auto before = [](const Cand& a, const Cand& b) {
+    const uint32_t ka = a.idx == INT32_MAX ? 0u : ord_ukey(a.x) + 1u;
+    const uint32_t kb = b.idx == INT32_MAX ? 0u : ord_ukey(b.x) + 1u;
+    return ka > kb || (ka == kb && a.idx < b.idx);
+  };
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t = threadIdx.x; t < P / 2; t += NT) {
+        const int lo = 2 * t - (t & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const Cand a = c[lo], b = c[hi];
+        if (before(b, a) == up) {
+          c[lo] = b;
+          c[hi] = a;
+        }
+      }
+      lds_barrier();
+    }
+  }
+  const int n = min(L.ncand, P);
+  auto mass = [&](int k) -> double {
+    const Cand v = c[k];
+    const double r = weight(v.x, m, T) / s.w - q.q(Elem<E>::at(y, v.idx), v.idx);
+    return r > 0.0 ? r : 0.0;
+  };
+  const int per = (n + NT - 1) / NT;
+  const int k0 = min(n, static_cast<int>(threadIdx.x) * per), k1 = min(n, k0 + per);
+  double seg = 0.0;
+  int mylast = -1;
+  for (int k = k0; k < k1; ++k) {
+    const double r = mass(k);
+    seg += r;
+    if (r > 0.0) mylast = k;
+  }
+  double total;
+  const double incl = block_scan_incl<NT, double>(seg, L.red_d, total);
+  if (!(total > 0.0)) return -1;  // uniform
+  const double target = u * total;
+  if (threadIdx.x == 0) L.bi[3] = INT32_MAX;
+  lds_barrier();
+  if (seg > 0.0 && incl - seg <= target && incl > target) {
+    double run = incl - seg;
+    int pick = -1;
+    for (int k = k0; k < k1; ++k) {
+      const double r = mass(k);
+      if (r > 0.0) {
+        pick = k;
+        run += r;
+        if (run > target) break;
+      }
+    }
+    atomicMin(&L.bi[3], pick);
+  }
+  lds_barrier();
+  int k = L.bi[3];
+  if (k == INT32_MAX) k = block_reduce<NT>(mylast, MaxOp(), L.red_i);  // rounding: the last with mass
+  const int token = c[k].idx;
+  lds_barrier();
+  return token;
+}
+
 }  // namespace
 
 template <typename E, int NT, int U>
@@ -330,7 +414,8 @@ __global__ __launch_bounds__(NT) void verify_probabilistic_kernel(VerifyArgs a, 
           const double pd = in_support(ord_ukey(xd), d, s) ? weight(xd, res.max, Td) / s.w : 0.0;
           accept = ua * q.q(Elem<E>::at(y, d), d) < pd;
         }
-        const int t = residual_draw<E, NT>(row, y, a.V, res.max, Td, s, q, u, L);
+        const int t = s.n <= kCand ? residual_draw_sorted<E, NT>(row, y, a.V, res.max, Td, s, q, u, L)
+                                   : residual_draw<E, NT>(row, y, a.V, res.max, Td, s, q, u, L);
         if (t >= 0) token = t;
       }
     }
