@@ -266,15 +266,13 @@ __device__ int residual_draw(const E* __restrict__ x, const E* __restrict__ y, i
   return block_reduce<NT>(mylast, MaxOp(), L.red_i);
 }
 
-// The residual draw when the survivors fit in the candidate buffer (the
-// usual case: top-p keeps a small head of the order). The survivors are
-// gathered into LDS, sorted into rank order (bitonic, key descending, index
-// ascending), and the first one whose cumulative residual mass exceeds u
-// times the total is found by a block scan over contiguous runs of the
-// sorted list. Same result as residual_draw up to summation order.
+// When the survivors fit in the candidate buffer (the usual case: top-p
+// keeps a small head of the order) they are gathered into LDS and sorted
+// into rank order (bitonic; key descending, index ascending). The own draw
+// and the residual draw are then scans over that list. Returns n, the
+// entries c[0 .. n) of L.c.cand.
 template <typename E, int NT>
-__device__ int residual_draw_sorted(const E* __restrict__ x, const E* __restrict__ y, int V, float m, double T,
-                                    const Support& s, const DraftLaw& q, double u, SampledLds<NT>& L) {
+__device__ int gather_support(const E* __restrict__ x, int V, const Support& s, SampledLds<NT>& L) {
   int P = 1;
   while (P < s.n) P <<= 1;
   Cand* c = L.c.cand;
@@ -308,12 +306,15 @@ __device__ int residual_draw_sorted(const E* __restrict__ x, const E* __restrict
       lds_barrier();
     }
   }
-  const int n = min(L.ncand, P);
-  auto mass = [&](int k) -> double {
-    const Cand v = c[k];
-    const double r = weight(v.x, m, T) / s.w - q.q(Elem<E>::at(y, v.idx), v.idx);
-    return r > 0.0 ? r : 0.0;
-  };
+  return min(L.ncand, P);
+}
+
+// Position of the first of n listed entries whose cumulative mass exceeds u
+// times the list's total (the last entry with mass if rounding leaves the
+// target at the total), or -1 if the list has no mass. A block scan over
+// contiguous runs of the list finds the run; its thread walks it.
+template <int NT, typename Mass>
+__device__ int scan_pick(int n, Mass mass, double u, SampledLds<NT>& L) {
   const int per = (n + NT - 1) / NT;
   const int k0 = min(n, static_cast<int>(threadIdx.x) * per), k1 = min(n, k0 + per);
   double seg = 0.0;
@@ -344,10 +345,9 @@ __device__ int residual_draw_sorted(const E* __restrict__ x, const E* __restrict
   }
   lds_barrier();
   int k = L.bi[3];
-  if (k == INT32_MAX) k = block_reduce<NT>(mylast, MaxOp(), L.red_i);  // rounding: the last with mass
-  const int token = c[k].idx;
+  if (k == INT32_MAX) k = block_reduce<NT>(mylast, MaxOp(), L.red_i);
   lds_barrier();
-  return token;
+  return k;
 }
 
 }  // namespace
@@ -398,9 +398,18 @@ __global__ __launch_bounds__(NT) void verify_probabilistic_kernel(VerifyArgs a, 
     const Support s = support(fl, a.V, top_k, static_cast<double>(top_p), static_cast<double>(min_p));
     double u, ua;
     prob_uniforms(a.seed, a.offset, m.req, m.j, u, ua);
-    Pick own = fl.by_mass(u * s.w, true);
-    if (own.rank >= s.n) own = fl.by_count(s.n);
-    token = own.idx;
+    // survivors listed in rank order when they fit, else whole-row searches
+    const bool listed = s.n <= kCand;
+    const int n = listed ? gather_support<E, NT>(row, a.V, s, L) : 0;
+    const Cand* c = L.c.cand;
+    if (listed) {
+      const int k = scan_pick<NT>(n, [&](int k) { return weight(c[k].x, res.max, Td); }, u, L);
+      token = c[k < 0 ? 0 : k].idx;
+    } else {
+      Pick own = fl.by_mass(u * s.w, true);
+      if (own.rank >= s.n) own = fl.by_count(s.n);
+      token = own.idx;
+    }
     if (m.j < m.K) {
       const E* __restrict__ y = static_cast<const E*>(pa.draft_logits) + static_cast<int64_t>(r - m.req) * pa.dld;
       const double Tdq = (Tq >= 0.f && Tq < INFINITY) ? static_cast<double>(Tq) : 0.0;
@@ -414,8 +423,16 @@ __global__ __launch_bounds__(NT) void verify_probabilistic_kernel(VerifyArgs a, 
           const double pd = in_support(ord_ukey(xd), d, s) ? weight(xd, res.max, Td) / s.w : 0.0;
           accept = ua * q.q(Elem<E>::at(y, d), d) < pd;
         }
-        const int t = s.n <= kCand ? residual_draw_sorted<E, NT>(row, y, a.V, res.max, Td, s, q, u, L)
-                                   : residual_draw<E, NT>(row, y, a.V, res.max, Td, s, q, u, L);
+        int t = -1;
+        if (listed) {
+          const int k = scan_pick<NT>(n, [&](int k) {
+            const double r = weight(c[k].x, res.max, Td) / s.w - q.q(Elem<E>::at(y, c[k].idx), c[k].idx);
+            return r > 0.0 ? r : 0.0;
+          }, u, L);
+          if (k >= 0) t = c[k].idx;
+        } else {
+          t = residual_draw<E, NT>(row, y, a.V, res.max, Td, s, q, u, L);
+        }
         if (t >= 0) token = t;
       }
     }
