@@ -78,28 +78,36 @@ struct Support {
 // top-k survivors (the crossing token kept), min-p cut.
 template <typename E, int NT>
 __device__ Support support(FullLocator<E, NT>& loc, int V, int top_k, double top_p, double min_p) {
+  // `last` is the survivor set's last token whenever a filter has cut it
   int n = V;
   double w;
+  Pick last{};
+  bool have = false;
   if (top_k > 0 && top_k < V) {
     n = top_k;
-    w = loc.by_count(top_k).cum;
+    last = loc.by_count(top_k);
+    w = last.cum;
+    have = true;
   } else {
     w = loc.total_mass();
   }
   if (top_p < 1.0) {
-    const Pick p = loc.by_mass(top_p * w, false);
-    n = p.rank + 1;
-    w = p.cum;
+    last = loc.by_mass(top_p * w, false);
+    n = last.rank + 1;
+    w = last.cum;
+    have = true;
   }
   if (min_p > 0.0) {
     bool exact = false;
     const int lm = loc.count_minp(log(min_p), exact);
     if (lm < n) {
       n = lm > 0 ? lm : 1;
-      w = loc.by_count(n).cum;
+      last = loc.by_count(n);
+      w = last.cum;
+      have = true;
     }
   }
-  const Pick last = loc.by_count(n);
+  if (!have) last = loc.by_count(n);
   return Support{n, w, ord_ukey(loc.at(last.idx)), last.idx};
 }
 
