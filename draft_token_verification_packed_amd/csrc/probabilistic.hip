@@ -31,6 +31,8 @@ namespace vsv {
 
 namespace {
 
+constexpr int kBands = 64;  // bands of z = (x - m) / T, a quarter wide, for the top-p head
+
 // Visits every element e = threadIdx.x + k NT of a row as f(e, value),
 // with the loads of kBatch steps issued before any is used. These loops run
 // over rows already in the caches; with one load per iteration each thread
@@ -279,16 +281,16 @@ __device__ int residual_draw(const E* __restrict__ x, const E* __restrict__ y, i
 // into rank order (bitonic; key descending, index ascending). The own draw
 // and the residual draw are then scans over that list. Returns n, the
 // entries c[0 .. n) of L.c.cand.
-template <typename E, int NT>
-__device__ int gather_support(const E* __restrict__ x, int V, const Support& s, SampledLds<NT>& L) {
+template <typename E, int NT, typename Pred>
+__device__ int gather_sorted(const E* __restrict__ x, int V, int count, Pred keep, SampledLds<NT>& L) {
   int P = 1;
-  while (P < s.n) P <<= 1;
+  while (P < count) P <<= 1;
   Cand* c = L.c.cand;
   if (threadIdx.x == 0) L.ncand = 0;
   for (int k = threadIdx.x; k < P; k += NT) c[k] = Cand{-INFINITY, INT32_MAX};
   lds_barrier();
   for_each_elem<E, NT>(x, V, [&](int e, float xv) {
-    if (!in_support(ord_ukey(xv), e, s)) return;
+    if (!keep(e, xv)) return;
     const int slot = atomicAdd(&L.ncand, 1);
     if (slot < P) c[slot] = Cand{xv, e};
   });
@@ -322,7 +324,8 @@ __device__ int gather_support(const E* __restrict__ x, int V, const Support& s, 
 // target at the total), or -1 if the list has no mass. A block scan over
 // contiguous runs of the list finds the run; its thread walks it.
 template <int NT, typename Mass>
-__device__ int scan_pick(int n, Mass mass, double u, SampledLds<NT>& L) {
+__device__ int scan_pick(int n, Mass mass, double u, SampledLds<NT>& L, bool strict = true, double of = -1.0,
+                         bool last_if_none = true) {
   const int per = (n + NT - 1) / NT;
   const int k0 = min(n, static_cast<int>(threadIdx.x) * per), k1 = min(n, k0 + per);
   double seg = 0.0;
@@ -335,10 +338,11 @@ __device__ int scan_pick(int n, Mass mass, double u, SampledLds<NT>& L) {
   double total;
   const double incl = block_scan_incl<NT, double>(seg, L.red_d, total);
   if (!(total > 0.0)) return -1;  // uniform
-  const double target = u * total;
+  const double target = u * (of < 0.0 ? total : of);
+  auto past = [&](double c) { return strict ? c > target : c >= target; };
   if (threadIdx.x == 0) L.bi[3] = INT32_MAX;
   lds_barrier();
-  if (seg > 0.0 && incl - seg <= target && incl > target) {
+  if (seg > 0.0 && !past(incl - seg) && past(incl)) {
     double run = incl - seg;
     int pick = -1;
     for (int k = k0; k < k1; ++k) {
@@ -346,14 +350,14 @@ __device__ int scan_pick(int n, Mass mass, double u, SampledLds<NT>& L) {
       if (r > 0.0) {
         pick = k;
         run += r;
-        if (run > target) break;
+        if (past(run)) break;
       }
     }
     atomicMin(&L.bi[3], pick);
   }
   lds_barrier();
   int k = L.bi[3];
-  if (k == INT32_MAX) k = block_reduce<NT>(mylast, MaxOp(), L.red_i);
+  if (k == INT32_MAX) k = last_if_none ? block_reduce<NT>(mylast, MaxOp(), L.red_i) : -1;
   lds_barrier();
   return k;
 }
@@ -403,13 +407,66 @@ __global__ __launch_bounds__(NT) void verify_probabilistic_kernel(VerifyArgs a, 
     const double Td = static_cast<double>(T);
     lds_barrier();
     FullLocator<E, NT> fl(L, row, a.V, res.max, Td);
-    const Support s = support(fl, a.V, top_k, static_cast<double>(top_p), static_cast<double>(min_p));
+    const Cand* c = L.c.cand;
+    Support s{0, 0.0, 0u, 0};
+    bool listed = false;
+    if (!(top_k > 0 && top_k < a.V) && top_p < 1.f) {
+      // the top-p cut from a sorted head of the order: one pass for the
+      // total mass and counts per band of z = (x - m) / T, then the widest
+      // head of whole bands that fits the list; the cut is in the list when
+      // the list holds top_p of the total
+      const float mx = res.max;
+      auto band = [&](float xv) {
+        const double z = (static_cast<double>(xv) - static_cast<double>(mx)) / Td;
+        return z > -16.0 ? static_cast<int>(-z * 4.0) : kBands - 1;
+      };
+      for (int b = threadIdx.x; b < kBands; b += NT) L.u.radix.cnt[b] = 0;
+      lds_barrier();
+      double sw = 0.0;
+      for_each_elem<E, NT>(row, a.V, [&](int, float xv) {
+        sw += weight(xv, mx, Td);
+        atomicAdd(&L.u.radix.cnt[min(band(xv), kBands - 1)], 1);
+      });
+      const double W = block_reduce<NT>(sw, SumOp(), L.red_d);
+      if (threadIdx.x == 0) {
+        int cum = 0, top = -1;
+        for (int b = 0; b < kBands && cum + L.u.radix.cnt[b] <= kCand; ++b) {
+          cum += L.u.radix.cnt[b];
+          top = b;
+        }
+        L.bi[0] = top;
+        L.bi[1] = cum;
+      }
+      lds_barrier();
+      const int top = L.bi[0], cnt = L.bi[1];
+      lds_barrier();
+      if (top >= 0 && cnt > 0) {
+        const int nl = gather_sorted<E, NT>(row, a.V, cnt, [&](int, float xv) { return min(band(xv), kBands - 1) <= top; }, L);
+        const int k = scan_pick<NT>(nl, [&](int k) { return weight(c[k].x, mx, Td); },
+                                    static_cast<double>(top_p), L, false, W, false);
+        if (k >= 0) {
+          int n = k + 1;
+          if (min_p > 0.f) {
+            bool exact = false;
+            const int lm = fl.count_minp(log(static_cast<double>(min_p)), exact);
+            if (lm < n) n = lm > 0 ? lm : 1;
+          }
+          double sn = 0.0;
+          for (int q = threadIdx.x; q < n; q += NT) sn += weight(c[q].x, mx, Td);
+          const double w = block_reduce<NT>(sn, SumOp(), L.red_d);
+          s = Support{n, w, ord_ukey(c[n - 1].x), c[n - 1].idx};
+          listed = true;
+        }
+      }
+    }
+    if (!listed) {
+      s = support(fl, a.V, top_k, static_cast<double>(top_p), static_cast<double>(min_p));
+      listed = s.n <= kCand;
+      if (listed) gather_sorted<E, NT>(row, a.V, s.n, [&](int e, float xv) { return in_support(ord_ukey(xv), e, s); }, L);
+    }
+    const int n = s.n;
     double u, ua;
     prob_uniforms(a.seed, a.offset, m.req, m.j, u, ua);
-    // survivors listed in rank order when they fit, else whole-row searches
-    const bool listed = s.n <= kCand;
-    const int n = listed ? gather_support<E, NT>(row, a.V, s, L) : 0;
-    const Cand* c = L.c.cand;
     if (listed) {
       const int k = scan_pick<NT>(n, [&](int k) { return weight(c[k].x, res.max, Td); }, u, L);
       token = c[k < 0 ? 0 : k].idx;
