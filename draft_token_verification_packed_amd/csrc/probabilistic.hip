@@ -130,14 +130,25 @@ struct DraftLaw {
   }
 };
 
-// Returns false when the draft row has a NaN or no finite maximum.
+// One pass over the draft row: each thread keeps a running maximum and the
+// float64 sum of exp((y - max) / Td) rescaled when its maximum grows (for
+// Td = 0, the lowest index of its maximum). Returns false when the row has
+// a NaN or no finite maximum.
 template <typename E, int NT>
 __device__ bool draft_law(const E* __restrict__ y, int V, double Td, SampledLds<NT>& L, DraftLaw& q) {
   float mx = -INFINITY;
-  int nan = 0;
-  for_each_elem<E, NT>(y, V, [&](int, float v) {
-    nan |= (v != v) ? 1 : 0;
-    mx = fmaxf(mx, v);
+  double sum = 0.0;
+  int h = INT32_MAX, nan = 0;
+  for_each_elem<E, NT>(y, V, [&](int e, float v) {
+    if (v != v) {
+      nan = 1;
+    } else if (v > mx) {
+      if (Td > 0.0) sum = sum * exp((static_cast<double>(mx) - static_cast<double>(v)) / Td) + 1.0;
+      mx = v;
+      h = e;
+    } else if (Td > 0.0 && mx > -INFINITY) {
+      sum += exp((static_cast<double>(v) - static_cast<double>(mx)) / Td);
+    }
   });
   nan = block_reduce<NT>(nan, MaxOp(), L.red_i);
   const double md = block_reduce<NT>(static_cast<double>(mx), MaxOp(), L.red_d);
@@ -147,15 +158,11 @@ __device__ bool draft_law(const E* __restrict__ y, int V, double Td, SampledLds<
   q.h = 0;
   if (nan || !(md > -INFINITY) || !(md < INFINITY)) return false;
   if (Td > 0.0) {
-    double s = 0.0;
-    for_each_elem<E, NT>(y, V, [&](int, float v) { s += exp((static_cast<double>(v) - md) / Td); });
-    q.Z = block_reduce<NT>(s, SumOp(), L.red_d);
+    const double part = mx > -INFINITY ? sum * exp((static_cast<double>(mx) - md) / Td) : 0.0;
+    q.Z = block_reduce<NT>(part, SumOp(), L.red_d);
   } else {
-    int h = INT32_MAX;
-    for_each_elem<E, NT>(y, V, [&](int e, float v) {
-      if (v == q.my && e < h) h = e;
-    });
-    q.h = block_reduce<NT>(h, MinOp(), L.red_i);
+    // each thread's first index of its maximum is its lowest (indices grow)
+    q.h = block_reduce<NT>(mx == q.my ? h : INT32_MAX, MinOp(), L.red_i);
   }
   return true;
 }

@@ -31,7 +31,7 @@ def _store(x, dtype):
     return synth.f32_to_bf16_bits(x) if dtype == oracle.BF16 else x.astype(np.float32)
 
 
-def _batch(rng, B, Kmax, V, dtype, sigma=2.5, noise=0.3, params=None, same=False):
+def _batch(rng, B, Kmax, V, dtype, sigma=2.5, noise=0.3, params=None, same=False, ties=False, ninf=0):
     Ks = rng.integers(0, Kmax + 1, B)
     off = np.zeros(B + 1, dtype=np.int32)
     off[1:] = np.cumsum(Ks + 1)
@@ -40,6 +40,12 @@ def _batch(rng, B, Kmax, V, dtype, sigma=2.5, noise=0.3, params=None, same=False
     x = (rng.standard_normal((R, V)) * sigma).astype(np.float32)
     rows = [int(off[i]) + j for i in range(B) for j in range(int(Ks[i]))]   # draft rows, draft order
     y = x[rows] if same else (x[rows] + noise * rng.standard_normal((R - B, V))).astype(np.float32)
+    if ties:      # integer grids: many ties, at the maxima too
+        x = (rng.integers(-6, 7, (R, V)) * 0.5).astype(np.float32)
+        y = (rng.integers(-6, 7, (R - B, V)) * 0.5).astype(np.float32)
+    if ninf:      # every ninf-th draft logit is -inf
+        y = np.array(y, dtype=np.float32)
+        y[:, ::ninf] = -np.inf
     xs, ys = _store(x, dtype), _store(y.reshape(R - B, V), dtype)
     if params is None:
         def params(i):
@@ -163,3 +169,18 @@ def test_flags_and_empty_batch(vsv):
     out = vsv.verify_probabilistic(e, z, ei, ei, e, ef, ei, ef, ef, ef, 0, 0, vocab=16)
     torch.cuda.synchronize()
     assert int(host(out["error_flag"])[0]) == 0
+
+
+def test_tied_maxima_and_minus_inf(vsv):
+    """Draft rows with tied maxima (Td = 0 proposes the lowest arg-max) and
+    draft rows holding -inf logits, against the oracle."""
+    rng = np.random.default_rng(4700)
+    b = _batch(rng, 12, 4, 700, oracle.F32, ties=True,
+               params=lambda i: (float([0.0, 0.8, 1.0][i % 3]), 0, float([1.0, 0.9][i % 2]), 0.0,
+                                 float([0.0, 0.7][i % 2])))
+    print("probabilistic ties R=%d" % int(b["off"][-1]), flush=True)
+    _assert_same(_run(vsv, b, 11, 0), _oracle(b, 11, 0))
+    b = _batch(rng, 10, 4, 1200, oracle.BF16, ninf=7,
+               params=lambda i: (float([0.7, 1.0][i % 2]), 0, 0.9, 0.0, float([0.0, 0.5, 1.0][i % 3])))
+    _assert_same(_run(vsv, b, 12, 1), _oracle(b, 12, 1))
+
