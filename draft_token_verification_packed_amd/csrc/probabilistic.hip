@@ -417,22 +417,25 @@ __global__ __launch_bounds__(NT) void verify_probabilistic_kernel(VerifyArgs a, 
     const Cand* c = L.c.cand;
     Support s{0, 0.0, 0u, 0};
     bool listed = false;
-    if (!(top_k > 0 && top_k < a.V) && top_p < 1.f) {
-      // the top-p cut from a sorted head of the order: one pass for the
-      // total mass and counts per band of z = (x - m) / T, then the widest
-      // head of whole bands that fits the list; the cut is in the list when
-      // the list holds top_p of the total
+    const bool tk = top_k > 0 && top_k < a.V;
+    if (tk ? top_k <= kCand : top_p < 1.f) {
+      // the survivors from a sorted head of the order: one pass counts the
+      // elements in bands of z = (x - m) / T (and, without top-k, takes the
+      // total weight); the widest head of whole bands that fits the list is
+      // gathered and sorted. Bands are monotone in x, so the head is a
+      // prefix of the rank order. It decides when it holds the top-k, or
+      // top_p of the total.
       const float mx = res.max;
       auto band = [&](float xv) {
         const double z = (static_cast<double>(xv) - static_cast<double>(mx)) / Td;
-        return z > -16.0 ? static_cast<int>(-z * 4.0) : kBands - 1;
+        return z > -16.0 ? min(static_cast<int>(-z * 4.0), kBands - 1) : kBands - 1;
       };
       for (int b = threadIdx.x; b < kBands; b += NT) L.u.radix.cnt[b] = 0;
       lds_barrier();
       double sw = 0.0;
       for_each_elem<E, NT>(row, a.V, [&](int, float xv) {
-        sw += weight(xv, mx, Td);
-        atomicAdd(&L.u.radix.cnt[min(band(xv), kBands - 1)], 1);
+        if (!tk) sw += weight(xv, mx, Td);
+        atomicAdd(&L.u.radix.cnt[band(xv)], 1);
       });
       const double W = block_reduce<NT>(sw, SumOp(), L.red_d);
       if (threadIdx.x == 0) {
@@ -447,19 +450,29 @@ __global__ __launch_bounds__(NT) void verify_probabilistic_kernel(VerifyArgs a, 
       lds_barrier();
       const int top = L.bi[0], cnt = L.bi[1];
       lds_barrier();
-      if (top >= 0 && cnt > 0) {
-        const int nl = gather_sorted<E, NT>(row, a.V, cnt, [&](int, float xv) { return min(band(xv), kBands - 1) <= top; }, L);
-        const int k = scan_pick<NT>(nl, [&](int k) { return weight(c[k].x, mx, Td); },
-                                    static_cast<double>(top_p), L, false, W, false);
-        if (k >= 0) {
-          int n = k + 1;
+      if (top >= 0 && cnt >= (tk ? top_k : 1)) {
+        const int nl = gather_sorted<E, NT>(row, a.V, cnt, [&](int, float xv) { return band(xv) <= top; }, L);
+        auto wt = [&](int k) { return weight(c[k].x, mx, Td); };
+        int n = -1;
+        if (tk) {
+          n = top_k;
+          if (top_p < 1.f) {
+            double s1 = 0.0;
+            for (int q = threadIdx.x; q < top_k; q += NT) s1 += wt(q);
+            const double W1 = block_reduce<NT>(s1, SumOp(), L.red_d);
+            n = scan_pick<NT>(top_k, wt, static_cast<double>(top_p), L, false, W1, true) + 1;
+          }
+        } else {
+          n = scan_pick<NT>(nl, wt, static_cast<double>(top_p), L, false, W, false) + 1;
+        }
+        if (n > 0) {
           if (min_p > 0.f) {
             bool exact = false;
             const int lm = fl.count_minp(log(static_cast<double>(min_p)), exact);
             if (lm < n) n = lm > 0 ? lm : 1;
           }
           double sn = 0.0;
-          for (int q = threadIdx.x; q < n; q += NT) sn += weight(c[q].x, mx, Td);
+          for (int q = threadIdx.x; q < n; q += NT) sn += wt(q);
           const double w = block_reduce<NT>(sn, SumOp(), L.red_d);
           s = Support{n, w, ord_ukey(c[n - 1].x), c[n - 1].idx};
           listed = true;
