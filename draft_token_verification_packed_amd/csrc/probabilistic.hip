@@ -15,14 +15,16 @@
 // speculative inference", DSpark section "Launch example"): their point-mass
 // drafts, which the sampled path verifies, are its special case.
 //
-// How: correctness first, not speed. One workgroup per row streams the
-// target row for its maximum and arg-max. A sampled row then settles its
-// survivor set and own draw with the sampled path's exact whole-row radix
-// locator (several passes over the row, which stays in the caches), reads
-// the draft row for its maximum and exponent sum, and locates the residual
-// draw by a radix descent over the target's keys weighted by max(0, p - q),
-// then by index inside the located key. Each row stores a tagged word; the
-// workgroup that finishes last runs the per-request scan.
+// How: exact first. One workgroup per row streams the target row for its
+// maximum and arg-max. A sampled row then gathers a head of its rank order
+// (whole bands of z = (x - m) / T, up to 4096 entries) into LDS and sorts
+// it; when that head decides the top-k / top-p cut, the survivor set, the
+// own draw and the residual draw of max(0, p - q) are block scans over the
+// sorted list. Otherwise the sampled path's exact whole-row radix locator
+// settles them (several passes over the row, which stays in the caches).
+// The draft row is read once for its maximum and exponent sum. Each row
+// stores a tagged word; the workgroup that finishes last runs the
+// per-request scan.
 #include "probabilistic.hpp"
 #include "sampled_row.hpp"
 #include "verify_common.hpp"
