@@ -157,8 +157,9 @@ vsv_status vsv_verify_sampled(const vsv_batch* batch, const float* temperature,
  * of max(0, p - q) in rank order at u (its own draw from p if that residual
  * has no mass); a request whose drafts all pass emits the bonus row's draw.
  * row_token holds each row's emitted-if-first-rejected token (the bonus
- * row's own draw); row_lse and slow_rows are not written. Correctness first:
- * each sampled row takes several passes over its target and draft rows.
+ * row's own draw); row_lse and slow_rows are not written. Exact, not yet
+ * tuned: each sampled row takes several passes over its target row and one
+ * over its draft row.
  * Workspace: vsv_workspace_bytes(B, R, 0) or more.
  * Errors: as vsv_verify_sampled, plus VSV_EINVAL for NULL draft rows (when
  * R > B) or draft temperatures, draft_ld < vocab or misaligned draft rows.
