@@ -159,23 +159,49 @@ def workspace_bytes(num_requests, num_rows, sampled=False):
 _ws_cache = {}
 
 
+def _resolve_stream(stream, device=None):
+    if stream is not None:
+        return stream
+    return torch.cuda.current_stream(device)
+
+
 def workspace(num_requests, num_rows, sampled=False, device=None, stream=None):
     """A zeroed workspace tensor, cached per (device, stream) and grown on demand.
 
-    Calls on one stream run in order and each leaves the workspace zeroed, so
-    the cached buffer is safe to reuse for later calls on that stream.
+    The buffer is allocated and zero-filled on the stream the calls run on,
+    so the fill is ordered before them and the caching allocator hands its
+    memory to no other stream. Calls on one stream run in order and each
+    leaves the workspace ready for the next, so the cached buffer serves
+    every later call on that stream. Calls that may overlap need workspaces
+    of their own (pass `ws`).
     """
     need = workspace_bytes(num_requests, num_rows, sampled)
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
-    key = (dev.index, _stream(stream).value)
+    s = _resolve_stream(stream, dev)
+    key = (dev.index, s.cuda_stream)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.zeros(max(need, 4096), dtype=torch.uint8, device=dev)
+        size = max(need, 4096)
+        size = (size + 3) // 4 * 4
+        with torch.cuda.stream(s):
+            ws = torch.empty(size, dtype=torch.uint8, device=dev)
+        _check(lib().vsv_workspace_init(_ptr(ws), ws.numel(), ctypes.c_void_p(s.cuda_stream)))
         _ws_cache[key] = ws
     return ws
 
 
-def _prepare(logits, row_offsets, row_owner, draft_tokens, vocab):
+def _keep_alive(stream, *tensors):
+    """Tell the caching allocator that `tensors` are used on `stream` when it
+    is not the current stream, so their memory is not reused before the
+    stream's work on them is done."""
+    if stream is None or stream == torch.cuda.current_stream(stream.device):
+        return
+    for t in tensors:
+        if t is not None and t.is_cuda:
+            t.record_stream(stream)
+
+
+def _prepare(logits, row_offsets, row_owner, draft_tokens, vocab, stream=None):
     dtype, V, ld = _logits(logits, vocab)
     R = logits.shape[0]
     B = row_offsets.numel() - 1
@@ -184,7 +210,26 @@ def _prepare(logits, row_offsets, row_owner, draft_tokens, vocab):
     if R - B > 0:
         _vec(draft_tokens, R - B, torch.int32, "draft_tokens")
     dev = logits.device
-    out = dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
+    # outputs are allocated (and the ones with a fill are filled) on the
+    # stream the call runs on, so the fills are ordered before the kernels
+    with torch.cuda.stream(_resolve_stream(stream, dev)):
+        out = _new_outputs(B, R, dev)
+    batch = Batch(_ptr(logits), dtype, V, ld, B, R, _ptr(row_offsets), _ptr(row_owner),
+                  _ptr(draft_tokens) if R - B > 0 else None)
+    outs = _outputs_struct(out)
+    return batch, outs, out, B, R
+
+
+_OUT_KEYS = ("accepted_len", "next_token", "out_offsets", "out_tokens", "row_token", "row_lse", "error_flag",
+             "slow_rows")
+
+
+def _outputs_struct(out):
+    return Outputs(*[_ptr(out[k]) for k in _OUT_KEYS])
+
+
+def _new_outputs(B, R, dev):
+    return dict(accepted_len=torch.empty(B, dtype=torch.int32, device=dev),
                next_token=torch.empty(B, dtype=torch.int32, device=dev),
                out_offsets=torch.empty(B + 1, dtype=torch.int32, device=dev),
                out_tokens=torch.full((max(R, 1),), -1, dtype=torch.int32, device=dev),
@@ -192,18 +237,14 @@ def _prepare(logits, row_offsets, row_owner, draft_tokens, vocab):
                row_lse=torch.empty(R, dtype=torch.float32, device=dev),
                error_flag=torch.zeros(1, dtype=torch.int32, device=dev),
                slow_rows=torch.zeros(1, dtype=torch.int32, device=dev))
-    batch = Batch(_ptr(logits), dtype, V, ld, B, R, _ptr(row_offsets), _ptr(row_owner),
-                  _ptr(draft_tokens) if R - B > 0 else None)
-    outs = Outputs(*[_ptr(out[k]) for k in ("accepted_len", "next_token", "out_offsets", "out_tokens",
-                                            "row_token", "row_lse", "error_flag", "slow_rows")])
-    return batch, outs, out, B, R
 
 
 def verify_greedy(logits, row_offsets, row_owner, draft_tokens, relaxed_topk=1, vocab=None,
                   ws=None, stream=None):
     """Greedy verification of a packed batch; returns a dict of device tensors."""
-    batch, outs, out, B, R = _prepare(logits, row_offsets, row_owner, draft_tokens, vocab)
+    batch, outs, out, B, R = _prepare(logits, row_offsets, row_owner, draft_tokens, vocab, stream)
     ws = workspace(B, R, False, logits.device, stream) if ws is None else ws
+    _keep_alive(stream, logits, row_offsets, row_owner, draft_tokens, ws)
     _check(lib().vsv_verify_greedy(ctypes.byref(batch), int(relaxed_topk), ctypes.byref(outs),
                                    _ptr(ws), ws.numel(), _stream(stream)))
     return out
@@ -212,12 +253,13 @@ def verify_greedy(logits, row_offsets, row_owner, draft_tokens, relaxed_topk=1, 
 def verify_sampled(logits, row_offsets, row_owner, draft_tokens, temperature, top_k, top_p, min_p,
                    seed, offset=0, vocab=None, ws=None, stream=None):
     """Sampled / mixed verification of a packed batch; returns a dict of device tensors."""
-    batch, outs, out, B, R = _prepare(logits, row_offsets, row_owner, draft_tokens, vocab)
+    batch, outs, out, B, R = _prepare(logits, row_offsets, row_owner, draft_tokens, vocab, stream)
     _vec(temperature, B, torch.float32, "temperature")
     _vec(top_k, B, torch.int32, "top_k")
     _vec(top_p, B, torch.float32, "top_p")
     _vec(min_p, B, torch.float32, "min_p")
     ws = workspace(B, R, True, logits.device, stream) if ws is None else ws
+    _keep_alive(stream, logits, row_offsets, row_owner, draft_tokens, temperature, top_k, top_p, min_p, ws)
     _check(lib().vsv_verify_sampled(ctypes.byref(batch), _ptr(temperature), _ptr(top_k), _ptr(top_p),
                                     _ptr(min_p), int(seed) & (2**64 - 1), int(offset) & (2**64 - 1),
                                     ctypes.byref(outs), _ptr(ws), ws.numel(), _stream(stream)))
@@ -229,7 +271,7 @@ def verify_probabilistic(logits, row_offsets, row_owner, draft_tokens, draft_log
     """Rejection-sampling verification with probabilistic drafts; draft_logits
     holds the R - B draft rows in the draft tokens' layout. Returns a dict of
     device tensors (row_lse and slow_rows are not written)."""
-    batch, outs, out, B, R = _prepare(logits, row_offsets, row_owner, draft_tokens, vocab)
+    batch, outs, out, B, R = _prepare(logits, row_offsets, row_owner, draft_tokens, vocab, stream)
     for t, n in ((temperature, "temperature"), (top_p, "top_p"), (min_p, "min_p"),
                  (draft_temperature, "draft_temperature")):
         _vec(t, B, torch.float32, n)
@@ -242,6 +284,8 @@ def verify_probabilistic(logits, row_offsets, row_owner, draft_tokens, draft_log
             raise ValueError("draft_logits must be [R - B, >= vocab] of the logits' dtype")
         dld = draft_logits.stride(0) if draft_logits.shape[0] > 1 else max(draft_logits.shape[1], 1)
     ws = workspace(B, R, False, logits.device, stream) if ws is None else ws
+    _keep_alive(stream, logits, row_offsets, row_owner, draft_tokens, draft_logits, temperature, top_k, top_p,
+                min_p, draft_temperature, ws)
     _check(lib().vsv_verify_probabilistic(ctypes.byref(batch), _ptr(draft_logits) if R - B > 0 else None, int(dld),
                                           _ptr(temperature), _ptr(top_k), _ptr(top_p), _ptr(min_p),
                                           _ptr(draft_temperature), int(seed) & (2**64 - 1),
@@ -257,9 +301,11 @@ def draft_confidence(draft_logits, selected=None, vocab=None, stream=None):
     if selected is not None:
         _vec(selected, D, torch.int32, "selected")
     dev = draft_logits.device
-    conf = torch.empty(D, dtype=torch.float32, device=dev)
-    lse = torch.empty(D, dtype=torch.float32, device=dev)
-    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    with torch.cuda.stream(_resolve_stream(stream, dev)):
+        conf = torch.empty(D, dtype=torch.float32, device=dev)
+        lse = torch.empty(D, dtype=torch.float32, device=dev)
+        flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    _keep_alive(stream, draft_logits, selected)
     _check(lib().vsv_draft_confidence(_ptr(draft_logits), dtype, V, ld, D, _ptr(selected), _ptr(conf),
                                       _ptr(lse), _ptr(flag), _stream(stream)))
     return conf, lse, flag
@@ -294,7 +340,9 @@ def allocate_verify(confidence, draft_tokens, num_requests, num_drafts, row_budg
     """
     B, K, G = int(num_requests), int(num_drafts), int(row_budget)
     dev = confidence.device if confidence is not None else torch.device("cuda", torch.cuda.current_device())
-    out = _alloc_outputs(B, K, G, dev, draft_tokens is not None)
+    with torch.cuda.stream(_resolve_stream(stream, dev)):
+        out = _alloc_outputs(B, K, G, dev, draft_tokens is not None)
+    _keep_alive(stream, confidence, draft_tokens)
     _check(lib().vsv_allocate_verify(*_alloc_args(confidence, draft_tokens, B, K, G, out, stream)))
     return out
 
@@ -367,27 +415,27 @@ class PreparedCall:
 
 def prepare_greedy(logits, row_offsets, row_owner, draft_tokens, relaxed_topk=1, vocab=None,
                    out=None, ws=None, stream=None):
-    batch, outs, res, B, R = _prepare(logits, row_offsets, row_owner, draft_tokens, vocab)
+    batch, outs, res, B, R = _prepare(logits, row_offsets, row_owner, draft_tokens, vocab, stream)
     if out is not None:
         res = out
-        outs = Outputs(*[_ptr(res[k]) for k in ("accepted_len", "next_token", "out_offsets", "out_tokens",
-                                                "row_token", "row_lse", "error_flag", "slow_rows")])
+        outs = _outputs_struct(res)
     ws = workspace(B, R, False, logits.device, stream) if ws is None else ws
+    _keep_alive(stream, logits, row_offsets, row_owner, draft_tokens, ws)
     args = (ctypes.byref(batch), int(relaxed_topk), ctypes.byref(outs), _ptr(ws), ws.numel(), _stream(stream))
     return PreparedCall(lib().vsv_verify_greedy, args, (batch, outs, res, ws, logits)), res
 
 
 def prepare_sampled(logits, row_offsets, row_owner, draft_tokens, temperature, top_k, top_p, min_p,
                     seed, offset=0, vocab=None, out=None, ws=None, stream=None):
-    batch, outs, res, B, R = _prepare(logits, row_offsets, row_owner, draft_tokens, vocab)
+    batch, outs, res, B, R = _prepare(logits, row_offsets, row_owner, draft_tokens, vocab, stream)
     if out is not None:
         res = out
-        outs = Outputs(*[_ptr(res[k]) for k in ("accepted_len", "next_token", "out_offsets", "out_tokens",
-                                                "row_token", "row_lse", "error_flag", "slow_rows")])
+        outs = _outputs_struct(res)
     for t, dt, name in ((temperature, torch.float32, "temperature"), (top_k, torch.int32, "top_k"),
                         (top_p, torch.float32, "top_p"), (min_p, torch.float32, "min_p")):
         _vec(t, B, dt, name)
     ws = workspace(B, R, True, logits.device, stream) if ws is None else ws
+    _keep_alive(stream, logits, row_offsets, row_owner, draft_tokens, temperature, top_k, top_p, min_p, ws)
     args = (ctypes.byref(batch), _ptr(temperature), _ptr(top_k), _ptr(top_p), _ptr(min_p),
             int(seed) & (2**64 - 1), int(offset) & (2**64 - 1), ctypes.byref(outs), _ptr(ws), ws.numel(),
             _stream(stream))

@@ -14,9 +14,15 @@
  *
  * Conventions shared by every entry point:
  *  - Every data pointer is a caller-owned DEVICE pointer unless stated. The
- *    library allocates nothing and keeps no state between calls; calls are
- *    reentrant and may run concurrently on different streams as long as they
- *    use different workspaces and outputs.
+ *    library allocates nothing. What carries over from one verify call to
+ *    the next lives in the caller's workspace (see vsv_workspace_bytes): a
+ *    call counter, the row queue of sampled verification, and tagged words
+ *    through which workgroups hand results to the batch scan. The workspace
+ *    is zero-filled once before its first use and every call leaves it
+ *    ready for the next; one workspace serves one call at a time, so calls
+ *    that may overlap in time (on different streams) need workspaces and
+ *    outputs of their own. The host side keeps only a per-device cache of
+ *    the CU count.
  *  - All work is enqueued on `stream` (0 = the null stream). Nothing is
  *    synchronised and nothing is read back to the host; results are valid
  *    once the stream reaches them.
