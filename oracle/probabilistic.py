@@ -86,6 +86,36 @@ def residual_draw(x, p, q, u):
     return int(order[n])
 
 
+def row_margins(x, y, temperature, top_k, top_p, min_p, draft_temperature, d, u, u_acc):
+    """Distances of a draft row's two float decisions from their thresholds
+    (used to re-draw synthetic rows whose outcome would hinge on rounding).
+
+    Returns (accept_margin, residual_margin):
+    * accept_margin: |p(d) - u_acc q(d)| relative to the larger of the two,
+      inf when p(d) = 0 or q(d) = 0 (the test is then exact);
+    * residual_margin: how far, in probability mass, u times the residual
+      total lies from the nearest cumulative boundary of max(0, p - q) in
+      rank order; inf when the residual has no mass (the row then emits its
+      own draw, whose margin is the sampled path's).
+    The filters' own cuts are the sampled path's margins."""
+    p = target_probs(x, temperature, top_k, top_p, min_p)
+    q = draft_probs(y, draft_temperature)
+    accept_margin = np.inf
+    if 0 <= d < x.shape[0] and p[d] > 0 and q[d] > 0:
+        a, b = p[d], u_acc * q[d]
+        accept_margin = abs(a - b) / max(a, b)
+    residual = np.clip(p - q, 0.0, None)
+    c = np.cumsum(residual[rank_order(x)])
+    residual_margin = np.inf
+    if c[-1] > 0:
+        t = u * c[-1]
+        n = int(np.flatnonzero(c > t)[0])
+        residual_margin = c[n] - t
+        if n > 0:
+            residual_margin = min(residual_margin, t - c[n - 1])
+    return float(accept_margin), float(residual_margin)
+
+
 def row_uniforms(seed, request, row, offset):
     """(u, u_acc): words 0 and 1 of the Philox block of (request, row)."""
     seed, offset = int(seed), int(offset)

@@ -28,11 +28,17 @@ VOCAB = 152064
 
 
 def f32_to_bf16_bits(a):
-    """Round float32 to bfloat16 (nearest, ties to even); returns uint16 bits."""
+    """Round float32 to bfloat16 (nearest, ties to even); returns uint16 bits.
+
+    The upper half rounds up when the lower half is above one half, or
+    exactly one half with an odd upper half (a carry out of the top wraps,
+    as only NaN patterns can carry that far)."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    rounded = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
-    return rounded.astype(np.uint16)
+    u = a.view(np.uint32)
+    hi = u >> np.uint32(16)
+    lo = u & np.uint32(0xFFFF)
+    up = (lo + (hi & np.uint32(1))) > np.uint32(0x8000)
+    return (hi + up).astype(np.uint16)
 
 
 @dataclass
@@ -223,19 +229,37 @@ def make(key, *, B=None, V=None, K=None, ld=None, seed=None, pad=False,
                             for i in range(Bn)], dtype=np.int32)
         wl.planted = planted
 
-    for r in range(R):
-        _fill_row(wl, r)
+    _for_each(R, lambda r: _fill_row(wl, r))
 
     if spec.get("confidence"):
         D = R - Bn
         dl = np.empty((D, ld), dtype=wl.logits.dtype)
-        for q in range(D):
+
+        def draft_row(q):
             gq = _row_stream(seed, 4, q, 0)
             y = (gq.standard_normal(Vn, dtype=np.float32) * np.float32(spec["sigma"])).astype(np.float32)
             dl[q] = _store(spec, y, ld, pad)
+
+        _for_each(D, draft_row)
         wl.draft_logits = dl
         wl.selected = wl.drafts.copy()
     return wl
+
+
+def _for_each(n, fn):
+    """fn(0) .. fn(n - 1) on a few threads. Every row draws from its own
+    stream and writes only its own slots, so the result does not depend on
+    the order; NumPy releases the interpreter lock in the bulk work."""
+    import concurrent.futures
+    import os
+    workers = min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 4)
+    if n < 64 or workers < 2:
+        for k in range(n):
+            fn(k)
+        return
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        for _ in ex.map(fn, range(n), chunksize=16):
+            pass
 
 
 def _fill_row(wl, r):

@@ -183,37 +183,3 @@ def test_tied_maxima_and_minus_inf(vsv):
     b = _batch(rng, 10, 4, 1200, oracle.BF16, ninf=7,
                params=lambda i: (float([0.7, 1.0][i % 2]), 0, 0.9, 0.0, float([0.0, 0.5, 1.0][i % 3])))
     _assert_same(_run(vsv, b, 12, 1), _oracle(b, 12, 1))
-
-
-
-def test_large_mixed_full_size_requests(vsv):
-    """The full mixed batch (B=512, K=7, V=152064 bf16; even requests greedy,
-    odd ones T = 0.7, top_p 0.95) as the benchmark launches it, each draft
-    row the draft law at the request's temperature; 16 requests re-checked
-    one by one against the oracle."""
-    import torch
-    from oracle.probabilistic import row_uniforms
-    wl = synth.make("mixed")
-    td = wl.temperature.astype(np.float32)
-    out = vsv.verify_probabilistic(to_dev(wl.logits), to_dev(wl.offsets), to_dev(wl.owner), to_dev(wl.drafts),
-                                   to_dev(wl.draft_logits), to_dev(wl.temperature), to_dev(wl.top_k),
-                                   to_dev(wl.top_p), to_dev(wl.min_p), to_dev(td), wl.seed, wl.offset, vocab=wl.V)
-    torch.cuda.synchronize()
-    acc, nxt, rt = host(out["accepted_len"]), host(out["next_token"]), host(out["row_token"])
-    offs, toks = host(out["out_offsets"]), host(out["out_tokens"])
-    rng = np.random.default_rng(56)
-    for i in sorted(rng.choice(wl.B, size=16, replace=False).tolist()):
-        r0, r1 = int(wl.offsets[i]), int(wl.offsets[i + 1])
-        us = {(0, j): row_uniforms(wl.seed, i, j, wl.offset) for j in range(r1 - r0)}
-        sl = slice(i, i + 1)
-        ref = verify_probabilistic(wl.logits[r0:r1], wl.dtype, wl.V, np.array([0, r1 - r0]), None,
-                                   wl.drafts[r0 - i:r1 - i - 1], wl.draft_logits[r0 - i:r1 - i - 1],
-                                   wl.temperature[sl], wl.top_k[sl], wl.top_p[sl], wl.min_p[sl], td[sl],
-                                   wl.seed, wl.offset, uniforms=us)
-        assert acc[i] == ref["accepted_len"][0], i
-        assert nxt[i] == ref["next_token"][0], i
-        assert np.array_equal(rt[r0:r1], ref["row_token"]), i
-        n = int(ref["out_offsets"][1])
-        assert np.array_equal(toks[offs[i]:offs[i] + n], ref["out_tokens"]), i
-    assert int(offs[-1]) == int(acc.sum()) + wl.B
-    assert int(host(out["error_flag"])[0]) == 0

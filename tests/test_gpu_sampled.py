@@ -59,39 +59,6 @@ def test_large_mixed_batch(vsv, B):
     assert int(host(out["slow_rows"])[0]) <= max(1, sampled_rows // 20)
 
 
-def test_large_mixed_full_size_sampled_requests(vsv):
-    """The full mixed batch (B=512, K=7, V=152064 bf16) on the GPU; 24 requests
-    re-checked one by one against the oracle."""
-    wl = synth.make("mixed")
-    rng = np.random.default_rng(55)
-    check = sorted(rng.choice(wl.B, size=24, replace=False).tolist())
-    rows = [r for i in check for r in range(int(wl.offsets[i]), int(wl.offsets[i + 1]))]
-    from tests.workloads import margin_rows
-    for _ in range(20):
-        bad = margin_rows(wl, rows)
-        if not bad:
-            break
-        synth.redraw_rows(wl, bad)
-    out = run_sampled(vsv, wl)
-    acc, nxt, rt = host(out["accepted_len"]), host(out["next_token"]), host(out["row_token"])
-    offs, toks, lse = host(out["out_offsets"]), host(out["out_tokens"]), host(out["row_lse"])
-    for i in check:
-        r0, r1 = int(wl.offsets[i]), int(wl.offsets[i + 1])
-        sub = wl.logits[r0:r1]
-        us = {(0, j): oracle.row_uniform(wl.seed, i, j, wl.offset) for j in range(r1 - r0)}
-        ref = oracle.verify_sampled(sub, wl.dtype, wl.V, np.array([0, r1 - r0]), None,
-                                    wl.drafts[r0 - i:r1 - i - 1], wl.temperature[i:i + 1], wl.top_k[i:i + 1],
-                                    wl.top_p[i:i + 1], wl.min_p[i:i + 1], wl.seed, wl.offset, uniforms=us)
-        assert acc[i] == ref["accepted_len"][0]
-        assert nxt[i] == ref["next_token"][0]
-        assert np.array_equal(rt[r0:r1], ref["row_token"])
-        assert_lse_close(lse[r0:r1], ref["row_lse"])
-        n = int(ref["out_offsets"][1])
-        assert np.array_equal(toks[offs[i]:offs[i] + n], ref["out_tokens"])
-    assert int(offs[-1]) == int(acc.sum()) + wl.B
-    assert int(host(out["error_flag"])[0]) == 0
-
-
 def test_temperature_zero_is_greedy(vsv):
     import torch
     wl = synth.make("mixed", B=16)

@@ -145,6 +145,18 @@ MUTANTS = [
     ("goodput_counts_inclusive", "goodput.py",
      "accepted = np.array([int((a > j).sum())",
      "accepted = np.array([int((a >= j).sum())"),
+    ("margin_topp_farther_boundary", "verify.py",
+     "topp_margin = min(topp_margin, top_p - cn[L - 1])",
+     "topp_margin = max(topp_margin, top_p - cn[L - 1])"),
+    ("margin_minp_all_tokens", "verify.py",
+     "zs = z[S][x[S] < m]",
+     "zs = z[x < m]"),
+    ("margin_accept_smaller_side", "probabilistic.py",
+     "accept_margin = abs(a - b) / max(a, b)",
+     "accept_margin = abs(a - b) / min(a, b)"),
+    ("margin_residual_normalised", "probabilistic.py",
+     "        residual_margin = c[n] - t\n",
+     "        residual_margin = (c[n] - t) / c[-1]\n"),
 ]
 
 

@@ -418,3 +418,77 @@ def test_margins_are_consistent_with_decisions():
         t0 = oracle.sample_from_u(x, *params, u)
         assert oracle.sample_from_u(x, *params, u + 0.5 * um) == t0
         assert oracle.sample_from_u(x, *params, u - 0.5 * um) == t0
+
+
+def _survivors(x, T, k, p, mp):
+    return oracle.filtered_support(x, T, k, p, mp)[0].tolist()
+
+
+def test_topp_margin_is_the_distance_to_the_nearest_cut():
+    """Moving top_p by half its margin keeps the survivor set; moving it just
+    past the margin, toward the boundary the margin measures, changes it."""
+    rng = np.random.default_rng(140)
+    checked = 0
+    for trial in range(60):
+        V = int(rng.integers(8, 200))
+        x = rng.standard_normal(V) * float(rng.choice([1.0, 2.5, 4.0]))
+        T = float(rng.choice([0.5, 0.7, 1.0, 1.6]))
+        k = int(rng.choice([0, 5, 20]))
+        p = float(rng.uniform(0.05, 0.98))
+        tp, _, _ = oracle.sampled_row_margins(x, T, k, p, 0.0, 0.5)
+        assert 0 <= tp < 1
+        S = _survivors(x, T, k, p, 0.0)
+        assert _survivors(x, T, k, p + 0.5 * tp, 0.0) == S
+        assert _survivors(x, T, k, p - 0.5 * tp, 0.0) == S
+        moved = [_survivors(x, T, k, q, 0.0) for q in (p + tp + 1e-9, p - tp - 1e-9) if 0 < q < 1]
+        if not any(m != S for m in moved):
+            # the cut is at the last top-k token: the nearest boundary is the
+            # whole mass, which top_p cannot pass (top_p >= 1 is "off")
+            assert p + tp == pytest.approx(1.0, abs=1e-12), (trial, p, tp)
+            continue
+        checked += 1
+    assert checked > 40
+
+
+def test_minp_margin_is_the_distance_to_the_nearest_z():
+    """Moving ln(min_p) by half its margin keeps the survivor set; moving it
+    just past the margin, toward the z the margin measures, changes it."""
+    rng = np.random.default_rng(141)
+    for trial in range(60):
+        V = int(rng.integers(8, 200))
+        x = rng.standard_normal(V) * 2.5
+        T = float(rng.choice([0.5, 1.0, 1.5]))
+        k = int(rng.choice([0, 30]))
+        p = float(rng.choice([1.0, 0.95]))
+        mp = float(rng.uniform(0.01, 0.6))
+        _, _, mm = oracle.sampled_row_margins(x, T, k, p, mp, 0.5)
+        S = _survivors(x, T, k, p, mp)
+        if not np.isfinite(mm):
+            # only the maximum's ties are top-p survivors: min-p cannot cut
+            assert len(set(x[S].tolist())) == 1
+            continue
+        lm = math.log(mp)
+        for s_ in (0.5, -0.5):
+            if lm + s_ * mm <= 0.0:       # min_p above 1 is out of range
+                assert _survivors(x, T, k, p, math.exp(lm + s_ * mm)) == S
+        moved = [_survivors(x, T, k, p, math.exp(lm + s * (mm + 1e-9))) for s in (1, -1)
+                 if math.exp(lm + s * (mm + 1e-9)) <= 1.0]
+        assert any(m != S for m in moved), (trial, mp, mm)
+
+
+def test_margins_for_top_k_then_top_p_then_min_p():
+    """All three margins on one row where every filter cuts: each is the
+    distance the pins above define, taken after the filters before it."""
+    x = np.array([3.0, 2.0, 2.0, 1.0, 0.5, 0.0, -1.0, -3.0])
+    T, k, p, mp = 1.0, 6, 0.8, 0.3
+    tp, um, mm = oracle.sampled_row_margins(x, T, k, p, mp, 0.25)
+    w = np.exp(x - 3.0)
+    c = np.cumsum(w[:6]) / np.sum(w[:6])         # ranks 0..5 after top-k
+    L = int(np.flatnonzero(c >= p)[0])
+    assert tp == pytest.approx(min(c[L] - p, p - c[L - 1]), rel=1e-12)
+    zs = (x[:L + 1] - 3.0)[1:]                    # top-p survivors below the max
+    assert mm == pytest.approx(float(np.min(np.abs(zs - math.log(mp)))), rel=1e-12)
+    S = [t for t in range(L + 1) if x[t] - 3.0 >= math.log(mp)]
+    cs = np.cumsum(w[S]) / np.sum(w[S])
+    n = int(np.flatnonzero(cs > 0.25)[0])
+    assert um == pytest.approx(min(cs[n] - 0.25, 0.25 - cs[n - 1]) if n else cs[n] - 0.25, rel=1e-12)

@@ -129,3 +129,44 @@ def test_batch_worked_by_hand():
     out = verify_probabilistic(logits, oracle.F32, 4, off, owner, drafts, dlog, [1.0, 1.0], [0, 0], [1.0, 1.0],
                                [0.0, 0.0], [1.0, 1.0], 0, 0, uniforms=U)
     assert list(out["accepted_len"]) == [2, 2]
+
+
+def test_probabilistic_margins_bound_the_decisions():
+    """Moving u_acc by half the acceptance margin (relative) keeps the
+    acceptance; moving it just past flips it. Moving u by half the residual
+    margin (in residual mass) keeps the residual draw; just past changes it."""
+    from oracle.probabilistic import accepts, residual_draw, row_margins
+    rng = np.random.default_rng(4800)
+    flips = draws = 0
+    for trial in range(80):
+        V = int(rng.integers(6, 120))
+        x = rng.standard_normal(V) * 2.0
+        y = x + 0.8 * rng.standard_normal(V)
+        T, k, tp, mp = float(rng.choice([0.7, 1.0])), int(rng.choice([0, 10])), float(rng.choice([1.0, 0.9])), 0.0
+        Td = float(rng.choice([0.7, 1.0]))
+        p = target_probs(x, T, k, tp, mp)
+        q = draft_probs(y, Td)
+        d = int(rng.choice(V, p=q))
+        u, ua = float(rng.uniform(0.01, 0.99)), float(rng.uniform(0.01, 0.99))
+        am, rm = row_margins(x, y, T, k, tp, mp, Td, d, u, ua)
+        if np.isfinite(am):
+            ok = accepts(p, q, d, ua)
+            # ua * q(d) moves by the margin's share of the larger side
+            step = am * max(p[d], ua * q[d]) / q[d]
+            assert accepts(p, q, d, ua + 0.5 * step) == ok and accepts(p, q, d, ua - 0.5 * step) == ok
+            toward = ua + step * (1 + 1e-9) if ok else ua - step * (1 + 1e-9)
+            assert accepts(p, q, d, toward) != ok, trial
+            flips += 1
+        if np.isfinite(rm):
+            tot = float(np.sum(np.maximum(p - q, 0.0)))
+            t0 = residual_draw(x, p, q, u)
+            du = rm / tot
+            assert residual_draw(x, p, q, u + 0.5 * du) == t0 and residual_draw(x, p, q, u - 0.5 * du) == t0
+            moved = [residual_draw(x, p, q, v) for v in (u + du * (1 + 1e-9), u - du * (1 + 1e-9)) if 0 <= v < 1]
+            if not any(m != t0 for m in moved):
+                # the nearest boundary is 0 or the whole residual mass, which
+                # no u in [0, 1) passes
+                assert min(abs(u + du - 1.0), abs(u - du)) < 1e-9, trial
+                continue
+            draws += 1
+    assert flips > 40 and draws > 40
