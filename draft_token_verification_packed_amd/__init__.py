@@ -7,6 +7,7 @@ library is missing or cannot be loaded, every call raises.
 
 Entry points mirror the C ABI in include/vspec_verify.h:
     verify_greedy(logits, row_offsets, row_owner, draft_tokens, relaxed_topk=1)
+    verify_greedy_static(logits, row_offsets, row_owner, draft_tokens, relaxed_topk=1)
     verify_sampled(logits, row_offsets, row_owner, draft_tokens,
                    temperature, top_k, top_p, min_p, seed, offset=0)
     draft_confidence(draft_logits, selected=None)
@@ -30,7 +31,10 @@ FLAG_TOKEN = 2
 FLAG_LOGITS = 4
 FLAG_PARAMS = 8
 
-_STATUS = {0: "VSV_OK", 1: "VSV_EINVAL", 2: "VSV_EUNSUPPORTED", 3: "VSV_EWORKSPACE", 4: "VSV_EHIP"}
+_STATUS = {0: "VSV_OK", 1: "VSV_EINVAL", 2: "VSV_EUNSUPPORTED", 3: "VSV_EWORKSPACE", 4: "VSV_EHIP",
+           5: "VSV_ELIMIT"}
+VSV_ELIMIT = 5
+STATIC_MAX_ROWS = 16384
 
 
 class VSVError(RuntimeError):
@@ -53,7 +57,8 @@ class Outputs(ctypes.Structure):
                 ("error_flag", ctypes.c_void_p), ("slow_rows", ctypes.c_void_p)]
 
 
-SYMBOLS = ("vsv_workspace_bytes", "vsv_workspace_init", "vsv_verify_greedy", "vsv_verify_sampled",
+SYMBOLS = ("vsv_workspace_bytes", "vsv_workspace_init", "vsv_verify_greedy", "vsv_verify_greedy_static",
+           "vsv_verify_sampled",
            "vsv_verify_probabilistic", "vsv_draft_confidence", "vsv_allocate_verify", "vsv_goodput_init", "vsv_goodput_observe",
            "vsv_goodput_step", "vsv_goodput_select", "vsv_status_string", "vsv_version")
 
@@ -88,6 +93,8 @@ def lib():
     L.vsv_workspace_init.restype = ctypes.c_int
     L.vsv_verify_greedy.argtypes = [ctypes.POINTER(Batch), i32, ctypes.POINTER(Outputs), vp, sz, vp]
     L.vsv_verify_greedy.restype = ctypes.c_int
+    L.vsv_verify_greedy_static.argtypes = [ctypes.POINTER(Batch), i32, ctypes.POINTER(Outputs), vp]
+    L.vsv_verify_greedy_static.restype = ctypes.c_int
     L.vsv_verify_sampled.argtypes = [ctypes.POINTER(Batch), vp, vp, vp, vp, u64, u64,
                                      ctypes.POINTER(Outputs), vp, sz, vp]
     L.vsv_verify_sampled.restype = ctypes.c_int
@@ -248,6 +255,23 @@ def verify_greedy(logits, row_offsets, row_owner, draft_tokens, relaxed_topk=1, 
     _check(lib().vsv_verify_greedy(ctypes.byref(batch), int(relaxed_topk), ctypes.byref(outs),
                                    _ptr(ws), ws.numel(), _stream(stream)))
     return out
+
+
+def verify_greedy_static(logits, row_offsets, row_owner, draft_tokens, relaxed_topk=1, vocab=None, out=None,
+                         stream=None):
+    """Greedy verification through the entry point that allocates nothing
+    (vsv_verify_greedy_static: library-owned scratch, at most STATIC_MAX_ROWS
+    rows). `out`, if given, is a dict of output tensors as returned by
+    verify_greedy and is written in place; otherwise outputs are allocated
+    here. Returns the output dict."""
+    batch, outs, res, B, R = _prepare(logits, row_offsets, row_owner, draft_tokens, vocab, stream)
+    if out is not None:
+        res = out
+        outs = _outputs_struct(res)
+    _keep_alive(stream, logits, row_offsets, row_owner, draft_tokens)
+    _check(lib().vsv_verify_greedy_static(ctypes.byref(batch), int(relaxed_topk), ctypes.byref(outs),
+                                          _stream(stream)))
+    return res
 
 
 def verify_sampled(logits, row_offsets, row_owner, draft_tokens, temperature, top_k, top_p, min_p,

@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 LIB = os.path.join(PKG, "libvspec_verify.so")
-SOURCES = ["abi.cpp", "verify.hip", "sampled.hip", "probabilistic.hip", "confidence.hip", "allocate.hip", "goodput.cpp"]
+SOURCES = ["abi.cpp", "verify.hip", "sampled.hip", "probabilistic.hip", "confidence.hip", "allocate.hip", "goodput.cpp", "static_ws.hip"]
 ARCH = "gfx950"
 # Packed-FP32 VALU forms are kept out of the code objects: the compiler would
 # otherwise fuse float pairs into v_pk_* instructions.

@@ -190,6 +190,7 @@ const char* vsv_status_string(vsv_status status) {
     case VSV_EUNSUPPORTED: return "unsupported option";
     case VSV_EWORKSPACE: return "workspace missing, misaligned or too small";
     case VSV_EHIP: return "HIP launch failed";
+    case VSV_ELIMIT: return "batch larger than the static scratch serves";
   }
   return "unknown status";
 }

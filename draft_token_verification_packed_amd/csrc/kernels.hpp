@@ -145,15 +145,14 @@ constexpr size_t kWsAlign = 256;
 constexpr int kQueueNext = 0;
 constexpr int kQueueDone = 16;
 constexpr int kQueueWords = 17;
-inline size_t ws_align(size_t b) { return (b + kWsAlign - 1) / kWsAlign * kWsAlign; }
-inline size_t ws_row_bytes(int32_t R) { return ws_align(static_cast<size_t>(R > 0 ? R : 1) * 8); }
-inline size_t ws_part_bytes(int32_t R) {
+constexpr size_t ws_align(size_t b) { return (b + kWsAlign - 1) / kWsAlign * kWsAlign; }
+constexpr size_t ws_row_bytes(int32_t R) { return ws_align(static_cast<size_t>(R > 0 ? R : 1) * 8); }
+constexpr size_t ws_part_bytes(int32_t R) {
   return ws_align((static_cast<size_t>(R > 0 ? R : 0) + kMaxGroups) * kPartWords * 8);
 }
-inline size_t ws_bytes(int32_t B, int32_t R, int32_t sampled) {
+constexpr size_t ws_bytes(int32_t B, int32_t R, int32_t sampled) {
   (void)B;
-  const size_t perm = sampled ? ws_align(static_cast<size_t>(R > 0 ? R : 1) * 4) : 0;
-  return kWsAlign + ws_row_bytes(R) + ws_part_bytes(R) + perm;
+  return kWsAlign + ws_row_bytes(R) + ws_part_bytes(R) + (sampled ? ws_align(static_cast<size_t>(R > 0 ? R : 1) * 4) : 0);
 }
 // Tokens travel in the low 30 bits of a row word.
 constexpr int32_t kMaxVocab = 0x3FFFFFFF;

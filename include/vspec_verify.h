@@ -22,7 +22,8 @@
  *    ready for the next; one workspace serves one call at a time, so calls
  *    that may overlap in time (on different streams) need workspaces and
  *    outputs of their own. The host side keeps only a per-device cache of
- *    the CU count.
+ *    the CU count; vsv_verify_greedy_static alone uses library-owned device
+ *    memory (its own comment states the contract).
  *  - All work is enqueued on `stream` (0 = the null stream). Nothing is
  *    synchronised and nothing is read back to the host; results are valid
  *    once the stream reaches them.
@@ -52,7 +53,9 @@ typedef enum {
   VSV_EINVAL = 1,        /* NULL required pointer, bad size, dtype or option  */
   VSV_EUNSUPPORTED = 2,  /* option not built into this library                */
   VSV_EWORKSPACE = 3,    /* workspace NULL, misaligned or smaller than needed */
-  VSV_EHIP = 4           /* the HIP runtime refused the launch                */
+  VSV_EHIP = 4,          /* the HIP runtime refused the launch                */
+  VSV_ELIMIT = 5         /* batch beyond the fixed capacity of an entry point */
+                         /* that allocates nothing                            */
 } vsv_status;
 
 typedef enum { VSV_F32 = 0, VSV_BF16 = 1 } vsv_dtype;
@@ -125,6 +128,23 @@ vsv_status vsv_workspace_init(void* workspace, size_t bytes, hipStream_t stream)
 vsv_status vsv_verify_greedy(const vsv_batch* batch, int32_t relaxed_topk,
                              const vsv_outputs* out, void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
+
+/* Greedy verification that allocates nothing, for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation. Same arguments,
+ * results and errors as vsv_verify_greedy without the workspace: the
+ * library keeps one fixed scratch array per GPU for it, sized for
+ * VSV_STATIC_MAX_ROWS packed rows (about 0.95 MiB, held until the process
+ * ends), zero-filled on the first call on that GPU. Every call on a GPU
+ * shares that GPU's array and leaves its contents for the next call, so
+ * calls that may overlap in time on one GPU (different streams, threads)
+ * race and must not be issued. No hipMalloc, hipFree or other allocation
+ * happens in any call.
+ * Errors: as vsv_verify_greedy, plus VSV_ELIMIT for num_rows above
+ * VSV_STATIC_MAX_ROWS. */
+#define VSV_STATIC_MAX_ROWS 16384
+vsv_status vsv_verify_greedy_static(const vsv_batch* batch, int32_t relaxed_topk,
+                                    const vsv_outputs* out, hipStream_t stream);
 
 /* Sampled (or mixed) target verification with point-mass drafts.
  * Per-request device arrays [B]: temperature (0 = greedy arg-max for that

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_status_strings_and_version(L):
     assert L.vsv_status_string(0) == b"ok"
-    for s in range(1, 5):
+    for s in range(1, 6):
         assert len(L.vsv_status_string(s)) > 3
     assert L.vsv_version() >= 100
 
@@ -166,3 +166,15 @@ def test_allocate_validation(L):
     assert call(3, 4, 5, vl=None) == 1 and call(3, 4, 5, off=None) == 1 and call(3, 4, 5, own=None) == 1
     assert call(3, 4, 5, drafts=p) == 1            # drafts without packed output
     assert call(3, 4, 5, packed=p) == 1            # packed output without drafts
+
+
+def test_static_entry_point_rejects_batches_beyond_its_scratch(L):
+    """The entry point that allocates nothing refuses, before any HIP call,
+    a batch larger than its fixed scratch serves (and a missing batch)."""
+    out = vsv.Outputs(0x50000, 0x60000, 0x70000, 0x80000, None, None, None, None)
+    R = vsv.STATIC_MAX_ROWS + 1
+    b = _batch(num_requests=1, num_rows=R)
+    assert L.vsv_verify_greedy_static(ctypes.byref(b), 1, ctypes.byref(out), None) == vsv.VSV_ELIMIT
+    assert L.vsv_verify_greedy_static(None, 1, ctypes.byref(out), None) == 1
+    text = open(HEADER).read()
+    assert "#define VSV_STATIC_MAX_ROWS %d" % vsv.STATIC_MAX_ROWS in text
