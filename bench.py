@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+SPREAD_BLOCK = 10
 ROTATE_BYTES = 1 << 30
 KERNEL_SOURCES = ("csrc/device.hpp", "csrc/row_stream.hpp", "csrc/sampled_row.hpp", "csrc/verify_common.hpp",
                   "csrc/verify.hip", "csrc/sampled.hip", "csrc/confidence.hip", "csrc/kernels.hpp")
@@ -64,6 +65,13 @@ def upload(torch, arr):
     if arr.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).cuda().view(torch.bfloat16)
     return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def metric_name(wl):
+    """BASELINE's headline metric, named for the shape actually run."""
+    K = wl._spec["K"]
+    shape = "B=%d %s V=%d" % (wl.B, "K=%d" % K if K is not None else "K~U{0..%d}" % wl._spec["Kmax"], wl.V)
+    return "verified rows/sec and achieved HBM GB/s (% of peak), " + shape
 
 
 def build_steps(vsv, torch, wl):
@@ -108,31 +116,210 @@ def build_steps(vsv, torch, wl):
     return steps, kernels, ncopy, step_bytes
 
 
-def cpu_baseline(wl, budget_s=12.0):
-    """Oracle (float64 NumPy, one process) on whole requests of the workload."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_cores():
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    # the GPU host's share is at most 16 cores per GPU
+    return max(1, min(n, 16))
+
+
+def request_args(wl, i):
+    """The oracle's arguments for request i on its own (rows, drafts,
+    parameters, and its Philox uniforms keyed by its batch index)."""
+    r0, r1 = int(wl.offsets[i]), int(wl.offsets[i + 1])
+    a = dict(i=i, logits=wl.logits[r0:r1], dtype=wl.dtype, V=wl.V, drafts=wl.drafts[r0 - i:r1 - i - 1],
+             sampled=bool(wl.sampled), relaxed=wl.relaxed_topk, seed=wl.seed, offset=wl.offset,
+             draft_logits=None if wl.D == 0 else wl.draft_logits[r0 - i:r1 - i - 1])
+    if wl.sampled:
+        a.update(T=wl.temperature[i:i + 1], TK=wl.top_k[i:i + 1], TP=wl.top_p[i:i + 1], MP=wl.min_p[i:i + 1])
+    return a
+
+
+def oracle_request(a):
+    """One request through the oracle: verification of its rows (and draft
+    confidence of its draft rows). Runs in the bench process or a pool worker;
+    imports only NumPy and the oracle."""
     import numpy as np
     import oracle
+    n = a["logits"].shape[0]
+    off = np.array([0, n], dtype=np.int32)
+    if a["sampled"]:
+        us = {(0, j): oracle.row_uniform(a["seed"], a["i"], j, a["offset"]) for j in range(n)}
+        ref = oracle.verify_sampled(a["logits"], a["dtype"], a["V"], off, None, a["drafts"], a["T"], a["TK"], a["TP"],
+                                    a["MP"], a["seed"], a["offset"], uniforms=us)
+    else:
+        ref = oracle.verify_greedy(a["logits"], a["dtype"], a["V"], off, None, a["drafts"], relaxed_topk=a["relaxed"])
+    if a["draft_logits"] is not None:
+        ref["confidence"], ref["confidence_lse"] = oracle.draft_confidence(a["draft_logits"], a["dtype"], a["V"],
+                                                                           a["drafts"])
+    return ref
+
+
+def margin_request(a):
+    """True if a sampled row of the request lies within the tie margins (its
+    outcome would then hinge on rounding, so it is left out of the check)."""
+    import numpy as np
+    import oracle
+    if not a["sampled"] or float(np.float32(a["T"][0])) == 0.0:
+        return False
+    T = float(np.float32(a["T"][0]))
+    for j in range(a["logits"].shape[0]):
+        x = oracle.row_f64(a["logits"], a["dtype"], j, a["V"])
+        u = oracle.row_uniform(a["seed"], a["i"], j, a["offset"])
+        tp, um, mp = oracle.sampled_row_margins(x, T, int(a["TK"][0]), float(np.float32(a["TP"][0])),
+                                                float(np.float32(a["MP"][0])), u)
+        if tp < 2e-7 or um < 2e-7 or mp < 1e-9:
+            return True
+    return False
+
+
+_POOL_WL = None
+
+
+def _pool_init(meta, names):
+    """Pool worker set-up: attach to the shared logits blocks (no copy) and
+    rebuild a light view of the workload."""
+    import types
+    from multiprocessing import shared_memory
+    import numpy as np
+    import oracle  # noqa: F401  (imported once per worker, not per task)
+    global _POOL_WL
+    wl = types.SimpleNamespace(**meta)
+    blocks = []
+    for field, (name, shape, dtype) in names.items():
+        shm = shared_memory.SharedMemory(name=name)
+        blocks.append(shm)
+        setattr(wl, field, np.ndarray(shape, dtype=dtype, buffer=shm.buf))
+    wl._blocks = blocks
+    _POOL_WL = wl
+
+
+def _pool_task(i):
+    a = request_args(_POOL_WL, i)
+    oracle_request(a)
+    return a["logits"].shape[0] + (0 if a["draft_logits"] is None else a["draft_logits"].shape[0])
+
+
+def pool_rate(wl, cores, budget_s):
+    """Oracle rows/s over `cores` worker processes split by request: the
+    logits sit in shared memory, tasks are request indices, and whole
+    rounds of requests are issued until budget_s has passed."""
+    import multiprocessing
+    from multiprocessing import shared_memory
+    import numpy as np
+    shms, names = [], {}
+    try:
+        for field in ("logits", "draft_logits"):
+            arr = getattr(wl, field)
+            if arr is None:
+                continue
+            shm = shared_memory.SharedMemory(create=True, size=max(1, arr.nbytes))
+            shms.append(shm)
+            np.ndarray(arr.shape, dtype=arr.dtype, buffer=shm.buf)[...] = arr
+            names[field] = (shm.name, arr.shape, arr.dtype.str)
+        meta = dict(B=wl.B, V=wl.V, D=wl.D, dtype=wl.dtype, offsets=wl.offsets, drafts=wl.drafts,
+                    sampled=wl.sampled, relaxed_topk=wl.relaxed_topk, seed=wl.seed, offset=wl.offset,
+                    temperature=wl.temperature, top_k=wl.top_k, top_p=wl.top_p, min_p=wl.min_p,
+                    draft_logits=None)
+        ctx = multiprocessing.get_context("spawn")
+        with ctx.Pool(cores, initializer=_pool_init, initargs=(meta, names)) as pool:
+            pool.map(_pool_task, range(min(cores, wl.B)))          # start-up, not timed
+            rows, n, nxt = 0, 0, 0
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < budget_s:
+                chunk = [(nxt + k) % wl.B for k in range(4 * cores)]
+                nxt = (nxt + 4 * cores) % wl.B
+                rows += sum(pool.map(_pool_task, chunk, chunksize=1))
+                n += len(chunk)
+            dt = time.perf_counter() - t0
+    finally:
+        for shm in shms:
+            shm.close()
+            shm.unlink()
+    return rows / dt, n, rows, dt
+
+
+def compare_request(wl, i, ref, gpu):
+    """Mismatches between the oracle's result for request i and the GPU's."""
+    import numpy as np
+    r0, r1 = int(wl.offsets[i]), int(wl.offsets[i + 1])
+    bad = []
+    if int(gpu["accepted_len"][i]) != int(ref["accepted_len"][0]):
+        bad.append("accepted_len")
+    if int(gpu["next_token"][i]) != int(ref["next_token"][0]):
+        bad.append("next_token")
+    if not np.array_equal(gpu["row_token"][r0:r1], ref["row_token"]):
+        bad.append("row_token")
+    lse, want = gpu["row_lse"][r0:r1].astype(np.float64), ref["row_lse"]
+    if not np.all(np.abs(lse - want) <= 1e-5 * np.maximum(1.0, np.abs(want))):
+        bad.append("row_lse")
+    o = int(gpu["out_offsets"][i])
+    n = int(ref["out_offsets"][1])
+    if int(gpu["out_offsets"][i + 1]) - o != n or not np.array_equal(gpu["out_tokens"][o:o + n], ref["out_tokens"]):
+        bad.append("out_tokens")
+    if "confidence" in ref:
+        c = gpu["confidence"][r0 - i:r1 - i - 1].astype(np.float64)
+        if not np.all(np.abs(c - ref["confidence"]) <= 1e-5 * ref["confidence"]):
+            bad.append("confidence")
+    return bad
+
+
+def cpu_baseline(wl, gpu, budget_s=10.0):
+    """The float64 oracle on the host cores, and the parity check.
+
+    Single process: whole requests in batch order until about budget_s of CPU
+    work (repeating whole passes if the batch takes less). Pool: the same
+    oracle over len(sched_getaffinity) worker processes (at most 16), split by
+    request, for about budget_s (pool_rate). Every request the single-process leg ran first is compared with
+    the GPU's outputs of the first input copy (`gpu`, host arrays): bit-exact
+    tokens, lengths and compacted output, log-sum-exp and confidence within
+    1e-5 relative; sampled requests with a row inside the tie margins are
+    left out of that check and counted."""
+    import multiprocessing
+    import numpy as np
     t0 = time.perf_counter()
-    rows = 0
-    passes = 0
-    # one pass over the whole batch is seconds; repeat within the budget
+    rows, done, mismatched, margin_skipped = 0, 0, [], 0
+    checked = set()
     while True:
-        if wl.sampled:
-            oracle.verify_sampled(wl.logits, wl.dtype, wl.V, wl.offsets, wl.owner, wl.drafts,
-                                  wl.temperature, wl.top_k, wl.top_p, wl.min_p, wl.seed, wl.offset)
-        else:
-            oracle.verify_greedy(wl.logits, wl.dtype, wl.V, wl.offsets, wl.owner, wl.drafts,
-                                 relaxed_topk=wl.relaxed_topk)
-        if wl.D:
-            oracle.draft_confidence(wl.draft_logits, wl.dtype, wl.V, wl.selected)
-        rows += wl.R
-        passes += 1
+        i = done % wl.B
+        a = request_args(wl, i)
+        ref = oracle_request(a)
+        rows += a["logits"].shape[0] + (0 if a["draft_logits"] is None else a["draft_logits"].shape[0])
+        done += 1
+        if i not in checked:
+            checked.add(i)
+            bad = compare_request(wl, i, ref, gpu)
+            if bad:
+                if margin_request(a):
+                    margin_skipped += 1
+                else:
+                    mismatched.append((i, bad))
         if time.perf_counter() - t0 >= budget_s:
             break
-    dt = time.perf_counter() - t0
-    return dict(value=rows / dt, unit="rows/s", cores=1, kind="oracle",
-                sample="%d full pass(es) over the %d-row batch (%s), %.1f s, single process"
-                       % (passes, wl.R, "plus its draft rows" if wl.D else "verify rows only", dt))
+    dt1 = time.perf_counter() - t0
+    single = rows / dt1
+    cores = host_cores()
+    rate, n_pool, prow, dt2 = pool_rate(wl, cores, budget_s)
+    unit_rows = "verify + draft rows" if wl.D else "verify rows"
+    return dict(
+        value=rate, unit="rows/s", cores=cores, kind="oracle", cpu=cpu_model(),
+        single_core_value=single,
+        sample="%d requests (%d %s) over a pool of %d processes split by request, %.1f s; single process: "
+               "%d requests in %.1f s" % (n_pool, prow, unit_rows, cores, dt2, done, dt1),
+        parity=dict(requests_checked=len(checked), requests_mismatched=len(mismatched),
+                    margin_skipped=margin_skipped, first_mismatches=mismatched[:5],
+                    checked="accepted_len, next_token, row_token, compacted tokens bit-exact; row_lse%s within "
+                            "1e-5 relative" % (" and confidence" if wl.D else "")),
+    )
 
 
 def bench_allocate(args, vsv, torch):
@@ -361,6 +548,29 @@ def main():
     torch.cuda.synchronize()
     print("[bench] %d input copies, %.1f MB per step" % (ncopy, step_bytes / 1e6), file=sys.stderr, flush=True)
 
+    # The first copy's outputs, before any timing: the CPU-baseline leg
+    # compares them with the oracle's.
+    for call in steps[0]:
+        call.run()
+    torch.cuda.synchronize()
+    res = steps[0][0]._keep[2]
+    gpu = {k: res[k].cpu().numpy() for k in ("accepted_len", "next_token", "out_offsets", "out_tokens",
+                                             "row_token", "row_lse", "error_flag")}
+    if wl.D:
+        gpu["confidence"] = steps[0][1]._keep[2][0].cpu().numpy()
+    slow = int(res["slow_rows"].item()) if wl.sampled else None
+    baseline = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle and checking the first copy against it", file=sys.stderr, flush=True)
+        baseline = cpu_baseline(wl, gpu)
+        par = baseline["parity"]
+        print("[bench] parity: %d requests checked, %d mismatched, %d inside the tie margins"
+              % (par["requests_checked"], par["requests_mismatched"], par["margin_skipped"]),
+              file=sys.stderr, flush=True)
+        if par["requests_mismatched"] or int(gpu["error_flag"][0]) != 0:
+            print("[bench] GPU outputs differ from the oracle: %s" % par["first_mismatches"], file=sys.stderr)
+            return 3
+
     for k in range(args.warmup):
         for call in steps[k % ncopy]:
             call.run()
@@ -382,23 +592,41 @@ def main():
     total_ms = bounds[0].elapsed_time(bounds[ncall])
     per_kernel_ms = [bounds[c].elapsed_time(bounds[c + 1]) / args.steps for c in range(ncall)]
     ms = total_ms / args.steps
-    print("[bench] %.2f us/step; per kernel %s us" % (ms * 1e3, ["%.2f" % (t * 1e3) for t in per_kernel_ms]),
-          file=sys.stderr, flush=True)
+    # The spread of launch times: a second pass with an event after every
+    # SPREAD_BLOCK launches (an event between every two launches would add
+    # its own gap to each); median, p10 and p90 of the block means.
+    spread = []
+    nblk = max(1, args.steps // SPREAD_BLOCK)
+    for c in range(ncall):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(nblk + 1)]
+        ev[0].record()
+        for b in range(nblk):
+            for k in range(b * SPREAD_BLOCK, (b + 1) * SPREAD_BLOCK):
+                steps[k % ncopy][c].run()
+            ev[b + 1].record()
+        torch.cuda.synchronize()
+        t = sorted(ev[b].elapsed_time(ev[b + 1]) * 1e3 / SPREAD_BLOCK for b in range(nblk))
+        pick = lambda q: t[min(len(t) - 1, int(round(q * (len(t) - 1))))]
+        spread.append(dict(median=pick(0.5), p10=pick(0.1), p90=pick(0.9), block=SPREAD_BLOCK))
+    print("[bench] %.2f us/step; per kernel %s us; medians %s us" % (
+        ms * 1e3, ["%.2f" % (t * 1e3) for t in per_kernel_ms], ["%.2f" % d["median"] for d in spread]),
+        file=sys.stderr, flush=True)
 
-    slow = None
-    if wl.sampled:
-        slow = int(steps[0][0]._keep[2]["slow_rows"].item())  # rows sent to the exact path, summed over calls
     dom = max(range(ncall), key=lambda c: kernels[c][1])
     kname, kbytes = kernels[dom]
     kms = per_kernel_ms[dom]
     achieved = kbytes / (kms * 1e-3) / 1e9
     traffic = measured_traffic(kname, args.workload)
+    step_median_us = sum(d["median"] for d in spread)
     line = dict(
-        metric="verified rows/sec and achieved HBM GB/s (% of peak), B=128 K=4 V=152064",
+        metric=metric_name(wl),
         value=wl.R / (ms * 1e-3), unit="rows/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
         ms_per_step=ms, higher_is_better=True, scaling="weak", vs_baseline=None,
         dtype="bf16" if wl.dtype == 1 else "f32", data="synthetic",
         hbm_gbps=step_bytes / (ms * 1e-3) / 1e9, hbm_frac=step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        step_us=dict(mean=ms * 1e3, median=step_median_us, per_kernel=[
+            dict(kernel=kernels[c][0], mean=per_kernel_ms[c] * 1e3, **spread[c]) for c in range(ncall)]),
+        rows_per_s_at_median=wl.R / (step_median_us * 1e-6),
         config=dict(workload=wl.name, key=args.workload, B=wl.B, R=wl.R, D=wl.D, V=wl.V,
                     K=None if wl._spec["K"] is None else int(wl._spec["K"]),
                     relaxed_topk=wl.relaxed_topk, sampled=bool(wl.sampled), input_copies=ncopy,
@@ -406,11 +634,11 @@ def main():
                     slow_rows_first_copy=slow),
         roofline=dict(bound="hbm", kernel=kname, achieved=achieved, peak=HBM_PEAK_GBPS, unit="GB/s",
                       frac=achieved / HBM_PEAK_GBPS, traffic=traffic, bytes_per_launch=kbytes,
-                      launch_us=kms * 1e3),
+                      launch_us=kms * 1e3, launch_us_median=spread[dom]["median"],
+                      launch_us_p10=spread[dom]["p10"], launch_us_p90=spread[dom]["p90"]),
     )
-    if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(wl)
+    if baseline is not None:
+        line["cpu_baseline"] = baseline
     print(json.dumps(line), flush=True)
     return 0
 
