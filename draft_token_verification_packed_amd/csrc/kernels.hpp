@@ -132,6 +132,17 @@ struct ConfidenceArgs {
 // large workgroups and the merge across them dominates (20 rows: 20.7 us
 // against 14.1), and above, the row kernel wins up to 3000 rows.
 constexpr int kMaxGroups = 1024;
+// Row kernel: parts per row (one per about kPartBytes of logits, at most
+// kMaxRowParts), and the partial slots the workspace holds for them.
+#ifndef VSV_PART_BYTES
+#define VSV_PART_BYTES 152064
+#endif
+#ifndef VSV_FORCE_PARTS
+#define VSV_FORCE_PARTS 0
+#endif
+constexpr int64_t kPartBytes = VSV_PART_BYTES;
+constexpr int kMaxRowParts = 16;
+constexpr int kPartSlots = 8192;
 constexpr int kMaxLocalRows = 32;
 constexpr int kPartWords = 6;   // best, index, exponent ref, sum, rank, row info
 inline bool greedy_persistent(int32_t R, int32_t groups) {
@@ -147,8 +158,13 @@ constexpr int kQueueDone = 16;
 constexpr int kQueueWords = 17;
 constexpr size_t ws_align(size_t b) { return (b + kWsAlign - 1) / kWsAlign * kWsAlign; }
 constexpr size_t ws_row_bytes(int32_t R) { return ws_align(static_cast<size_t>(R > 0 ? R : 1) * 8); }
+// The partials area serves the persistent kernel (kPartWords per (row,
+// workgroup) slot, R + kMaxGroups slots) and the row kernel (6 words for
+// each part but a row's last, at most max(R + kMaxGroups, kPartSlots)).
 constexpr size_t ws_part_bytes(int32_t R) {
-  return ws_align((static_cast<size_t>(R > 0 ? R : 0) + kMaxGroups) * kPartWords * 8);
+  return ws_align(((static_cast<size_t>(R > 0 ? R : 0) + kMaxGroups) > static_cast<size_t>(kPartSlots)
+                       ? (static_cast<size_t>(R > 0 ? R : 0) + kMaxGroups)
+                       : static_cast<size_t>(kPartSlots)) * kPartWords * 8);
 }
 constexpr size_t ws_bytes(int32_t B, int32_t R, int32_t sampled) {
   (void)B;

@@ -28,6 +28,7 @@ struct RowPartial {
   float mc;     // exponent reference (log2 domain, integer-valued once set)
   double s;     // sum of exp2(x*c - mc)
   int rank;     // elements ordered before token d (relaxed acceptance)
+  int bad;      // a NaN was seen where the IEEE maximum (kMax3) would hide it
 };
 
 struct RowResult {
@@ -71,6 +72,7 @@ __device__ __forceinline__ void partial_init(RowPartial& p) {
   p.mc = -FLT_MAX;
   p.s = 0.0;
   p.rank = 0;
+  p.bad = 0;
 }
 
 // Raise the reference to ceil(vmax * c) if vmax * c exceeds it; the sum is
@@ -119,17 +121,22 @@ __device__ __forceinline__ void take_scalar(RowPartial& p, float x, int e, float
   }
   partial_rebase(p, x, c);
   p.s += static_cast<double>(fast_exp2(fmaf(x, c, -p.mc)));
+  p.bad |= (x != x) ? 1 : 0;
   if (kRank) p.rank += (x > xd || (x == xd && e < d)) ? 1 : 0;
 }
 
-// Decode one 16-byte vector into f and return its maximum.
-template <typename E>
+// Decode one 16-byte vector into f and return its maximum. kMax3 takes the
+// IEEE maximum (NaN propagates, -0 < +0), which gfx950 folds three operands
+// at a time into v_maximum3_f32 with no NaN-quieting step per operand; only
+// callers whose rows are flagged anyway when they hold a NaN, and who
+// compare the result with ==, use it.
+template <typename E, bool kMax3 = false>
 __device__ __forceinline__ float vec_max(const u32x4& w, float* f) {
   constexpr int N = Elem<E>::kVec;
   Elem<E>::decode(w, f);
   float vmax = f[0];
 #pragma unroll
-  for (int k = 1; k < N; ++k) vmax = fmaxf(vmax, f[k]);
+  for (int k = 1; k < N; ++k) vmax = kMax3 ? __builtin_elementwise_maximum(vmax, f[k]) : fmaxf(vmax, f[k]);
   return vmax;
 }
 
@@ -167,7 +174,7 @@ struct NoCapture {
 // beyond nvec (loaded duplicates or zeros) count as -inf; other groups carry
 // no masking code at all.
 template <typename E, int U, int NT, bool kRank, bool kPartial = false, typename Keep = NoKeep,
-          typename Cap = NoCapture>
+          typename Cap = NoCapture, bool kMax3 = false>
 __device__ __forceinline__ void take_group(RowPartial& p, const u32x4* w, int v, int head, float c, float xd, int d,
                                            Keep& keep, int nvec = 0, Cap cap = Cap()) {
   constexpr int N = Elem<E>::kVec;
@@ -176,14 +183,17 @@ __device__ __forceinline__ void take_group(RowPartial& p, const u32x4* w, int v,
   float gmax = -INFINITY;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    vmx[u] = vec_max<E>(w[u], f[u]);
+    vmx[u] = vec_max<E, kMax3>(w[u], f[u]);
     if (kPartial && v + u * NT >= nvec) {
       vmx[u] = -INFINITY;
 #pragma unroll
       for (int k = 0; k < N; ++k) f[u][k] = -INFINITY;
     }
-    gmax = fmaxf(gmax, vmx[u]);
+    gmax = kMax3 ? __builtin_elementwise_maximum(gmax, vmx[u]) : fmaxf(gmax, vmx[u]);
   }
+  // the IEEE maximum carries a NaN into the group max, which then neither
+  // becomes the best nor sets the exponent reference: remember it instead
+  if constexpr (kMax3) p.bad |= (gmax != gmax) ? 1 : 0;
 #pragma unroll
   for (int u = 0; u < U; ++u) cap(u, vmx[u]);
   const bool gt = gmax > p.best;
@@ -240,7 +250,7 @@ __device__ __forceinline__ void load_group(u32x4* dst, const u32x4* __restrict__
 // once, right after the first group's loads are issued, so loads it issues
 // overlap the stream instead of trailing it. `keep` receives the thread's
 // best group (GroupKeep) or is ignored (NoKeep).
-template <typename E, int NT, int U, bool kRank, typename Keep = NoKeep, typename Hook = NoHook>
+template <typename E, int NT, int U, bool kRank, typename Keep = NoKeep, typename Hook = NoHook, bool kMax3 = false>
 __device__ __forceinline__ void stream_row(const E* __restrict__ row, int V, float c, float xd, int d,
                                            RowPartial& p, Keep& keep, Hook hook = Hook()) {
   constexpr int N = Elem<E>::kVec;
@@ -265,16 +275,16 @@ __device__ __forceinline__ void stream_row(const E* __restrict__ row, int V, flo
     int g = 0;
     for (; g + 2 <= nfull; g += 2) {
       load_group<NT, U>(b, vp, g + 1, nvec);
-      take_group<E, U, NT, kRank>(p, a, g * G + tid, head, c, xd, d, keep);
+      take_group<E, U, NT, kRank, false, Keep, NoCapture, kMax3>(p, a, g * G + tid, head, c, xd, d, keep);
       load_group<NT, U>(a, vp, g + 2, nvec);
-      take_group<E, U, NT, kRank>(p, b, (g + 1) * G + tid, head, c, xd, d, keep);
+      take_group<E, U, NT, kRank, false, Keep, NoCapture, kMax3>(p, b, (g + 1) * G + tid, head, c, xd, d, keep);
     }
     if (g < nfull) {
       load_group<NT, U>(b, vp, g + 1, nvec);
-      take_group<E, U, NT, kRank>(p, a, g * G + tid, head, c, xd, d, keep);
-      take_group<E, U, NT, kRank, true>(p, b, nfull * G + tid, head, c, xd, d, keep, nvec);
+      take_group<E, U, NT, kRank, false, Keep, NoCapture, kMax3>(p, a, g * G + tid, head, c, xd, d, keep);
+      take_group<E, U, NT, kRank, true, Keep, NoCapture, kMax3>(p, b, nfull * G + tid, head, c, xd, d, keep, nvec);
     } else {
-      take_group<E, U, NT, kRank, true>(p, a, nfull * G + tid, head, c, xd, d, keep, nvec);
+      take_group<E, U, NT, kRank, true, Keep, NoCapture, kMax3>(p, a, nfull * G + tid, head, c, xd, d, keep, nvec);
     }
   } else {
     hook();
@@ -375,6 +385,83 @@ __device__ __forceinline__ RowResult finish_row(const RowPartial& p, RowScratch<
   out.sum = r.s;
   out.mref = r.mc;
   out.lse = 0.69314718055994530942 * (static_cast<double>(r.mc) + log2(r.s));
+  return out;
+}
+
+// LDS for finish_row_lean: two rounds of one value per wave.
+template <int NT> struct LeanScratch {
+  float mx[NT / kWave];
+  float mc[NT / kWave];
+  float s[NT / kWave];
+  int idx[NT / kWave];
+  int rank[NT / kWave];
+};
+
+// What a workgroup's stream of (part of) a row leaves: its maximum, the
+// lowest index holding it, the exponent reference and the sum of
+// exp2(x * c - mref), the rank count.
+struct RowStats {
+  float max;
+  int argmax;
+  float mref;
+  double sum;
+  int rank;
+};
+
+// Block combination of the threads' partials in two rounds, with the least
+// work per wave (every wave of a launch reaches it at about the same time,
+// so its instructions add to the launch): round 1 takes the block maximum
+// and exponent reference (every thread's reference is already an integer in
+// log2 units, so sums rebase exactly); round 2 adds the rebased sums (float
+// per wave: the terms are positive, so the wave sum's relative error stays
+// below 64 float roundings; float64 across waves), and takes the lowest
+// index of the maximum, which only lanes holding the block maximum search
+// for in their kept group. Every thread receives the result.
+template <typename E, int NT, int U, bool kRank, typename Keep>
+__device__ __forceinline__ RowStats finish_row_lean(const RowPartial& p, LeanScratch<NT>& sc, const Keep& keep,
+                                                    const E* __restrict__ row, int V) {
+  constexpr int N = Elem<E>::kVec;
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const float mw = wave_all(p.best, MaxOp());
+  const float cw = wave_all(p.mc, MaxOp());
+  if (lane == 0) {
+    sc.mx[w] = mw;
+    sc.mc[w] = cw;
+  }
+  lds_barrier();
+  float m = sc.mx[0], mg = sc.mc[0];
+#pragma unroll
+  for (int k = 1; k < NW; ++k) {
+    m = fmaxf(m, sc.mx[k]);
+    mg = fmaxf(mg, sc.mc[k]);
+  }
+  int idx = INT32_MAX;
+  if (p.best == m) {
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
+    int head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(E));
+    if (head > V) head = V;
+    idx = lane_argmax<E, NT, U>(p, keep, head, (V - head) / N);
+  }
+  float sl = (p.mc > -FLT_MAX) ? static_cast<float>(ldexp(p.s, static_cast<int>(fmaxf(p.mc - mg, -2000.f)))) : 0.f;
+  if (p.bad) sl = __builtin_nanf("");   // the row is flagged through its sum
+  const float sw = wave_all(sl, SumOp());
+  const int iw = wave_all(idx, MinOp());
+  const int rw = kRank ? wave_all(p.rank, SumOp()) : 0;
+  if (lane == 0) {
+    sc.s[w] = sw;
+    sc.idx[w] = iw;
+    sc.rank[w] = rw;
+  }
+  lds_barrier();
+  RowStats out{m, INT32_MAX, mg, 0.0, 0};
+#pragma unroll
+  for (int k = 0; k < NW; ++k) {
+    out.sum += static_cast<double>(sc.s[k]);
+    out.argmax = min(out.argmax, sc.idx[k]);
+    out.rank += sc.rank[k];
+  }
   return out;
 }
 

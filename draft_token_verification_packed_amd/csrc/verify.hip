@@ -444,38 +444,42 @@ __global__ __launch_bounds__(NT) void verify_greedy_kernel(VerifyArgs a) {
   if (p == plan.P - 1) greedy_tail<NT, kRelaxed>(a, plan, tag, tail, s_lo);
 }
 
-// Words of a first half's statistics (row-major, kHalfWords per row in the
-// workspace's partials area): max, its lowest index, exponent reference,
-// the float64 sum as two halves, rank count.
-constexpr int kHalfWords = 6;
+// Words of a part's statistics (row-major in the workspace's partials area,
+// parts 0 .. P - 2 of row r at slots r * (P - 1) + p, kPartStatWords words
+// per slot): max, its lowest index, exponent reference, the float64 sum as
+// two halves, rank count.
+constexpr int kPartStatWords = 6;
 
-// One workgroup per row, or per half row (a.parts = 2), for batches with
-// more rows than CUs. Halves are used where they give the CUs a more even
-// number of parts. The first half stores its statistics as tagged words;
-// the second half, dispatched after it, waits for them (so the wait always
-// ends), merges, and decides the row. The row's word goes to the scan like a
-// sampled row's.
+// One workgroup per row part (a.parts = P parts per row, 1 <= P <=
+// kMaxRowParts), for batches with more rows than CUs. The parts of a row
+// are consecutive workgroups, each streaming an equal share of the row's
+// 16-byte body (the first also takes the elements before it, the last those
+// after it). Each part combines its threads (finish_row_lean). Parts
+// 0 .. P - 2 store their statistics as tagged words and exit; the last
+// part, dispatched after them (so its wait always ends), gathers them
+// across one wave, merges them with its own, decides the row and hands its
+// word to the scan run by the launch's last workgroup.
 template <typename E, int NT, int U, bool kRelaxed>
 __global__ __launch_bounds__(NT) void verify_greedy_rows_kernel(VerifyArgs a) {
-  __shared__ RowScratch<NT> scr;
+  __shared__ LeanScratch<NT> scr;
   __shared__ TailScratch tail;
   constexpr int N = Elem<E>::kVec;
-  const bool halves = a.parts == 2;
-  const int r = halves ? static_cast<int>(blockIdx.x >> 1) : static_cast<int>(blockIdx.x);
-  const int part = halves ? static_cast<int>(blockIdx.x & 1) : 0;
+  const int P = a.parts;
+  const int r = static_cast<int>(blockIdx.x) / P;
+  const int part = static_cast<int>(blockIdx.x) - r * P;
   const uint32_t tag = call_tag(a);
   const E* __restrict__ row = static_cast<const E*>(a.logits) + static_cast<int64_t>(r) * a.ld;
-  // the part's elements [e0, e1): the halves split the row's 16-byte body;
-  // the first also holds the elements before it, the second those after it
+  // the part's elements [e0, e1): equal shares of the row's 16-byte body
   int e0 = 0, e1 = a.V;
-  if (halves) {
+  if (P > 1) {
     const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
     int head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(E));
     if (head > a.V) head = a.V;
-    const int mid = head + ((a.V - head) / N / 2) * N;
-    e0 = part == 0 ? 0 : mid;
-    e1 = part == 0 ? mid : a.V;
+    const int64_t nv = (a.V - head) / N;
+    e0 = part == 0 ? 0 : head + static_cast<int>(nv * part / P) * N;
+    e1 = part == P - 1 ? a.V : head + static_cast<int>(nv * (part + 1) / P) * N;
   }
+  const bool last = part == P - 1;
   const int owner = a.owner[r];
   RowMeta m{-1, 0, 0, -1};
   float xd = INFINITY;
@@ -488,51 +492,67 @@ __global__ __launch_bounds__(NT) void verify_greedy_rows_kernel(VerifyArgs a) {
   GroupKeep<U> keep{};
   constexpr float kLog2e = 1.4426950408889634f;
   // element indices inside the part are relative to e0, so the draft's is too
-  stream_row<E, NT, U, kRelaxed>(row + e0, e1 - e0, kLog2e, xd, kRelaxed ? m.draft - e0 : 0, p, keep, [&]() {
-    if (!kRelaxed) m = load_meta(a, r, owner);
-  });
-  const RowResult res = finish_row<E, NT, U, kRelaxed, true>(p, scr, keep, row + e0, e1 - e0);
-  if (threadIdx.x == 0) {
-    const int idx = res.argmax == INT32_MAX ? INT32_MAX : e0 + res.argmax;
-    uint64_t* hw = a.ws_part + static_cast<size_t>(r) * kHalfWords;
-    if (halves && part == 0) {
-      const uint64_t sb = __builtin_bit_cast(uint64_t, res.sum);
-      store_agent64(hw + 0, tagged(tag, __float_as_uint(res.max)));
-      store_agent64(hw + 1, tagged(tag, static_cast<uint32_t>(idx)));
-      store_agent64(hw + 2, tagged(tag, __float_as_uint(res.mref)));
-      store_agent64(hw + 3, tagged(tag, static_cast<uint32_t>(sb)));
-      store_agent64(hw + 4, tagged(tag, static_cast<uint32_t>(sb >> 32)));
-      store_agent64(hw + 5, tagged(tag, static_cast<uint32_t>(res.rank)));
-    } else {
-      RowRed red{res.sum, res.max, idx, res.mref, res.rank};
-      int stalled = 0;
-      if (halves) {
-        uint64_t w[kHalfWords];
-        auto load_all = [&]() {
+  auto hook = [&]() {
+    if (!kRelaxed && last) m = load_meta(a, r, owner);
+  };
+  stream_row<E, NT, U, kRelaxed, GroupKeep<U>, decltype(hook), true>(row + e0, e1 - e0, kLog2e, xd,
+                                                                      kRelaxed ? m.draft - e0 : 0, p, keep, hook);
+  const RowStats st = finish_row_lean<E, NT, U, kRelaxed>(p, scr, keep, row + e0, e1 - e0);
+  const int idx = st.argmax == INT32_MAX ? INT32_MAX : e0 + st.argmax;
+  uint64_t* slots = a.ws_part + static_cast<size_t>(r) * (P - 1) * kPartStatWords;
+  if (!last) {
+    if (threadIdx.x < kPartStatWords) {
+      const uint64_t sb = __builtin_bit_cast(uint64_t, st.sum);
+      const uint32_t v[kPartStatWords] = {__float_as_uint(st.max), static_cast<uint32_t>(idx),
+                                          __float_as_uint(st.mref), static_cast<uint32_t>(sb),
+                                          static_cast<uint32_t>(sb >> 32), static_cast<uint32_t>(st.rank)};
+      uint32_t mine = v[0];
 #pragma unroll
-          for (int f = 0; f < kHalfWords; ++f) w[f] = load_agent64(hw + f);
-        };
-        auto complete = [&]() {
-          bool ok = true;
+      for (int f = 1; f < kPartStatWords; ++f) mine = threadIdx.x == f ? v[f] : mine;
+      store_agent64(slots + static_cast<size_t>(part) * kPartStatWords + threadIdx.x, tagged(tag, mine));
+    }
+  } else if (threadIdx.x < kWave) {
+    // wave 0: lane q < P - 1 gathers part q's words, lane P - 1 holds this
+    // part's result, and one wave reduction merges them (largest max,
+    // lowest index among equal maxima, sums rebased to the largest
+    // reference, ranks added)
+    const int lane = threadIdx.x;
+    RowRed mine{0.0, -INFINITY, INT32_MAX, -FLT_MAX, 0};
+    int stalled = 0;
+    if (lane < P - 1) {
+      const uint64_t* hw = slots + static_cast<size_t>(lane) * kPartStatWords;
+      uint64_t w[kPartStatWords];
+      auto load_all = [&]() {
 #pragma unroll
-          for (int f = 0; f < kHalfWords; ++f) ok = ok && static_cast<uint32_t>(w[f] >> 32) == tag;
-          return ok;
-        };
-        int budget = kPollBudget;
+        for (int f = 0; f < kPartStatWords; ++f) w[f] = load_agent64(hw + f);
+      };
+      auto complete = [&]() {
+        bool ok = true;
+#pragma unroll
+        for (int f = 0; f < kPartStatWords; ++f) ok = ok && static_cast<uint32_t>(w[f] >> 32) == tag;
+        return ok;
+      };
+      int budget = kPollBudget;
+      load_all();
+      while (!complete() && budget > 0) {
+        --budget;
+        __builtin_amdgcn_s_sleep(2);
         load_all();
-        while (!complete() && budget > 0) {
-          --budget;
-          __builtin_amdgcn_s_sleep(2);
-          load_all();
-        }
-        stalled = complete() ? 0 : 1;
-        const uint64_t sb = (static_cast<uint64_t>(static_cast<uint32_t>(w[4])) << 32) | static_cast<uint32_t>(w[3]);
-        const RowRed first{__builtin_bit_cast(double, sb), __uint_as_float(static_cast<uint32_t>(w[0])),
-                           static_cast<int>(static_cast<uint32_t>(w[1])), __uint_as_float(static_cast<uint32_t>(w[2])),
-                           static_cast<int>(static_cast<uint32_t>(w[5]))};
-        red = combine(first, red);
       }
-      const double lse = 0.69314718055994530942 * (static_cast<double>(red.mc) + log2(red.s));
+      stalled = complete() ? 0 : 1;
+      const uint64_t sb = (static_cast<uint64_t>(static_cast<uint32_t>(w[4])) << 32) | static_cast<uint32_t>(w[3]);
+      mine = RowRed{__builtin_bit_cast(double, sb), __uint_as_float(static_cast<uint32_t>(w[0])),
+                    static_cast<int>(static_cast<uint32_t>(w[1])), __uint_as_float(static_cast<uint32_t>(w[2])),
+                    static_cast<int>(static_cast<uint32_t>(w[5]))};
+    } else if (lane == P - 1) {
+      mine = RowRed{st.sum, st.max, idx, st.mref, st.rank};
+    }
+    const RowRed red = wave_red<kRelaxed>(mine);
+    stalled = wave_all(stalled, MaxOp());
+    if (lane == 0) {
+      // the sum holds the maximum's own term (at least 1/2), so float log2
+      // keeps the log-sum-exp within a few units of float rounding
+      const float lse = 0.69314718f * (red.mc + __log2f(static_cast<float>(red.s)));
       int token = red.idx;
       int bits = stalled ? VSV_FLAG_STALLED : 0;
       if (!(red.best < INFINITY) || token == INT32_MAX || !isfinite(lse)) {
@@ -543,11 +563,36 @@ __global__ __launch_bounds__(NT) void verify_greedy_rows_kernel(VerifyArgs a) {
       const uint32_t word = row_word(a, m, token, ok, bits);
       if (bits) set_flag(a, bits);
       if (a.row_token) a.row_token[r] = token;
-      if (a.row_lse) a.row_lse[r] = static_cast<float>(lse);
+      if (a.row_lse) a.row_lse[r] = lse;
       store_agent64(a.ws_row + r, tagged(tag, word));
     }
   }
   if (blockIdx.x == gridDim.x - 1) words_tail<NT>(a, tag, tail);
+}
+
+// Parts per row for the row kernel: about one part per kPartBytes of the
+// row, at most kMaxRowParts, and no more partial slots than the workspace
+// holds (R * (P - 1) <= max(R + kMaxGroups, kPartSlots)); rows too short
+// for two such parts are halved where halves give the CUs a more even count
+// of parts.
+inline int row_parts(const VerifyArgs& a, int64_t row_bytes) {
+#if VSV_FORCE_PARTS > 0
+  int P = VSV_FORCE_PARTS;
+#else
+  int P = static_cast<int>((row_bytes + kPartBytes / 2) / kPartBytes);
+#endif
+  P = P < 1 ? 1 : (P > kMaxRowParts ? kMaxRowParts : P);
+  const int64_t R = a.R > 0 ? a.R : 1;
+  const int64_t slots = R + kMaxGroups > kPartSlots ? R + kMaxGroups : kPartSlots;
+  const int64_t cap = 1 + slots / R;
+  if (P > cap) P = static_cast<int>(cap);
+  if (P == 1 && a.groups > 0 && 2 * R <= slots) {
+    // ceil(R S / CUs) / (R S / CUs) closer to 1 with S = 2 than with S = 1
+    const int64_t c = a.groups, r1 = R, r2 = 2 * R;
+    const int64_t w1 = (r1 + c - 1) / c, w2 = (r2 + c - 1) / c;
+    if (w2 * r1 < w1 * r2) P = 2;   // w2 / r2 < w1 / r1, exactly
+  }
+  return P;
 }
 
 template <typename E, bool kRelaxed>
@@ -559,17 +604,11 @@ static hipError_t launch_greedy_t(VerifyArgs a, hipStream_t s) {
     a.cpr = nvmax > 0 ? (nvmax + CH - 1) / CH : 1;
     verify_greedy_kernel<E, kGreedyThreads, kUnroll, kRelaxed><<<dim3(a.groups), dim3(kGreedyThreads), 0, s>>>(a);
   } else {
-    // halves where they even out the parts per CU, i.e. where
-    // ceil(R S / CUs) / (R S / CUs) is closer to 1 with S = 2 than with S = 1
-    // (320 EAGLE-shaped rows on 256 CUs: 25.4 -> 22.5 us)
-    a.parts = 1;
-    if (a.groups > 0 && a.R <= (1 << 29)) {
-      const int64_t c = a.groups, r1 = a.R, r2 = 2 * static_cast<int64_t>(a.R);
-      const int64_t w1 = (r1 + c - 1) / c, w2 = (r2 + c - 1) / c;
-      if (w2 * r1 < w1 * r2) a.parts = 2;   // w2 / r2 < w1 / r1, exactly
-    }
+    a.parts = row_parts(a, static_cast<int64_t>(a.V) * static_cast<int64_t>(sizeof(E)));
+    const int64_t grid = static_cast<int64_t>(a.R) * a.parts;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
     verify_greedy_rows_kernel<E, kRowThreads, kUnrollRows, kRelaxed>
-        <<<dim3(a.R * a.parts), dim3(kRowThreads), 0, s>>>(a);
+        <<<dim3(static_cast<unsigned>(grid)), dim3(kRowThreads), 0, s>>>(a);
   }
   return hipGetLastError();
 }

@@ -109,11 +109,17 @@ struct ReqRange {
   int r0, r1;
 };
 
-struct TailScratch {
-  uint32_t words[kTailStage];
+// LDS of the per-request scan: the words of the first STAGE rows, the
+// block scan's per-wave sums, and the ranges of the first NT requests
+// (staged early).
+template <int NT, int STAGE>
+struct TailScratchT {
+  static constexpr int kStage = STAGE;
+  uint32_t words[STAGE];
   int scan[16];
-  ReqRange first[1024];  // ranges of the first blockDim requests, staged early
+  ReqRange first[NT];
 };
+using TailScratch = TailScratchT<1024, kTailStage>;
 
 // The tails load the ranges of the first NT requests early and stage them
 // in LDS, so the scan never waits on a global load: on this architecture
@@ -126,8 +132,8 @@ __device__ __forceinline__ ReqRange load_range(const VerifyArgs& a, int i) {
 // was accepted): prefix-accept count, exclusive scan of (a_i + 1), scatter of
 // the emitted tokens. `word(r)` returns row r's word; `first` holds the range
 // of request tid.
-template <int NT, typename Word>
-__device__ __forceinline__ void scan_requests(const VerifyArgs& a, TailScratch& t, Word word) {
+template <int NT, typename Scratch, typename Word>
+__device__ __forceinline__ void scan_requests(const VerifyArgs& a, Scratch& t, Word word) {
   const int tid = threadIdx.x;
   int carry = 0;
   // Requests go to the threads from the top down (request base + k to thread
@@ -178,15 +184,44 @@ __device__ __forceinline__ void scan_requests(const VerifyArgs& a, TailScratch& 
 // Run by the workgroup that ends the launch when rows are handled by one
 // workgroup each: gather every row's word (the first kTailStage in LDS,
 // later ones where they are read) and run the per-request scan.
+// Gather the words of rows [0, n) into LDS: each thread loads its words
+// kGatherBatch at a time, all loads of a batch in flight together, and polls
+// again only the words not yet tagged for this call, so a thread waits one
+// round trip per batch instead of one per word.
+constexpr int kGatherBatch = 8;
 template <int NT>
-__device__ __forceinline__ void words_tail(const VerifyArgs& a, uint32_t tag, TailScratch& t) {
+__device__ __forceinline__ void gather_words(const VerifyArgs& a, uint32_t tag, uint32_t* words, int n, int& budget,
+                                             int& stalled) {
+  const int tid = threadIdx.x;
+  for (int k0 = tid; k0 < n; k0 += NT * kGatherBatch) {
+    uint64_t w[kGatherBatch];
+#pragma unroll
+    for (int b = 0; b < kGatherBatch; ++b) {
+      const int k = k0 + b * NT;
+      w[b] = load_agent64(a.ws_row + (k < n ? k : 0));
+    }
+#pragma unroll
+    for (int b = 0; b < kGatherBatch; ++b) {
+      const int k = k0 + b * NT;
+      if (k < n) {
+        uint32_t v = static_cast<uint32_t>(w[b]);
+        if (static_cast<uint32_t>(w[b] >> 32) != tag) v = poll_tagged(a.ws_row + k, tag, budget, stalled);
+        words[k] = v;
+      }
+    }
+  }
+}
+
+template <int NT, typename Scratch>
+__device__ __forceinline__ void words_tail(const VerifyArgs& a, uint32_t tag, Scratch& t) {
+  constexpr int kStage = Scratch::kStage;
   const int tid = threadIdx.x;
   t.first[tid] = load_range(a, tid);
   int stalled = 0, budget = kPollBudget;
-  const int staged = min(a.R, kTailStage);
-  for (int k = tid; k < staged; k += NT) t.words[k] = poll_tagged(a.ws_row + k, tag, budget, stalled);
+  const int staged = min(a.R, kStage);
+  gather_words<NT>(a, tag, t.words, staged, budget, stalled);
   lds_barrier();
-  if (a.R <= kTailStage)
+  if (a.R <= kStage)
     scan_requests<NT>(a, t, [&](int row) -> uint32_t { return t.words[row]; });
   else
     scan_requests<NT>(a, t, [&](int row) -> uint32_t {
