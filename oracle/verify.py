@@ -230,6 +230,84 @@ def verify_greedy(logits, dtype, vocab, offsets, owner, drafts, relaxed_topk=1):
                 out_tokens=toks, row_token=row_token, row_lse=row_lse)
 
 
+def relaxed_accepts(x, j, generated, draft, topk=1, margin=0.0, from_position=0, after_tokens=0,
+                    protected=()):
+    """Whether greedy verification accepts `draft` at draft position j of a
+    request that has generated `generated` tokens, given its target row x.
+
+    The pages name these switches without formulas (vllm-hust-vspec 0.13.0
+    README: "Launch" sets a confidence-accept margin of 5.25 and says it
+    relaxes greedy acceptance; "General parameters" lists the margin, its
+    from-position and after-tokens gates and protected token ids; "EAGLE
+    features" lists top-K relaxed acceptance, its after-tokens gate and the
+    strict prefix). The reading taken here:
+      * a draft equal to the target's greedy token is always accepted;
+      * otherwise relaxation applies only at positions j >= from_position
+        where generated + j >= after_tokens (the first tokens of an answer
+        and of a window stay strict), and only when neither the draft nor
+        the greedy token is protected;
+      * where it applies, top-K accepts a draft whose rank is below topk
+        (topk > 1), and the margin accepts a draft whose logit lies less than
+        `margin` below the row maximum (margin > 0), i.e. whose target
+        log-probability is within `margin` of the greedy token's.
+    With topk = 1 and margin = 0 every draft is verified strictly.
+    """
+    V = x.shape[0]
+    if not 0 <= draft < V:
+        return False
+    g = greedy_token(x)
+    if draft == g:
+        return True
+    if j < from_position or generated + j < after_tokens:
+        return False
+    if draft in protected or g in protected:
+        return False
+    if topk > 1 and rank_of(x, draft) < topk:
+        return True
+    if margin > 0.0 and float(np.max(x)) - float(x[draft]) < margin:
+        return True
+    return False
+
+
+def verify_greedy_relaxed(logits, dtype, vocab, offsets, owner, drafts, topk=1, margin=0.0, from_position=0,
+                          after_tokens=0, generated=None, protected=()):
+    """Greedy verification with the relaxed acceptance variants of
+    relaxed_accepts. generated[i] is request i's count of generated tokens
+    (None: 0 for all); margin is read as the float32 value the device takes.
+    An accepted draft is emitted as itself; the replacement and bonus are
+    the greedy tokens."""
+    R = logits.shape[0]
+    off, B = _check_layout(offsets, owner, R)
+    drafts = np.asarray(drafts, dtype=np.int64)
+    if drafts.shape[0] != R - B:
+        raise ValueError("need R - B draft tokens")
+    if not 1 <= topk <= vocab:
+        raise ValueError("topk must lie in [1, V]")
+    margin = float(np.float32(margin))
+    gen = np.zeros(B, dtype=np.int64) if generated is None else np.asarray(generated, dtype=np.int64)
+    prot = set(int(t) for t in protected)
+    row_token = np.zeros(R, dtype=np.int32)
+    row_lse = np.zeros(R, dtype=np.float64)
+    results = []
+    for i in range(B):
+        r0, r1 = int(off[i]), int(off[i + 1])
+        K = r1 - r0 - 1
+        d = drafts[r0 - i: r0 - i + K]
+        accepts = []
+        for j in range(K + 1):
+            x = row_f64(logits, dtype, r0 + j, vocab)
+            check_row(x)
+            row_token[r0 + j] = greedy_token(x)
+            row_lse[r0 + j] = logsumexp(x)
+            if j < K:
+                accepts.append(relaxed_accepts(x, j, int(gen[i]), int(d[j]), topk, margin, from_position,
+                                               after_tokens, prot))
+        results.append(_prefix_accept(row_token[r0: r1], accepts, d))
+    acc, nxt, out_off, toks = _compact(B, results)
+    return dict(accepted_len=acc, next_token=nxt, out_offsets=out_off,
+                out_tokens=toks, row_token=row_token, row_lse=row_lse)
+
+
 def verify_sampled(logits, dtype, vocab, offsets, owner, drafts, temperature,
                    top_k, top_p, min_p, seed, offset, uniforms=None):
     """Sampled (or mixed) target verification of a packed batch.

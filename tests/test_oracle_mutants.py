@@ -145,6 +145,24 @@ MUTANTS = [
     ("goodput_counts_inclusive", "goodput.py",
      "accepted = np.array([int((a > j).sum())",
      "accepted = np.array([int((a >= j).sum())"),
+    ("relaxed_margin_inclusive", "verify.py",
+     "float(np.max(x)) - float(x[draft]) < margin",
+     "float(np.max(x)) - float(x[draft]) <= margin"),
+    ("relaxed_margin_against_min", "verify.py",
+     "float(np.max(x)) - float(x[draft]) < margin",
+     "float(x[draft]) - float(np.min(x)) < margin"),
+    ("relaxed_from_position_off_by_one", "verify.py",
+     "if j < from_position or generated + j < after_tokens:",
+     "if j <= from_position or generated + j < after_tokens:"),
+    ("relaxed_after_tokens_off_by_one", "verify.py",
+     "if j < from_position or generated + j < after_tokens:",
+     "if j < from_position or generated + j + 1 < after_tokens:"),
+    ("relaxed_protects_draft_only", "verify.py",
+     "if draft in protected or g in protected:",
+     "if draft in protected:"),
+    ("relaxed_gate_ignores_generated", "verify.py",
+     "if j < from_position or generated + j < after_tokens:",
+     "if j < from_position or j < after_tokens:"),
     ("margin_topp_farther_boundary", "verify.py",
      "topp_margin = min(topp_margin, top_p - cn[L - 1])",
      "topp_margin = max(topp_margin, top_p - cn[L - 1])"),

@@ -492,3 +492,109 @@ def test_margins_for_top_k_then_top_p_then_min_p():
     cs = np.cumsum(w[S]) / np.sum(w[S])
     n = int(np.flatnonzero(cs > 0.25)[0])
     assert um == pytest.approx(min(cs[n] - 0.25, 0.25 - cs[n - 1]) if n else cs[n] - 0.25, rel=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Relaxed acceptance variants (margin, position and token gates, protected
+# ids): what the reading fixes, stated independently of the oracle's code.
+
+
+def _tiny_accept_set(xs, margin, protected=()):
+    """Drafts accepted at an ungated position, by plain enumeration: the
+    lowest index of the maximum, and every other token whose value lies
+    strictly less than `margin` below the maximum, unless it or the greedy
+    token is protected."""
+    m = max(xs)
+    g = min(t for t in range(len(xs)) if xs[t] == m)
+    out = {g}
+    if g in protected:
+        return out
+    for t in range(len(xs)):
+        if t not in protected and margin > 0 and (m - xs[t]) < margin:
+            out.add(t)
+    return out
+
+
+def test_relaxed_defaults_are_strict():
+    for key, kw in (("tiny", {}), ("relaxed", dict(B=6, V=700))):
+        wl = synth.make(key, **kw)
+        a = oracle.verify_greedy(wl.logits, wl.dtype, wl.V, wl.offsets, wl.owner, wl.drafts)
+        b = oracle.verify_greedy_relaxed(wl.logits, wl.dtype, wl.V, wl.offsets, wl.owner, wl.drafts)
+        for k in a:
+            assert np.array_equal(a[k], b[k]), k
+
+
+def test_relaxed_topk_alone_is_top_k_acceptance():
+    wl = synth.make("relaxed", B=8, V=900)
+    for K in (2, 4, 9):
+        a = oracle.verify_greedy(wl.logits, wl.dtype, wl.V, wl.offsets, wl.owner, wl.drafts, relaxed_topk=K)
+        b = oracle.verify_greedy_relaxed(wl.logits, wl.dtype, wl.V, wl.offsets, wl.owner, wl.drafts, topk=K)
+        for k in a:
+            assert np.array_equal(a[k], b[k]), (K, k)
+
+
+def test_margin_worked_row():
+    # maximum 3.0 at tokens 1 and 3 (the lowest index, 1, is greedy); token 2
+    # lies 0.5 below it, token 0 2.0 below
+    x = np.array([1.0, 3.0, 2.5, 3.0])
+    acc = lambda m: {d for d in range(4) if oracle.relaxed_accepts(x, 0, 0, d, margin=m)}
+    assert acc(0.0) == {1}
+    assert acc(0.5) == {1, 3}               # 0.5 below is not strictly within 0.5
+    assert acc(0.500001) == {1, 2, 3}
+    assert acc(2.0) == {1, 2, 3}
+    assert acc(2.000001) == {0, 1, 2, 3}
+    assert {d for d in range(4) if oracle.relaxed_accepts(x, 0, 0, d, margin=5.25, protected={3})} == {0, 1, 2}
+    assert {d for d in range(4) if oracle.relaxed_accepts(x, 0, 0, d, margin=5.25, protected={1})} == {1}
+    assert not oracle.relaxed_accepts(x, 0, 0, 4, margin=100.0)   # out of range
+
+
+def test_margin_brute_force_tiny_vocab():
+    rng = np.random.default_rng(150)
+    for trial in range(300):
+        V = int(rng.integers(1, 12))
+        xs = [float(v) for v in rng.integers(-6, 7, size=V) * 0.5]
+        margin = float(rng.choice([0.0, 0.25, 0.5, 1.0, 1.75, 5.25]))
+        prot = set(int(t) for t in rng.choice(V, size=int(rng.integers(0, 3)), replace=True)) if V else set()
+        x = np.array(xs)
+        got = {d for d in range(V) if oracle.relaxed_accepts(x, 3, 10, d, margin=margin, protected=prot)}
+        assert got == _tiny_accept_set(xs, margin, prot), (xs, margin, prot)
+
+
+def test_margin_huge_accepts_every_draft_like_top_v():
+    wl = synth.make("relaxed", B=5, V=333)
+    a = oracle.verify_greedy(wl.logits, wl.dtype, wl.V, wl.offsets, wl.owner, wl.drafts, relaxed_topk=wl.V)
+    b = oracle.verify_greedy_relaxed(wl.logits, wl.dtype, wl.V, wl.offsets, wl.owner, wl.drafts, margin=1e30)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    assert np.array_equal(b["accepted_len"], np.diff(wl.offsets) - 1)
+
+
+def test_relaxed_gates_and_protection_on_a_request():
+    """One request of four drafts: drafts 0 and 1 are the greedy tokens,
+    drafts 2 and 3 are other tokens within the margin. Where relaxation is
+    allowed only from position p (or from output token N), the accepted
+    length is the first gated-off position of a non-greedy draft."""
+    V = 10
+    rows = np.zeros((5, V), dtype=np.float32)
+    for j in range(5):
+        rows[j] = np.arange(V, dtype=np.float32) * 0.1
+        rows[j, j] = 5.0                     # greedy token of row j is j
+        rows[j, 9] = 4.5                     # 0.5 below the maximum
+    drafts = np.array([0, 1, 9, 9], dtype=np.int32)
+    off, own = np.array([0, 5]), np.zeros(5, dtype=np.int32)
+    run = lambda **kw: oracle.verify_greedy_relaxed(rows, oracle.F32, V, off, own, drafts, **kw)
+    assert run()["accepted_len"][0] == 2                         # strict
+    assert run(margin=1.0)["accepted_len"][0] == 4
+    assert run(margin=1.0)["next_token"][0] == 4                 # bonus = greedy token of the last row
+    assert list(run(margin=1.0)["out_tokens"]) == [0, 1, 9, 9, 4]
+    assert run(margin=1.0, from_position=2)["accepted_len"][0] == 4
+    assert run(margin=1.0, from_position=3)["accepted_len"][0] == 2
+    assert run(margin=1.0, after_tokens=5, generated=[3])["accepted_len"][0] == 4   # 3 + 2 >= 5
+    assert run(margin=1.0, after_tokens=5, generated=[2])["accepted_len"][0] == 2   # 2 + 2 < 5
+    assert run(margin=1.0, protected=[9])["accepted_len"][0] == 2
+    assert run(margin=1.0, protected=[2])["accepted_len"][0] == 2   # greedy token of row 2 protected
+    assert run(margin=1.0, protected=[3])["accepted_len"][0] == 3   # ... of row 3
+    assert run(margin=0.4)["accepted_len"][0] == 2
+    assert run(topk=2)["accepted_len"][0] == 4                   # token 9 ranks second
+    assert run(topk=2, after_tokens=4, generated=[1])["accepted_len"][0] == 2   # 1 + 2 < 4
+    assert run(topk=2, after_tokens=4, generated=[2])["accepted_len"][0] == 4   # 2 + 2 >= 4
