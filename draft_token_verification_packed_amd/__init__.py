@@ -7,6 +7,8 @@ library is missing or cannot be loaded, every call raises.
 
 Entry points mirror the C ABI in include/vspec_verify.h:
     verify_greedy(logits, row_offsets, row_owner, draft_tokens, relaxed_topk=1)
+    verify_greedy_relaxed(logits, row_offsets, row_owner, draft_tokens, topk=1, margin=0.0,
+                          from_position=0, after_tokens=0, generated=None, protected_ids=None)
     verify_greedy_static(logits, row_offsets, row_owner, draft_tokens, relaxed_topk=1)
     verify_sampled(logits, row_offsets, row_owner, draft_tokens,
                    temperature, top_k, top_p, min_p, seed, offset=0)
@@ -57,7 +59,16 @@ class Outputs(ctypes.Structure):
                 ("error_flag", ctypes.c_void_p), ("slow_rows", ctypes.c_void_p)]
 
 
-SYMBOLS = ("vsv_workspace_bytes", "vsv_workspace_init", "vsv_verify_greedy", "vsv_verify_greedy_static",
+class Relax(ctypes.Structure):
+    _fields_ = [("topk", ctypes.c_int32), ("margin", ctypes.c_float), ("from_position", ctypes.c_int32),
+                ("after_tokens", ctypes.c_int32), ("generated", ctypes.c_void_p), ("protected_ids", ctypes.c_void_p),
+                ("num_protected", ctypes.c_int32)]
+
+
+MAX_PROTECTED = 256
+
+SYMBOLS = ("vsv_workspace_bytes", "vsv_workspace_init", "vsv_verify_greedy", "vsv_verify_greedy_relaxed",
+           "vsv_verify_greedy_static",
            "vsv_verify_sampled",
            "vsv_verify_probabilistic", "vsv_draft_confidence", "vsv_allocate_verify", "vsv_goodput_init", "vsv_goodput_observe",
            "vsv_goodput_step", "vsv_goodput_select", "vsv_status_string", "vsv_version")
@@ -93,6 +104,9 @@ def lib():
     L.vsv_workspace_init.restype = ctypes.c_int
     L.vsv_verify_greedy.argtypes = [ctypes.POINTER(Batch), i32, ctypes.POINTER(Outputs), vp, sz, vp]
     L.vsv_verify_greedy.restype = ctypes.c_int
+    L.vsv_verify_greedy_relaxed.argtypes = [ctypes.POINTER(Batch), ctypes.POINTER(Relax), ctypes.POINTER(Outputs),
+                                            vp, sz, vp]
+    L.vsv_verify_greedy_relaxed.restype = ctypes.c_int
     L.vsv_verify_greedy_static.argtypes = [ctypes.POINTER(Batch), i32, ctypes.POINTER(Outputs), vp]
     L.vsv_verify_greedy_static.restype = ctypes.c_int
     L.vsv_verify_sampled.argtypes = [ctypes.POINTER(Batch), vp, vp, vp, vp, u64, u64,
@@ -254,6 +268,30 @@ def verify_greedy(logits, row_offsets, row_owner, draft_tokens, relaxed_topk=1, 
     _keep_alive(stream, logits, row_offsets, row_owner, draft_tokens, ws)
     _check(lib().vsv_verify_greedy(ctypes.byref(batch), int(relaxed_topk), ctypes.byref(outs),
                                    _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def verify_greedy_relaxed(logits, row_offsets, row_owner, draft_tokens, topk=1, margin=0.0, from_position=0,
+                          after_tokens=0, generated=None, protected_ids=None, vocab=None, ws=None, stream=None):
+    """Greedy verification with relaxed acceptance (vsv_verify_greedy_relaxed):
+    top-K and/or a logit margin, gated by draft position and by each
+    request's generated-token count (`generated`, int32 [B] device or None),
+    never relaxing a protected token (`protected_ids`, int32 device vector
+    or None). Returns a dict of device tensors."""
+    batch, outs, out, B, R = _prepare(logits, row_offsets, row_owner, draft_tokens, vocab, stream)
+    if generated is not None:
+        _vec(generated, B, torch.int32, "generated")
+    nprot = 0
+    if protected_ids is not None:
+        nprot = protected_ids.numel()
+        if nprot:
+            _vec(protected_ids, nprot, torch.int32, "protected_ids")
+    relax = Relax(int(topk), float(margin), int(from_position), int(after_tokens), _ptr(generated),
+                  _ptr(protected_ids) if nprot else None, int(nprot))
+    ws = workspace(B, R, False, logits.device, stream) if ws is None else ws
+    _keep_alive(stream, logits, row_offsets, row_owner, draft_tokens, generated, protected_ids, ws)
+    _check(lib().vsv_verify_greedy_relaxed(ctypes.byref(batch), ctypes.byref(relax), ctypes.byref(outs), _ptr(ws),
+                                           ws.numel(), _stream(stream)))
     return out
 
 

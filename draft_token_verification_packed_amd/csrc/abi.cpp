@@ -1,6 +1,7 @@
 // C ABI entry points: host-side validation, workspace carving and launch.
 // Nothing here synchronises, allocates or reads device memory.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "allocate.hpp"
@@ -108,6 +109,31 @@ vsv_status vsv_verify_greedy(const vsv_batch* batch, int32_t relaxed_topk, const
   if (st != VSV_OK || empty) return st;
   if (relaxed_topk < 1 || relaxed_topk > batch->vocab) return VSV_EINVAL;
   a.relaxed_k = relaxed_topk;
+  return vsv::launch_verify_greedy(a, stream) == hipSuccess ? VSV_OK : VSV_EHIP;
+}
+
+vsv_status vsv_verify_greedy_relaxed(const vsv_batch* batch, const vsv_relax* relax, const vsv_outputs* out,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!relax) return VSV_EINVAL;
+  VerifyArgs a;
+  bool empty = false;
+  const vsv_status st = prepare(batch, out, workspace, workspace_bytes, 0, &a, &empty);
+  if (st != VSV_OK || empty) return st;
+  if (relax->topk < 1 || relax->topk > batch->vocab) return VSV_EINVAL;
+  if (!(relax->margin >= 0.f) || !(relax->margin < INFINITY)) return VSV_EINVAL;
+  if (relax->from_position < 0 || relax->after_tokens < 0) return VSV_EINVAL;
+  if (relax->num_protected < 0 || relax->num_protected > VSV_MAX_PROTECTED) return VSV_EINVAL;
+  if (relax->num_protected > 0 && !relax->protected_ids) return VSV_EINVAL;
+  a.relaxed_k = relax->topk;
+  a.margin = relax->margin;
+  a.from_pos = relax->from_position;
+  a.after_tok = relax->after_tokens;
+  a.generated = relax->generated;
+  a.prot = relax->num_protected > 0 ? relax->protected_ids : nullptr;
+  a.nprot = relax->num_protected;
+  // top-K alone needs none of the extra decision inputs
+  a.relax_var = (relax->margin > 0.f || relax->from_position > 0 || relax->after_tokens > 0 ||
+                 relax->num_protected > 0) ? 1 : 0;
   return vsv::launch_verify_greedy(a, stream) == hipSuccess ? VSV_OK : VSV_EHIP;
 }
 

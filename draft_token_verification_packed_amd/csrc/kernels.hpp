@@ -68,6 +68,14 @@ struct VerifyArgs {
   const int32_t* owner;
   const int32_t* drafts;
   int32_t relaxed_k;
+  // relaxed acceptance beyond top-K (greedy only): margin, gates, protected
+  // ids; relax_var is set when any of them is in force
+  int32_t relax_var;
+  float margin;
+  int32_t from_pos, after_tok;
+  const int32_t* generated;
+  const int32_t* prot;
+  int32_t nprot;
   int32_t groups;       // greedy: persistent workgroups (one per CU)
   int32_t cpr;          // greedy: chunks per row (set at launch)
   int32_t parts;        // greedy, one workgroup per row part: 1 or 2 parts per row

@@ -463,6 +463,9 @@ template <typename E, int NT, int U, bool kRelaxed>
 __global__ __launch_bounds__(NT) void verify_greedy_rows_kernel(VerifyArgs a) {
   __shared__ LeanScratch<NT> scr;
   __shared__ TailScratch tail;
+  __shared__ int s_prot[VSV_MAX_PROTECTED];
+  static_assert(VSV_MAX_PROTECTED % NT == 0 || NT % VSV_MAX_PROTECTED == 0, "protected ids per thread");
+  constexpr int kProtPer = VSV_MAX_PROTECTED >= NT ? VSV_MAX_PROTECTED / NT : 1;
   constexpr int N = Elem<E>::kVec;
   const int P = a.parts;
   const int r = static_cast<int>(blockIdx.x) / P;
@@ -491,12 +494,39 @@ __global__ __launch_bounds__(NT) void verify_greedy_rows_kernel(VerifyArgs a) {
   partial_init(p);
   GroupKeep<U> keep{};
   constexpr float kLog2e = 1.4426950408889634f;
-  // element indices inside the part are relative to e0, so the draft's is too
+  // The last part gathers what the row's decision needs while the first
+  // loads are in flight (values only, used after the stream): the row's
+  // metadata and, for the relaxed variants, the draft's logit, the
+  // request's generated-token count and its share of the protected ids.
+  float xm = xd;
+  int gen = 0;
+  int prot_reg[kProtPer];
+#pragma unroll
+  for (int k = 0; k < kProtPer; ++k) prot_reg[k] = -1;
   auto hook = [&]() {
-    if (!kRelaxed && last) m = load_meta(a, r, owner);
+    if (last) {
+      if (!kRelaxed) m = load_meta(a, r, owner);
+      if (a.relax_var) {
+        if (!kRelaxed && m.draft >= 0 && m.draft < a.V) xm = Elem<E>::at(row, m.draft);
+        if (a.generated && m.req >= 0) gen = a.generated[m.req];
+#pragma unroll
+        for (int k = 0; k < kProtPer; ++k) {
+          const int q = static_cast<int>(threadIdx.x) + k * NT;
+          if (q < a.nprot) prot_reg[k] = a.prot[q];
+        }
+      }
+    }
   };
+  // element indices inside the part are relative to e0, so the draft's is too
   stream_row<E, NT, U, kRelaxed, GroupKeep<U>, decltype(hook), true>(row + e0, e1 - e0, kLog2e, xd,
                                                                       kRelaxed ? m.draft - e0 : 0, p, keep, hook);
+  if (last && a.relax_var) {
+#pragma unroll
+    for (int k = 0; k < kProtPer; ++k) {
+      const int q = static_cast<int>(threadIdx.x) + k * NT;
+      if (q < VSV_MAX_PROTECTED) s_prot[q] = prot_reg[k];   // ordered by the epilogue's barriers
+    }
+  }
   const RowStats st = finish_row_lean<E, NT, U, kRelaxed>(p, scr, keep, row + e0, e1 - e0);
   const int idx = st.argmax == INT32_MAX ? INT32_MAX : e0 + st.argmax;
   uint64_t* slots = a.ws_part + static_cast<size_t>(r) * (P - 1) * kPartStatWords;
@@ -549,6 +579,14 @@ __global__ __launch_bounds__(NT) void verify_greedy_rows_kernel(VerifyArgs a) {
     }
     const RowRed red = wave_red<kRelaxed>(mine);
     stalled = wave_all(stalled, MaxOp());
+    // relaxed variants: is the draft or the greedy token protected? (every
+    // lane checks its share of the ids)
+    bool prot = false;
+    if (a.relax_var && a.nprot > 0) {
+      bool hit = false;
+      for (int k = lane; k < a.nprot; k += kWave) hit |= s_prot[k] == m.draft || s_prot[k] == red.idx;
+      prot = __builtin_amdgcn_ballot_w64(hit) != 0;
+    }
     if (lane == 0) {
       // the sum holds the maximum's own term (at least 1/2), so float log2
       // keeps the log-sum-exp within a few units of float rounding
@@ -559,7 +597,8 @@ __global__ __launch_bounds__(NT) void verify_greedy_rows_kernel(VerifyArgs a) {
         bits |= VSV_FLAG_LOGITS;
         if (token == INT32_MAX) token = 0;
       }
-      const bool ok = kRelaxed ? (red.rank < a.relaxed_k) : (m.draft == token);
+      const bool ok = a.relax_var ? relaxed_ok(a, m, token, red.best, xm, red.rank, prot, gen)
+                                  : (kRelaxed ? (red.rank < a.relaxed_k) : (m.draft == token));
       const uint32_t word = row_word(a, m, token, ok, bits);
       if (bits) set_flag(a, bits);
       if (a.row_token) a.row_token[r] = token;
@@ -599,7 +638,8 @@ template <typename E, bool kRelaxed>
 static hipError_t launch_greedy_t(VerifyArgs a, hipStream_t s) {
   constexpr int N = Elem<E>::kVec;
   constexpr int CH = kWave * kUnroll;
-  if (greedy_persistent(a.R, a.groups)) {
+  // the relaxed variants decide rows in the row kernel's merging lane only
+  if (!a.relax_var && greedy_persistent(a.R, a.groups)) {
     const int nvmax = a.V / N;
     a.cpr = nvmax > 0 ? (nvmax + CH - 1) / CH : 1;
     verify_greedy_kernel<E, kGreedyThreads, kUnroll, kRelaxed><<<dim3(a.groups), dim3(kGreedyThreads), 0, s>>>(a);

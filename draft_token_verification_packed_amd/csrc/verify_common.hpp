@@ -99,6 +99,21 @@ __device__ __forceinline__ uint32_t row_word(const VerifyArgs& a, const RowMeta&
   return static_cast<uint32_t>(token);
 }
 
+// Relaxed greedy acceptance of row (request m.req, draft position m.j):
+// the greedy token always passes; another draft passes only past the
+// position and generated-token gates, when neither it nor the greedy token
+// is protected, and when top-K (rank below relaxed_k) or the margin
+// (max - x[d] < margin, in double) holds. Out-of-range drafts are rejected
+// by row_word.
+__device__ __forceinline__ bool relaxed_ok(const VerifyArgs& a, const RowMeta& m, int token, float best, float xd,
+                                           int rank, bool prot, int gen) {
+  if (m.draft == token) return true;
+  if (m.j < a.from_pos || static_cast<int64_t>(gen) + m.j < static_cast<int64_t>(a.after_tok)) return false;
+  if (prot) return false;
+  if (a.relaxed_k > 1 && rank < a.relaxed_k) return true;
+  return a.margin > 0.f && static_cast<double>(best) - static_cast<double>(xd) < static_cast<double>(a.margin);
+}
+
 // ---------------------------------------------------------------- scan
 
 // Rows whose words the scan stages in LDS.

@@ -129,6 +129,44 @@ vsv_status vsv_verify_greedy(const vsv_batch* batch, int32_t relaxed_topk,
                              const vsv_outputs* out, void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
 
+/* Relaxed greedy acceptance, as the serving switches name it without a
+ * formula (vllm-hust-vspec 0.13.0 README: section "Launch" sets a
+ * confidence-accept margin of 5.25 and says it relaxes greedy acceptance,
+ * output no longer matching the target alone token for token; section
+ * "General parameters" lists the margin, its from-position and after-tokens
+ * gates and protected token ids; section "EAGLE features" lists top-K
+ * relaxed acceptance with an after-tokens gate and the strict prefix).
+ * A draft equal to the row's greedy token is always accepted. Any other
+ * draft d at draft position j of request i is accepted only if
+ * j >= from_position, generated[i] + j >= after_tokens, neither d nor the
+ * greedy token is in protected_ids, and either top-K holds (topk > 1 and
+ * rank(d) < topk, rank in the order value desc, index asc) or the margin
+ * holds (margin > 0 and max - x[d] < margin, evaluated in double from the
+ * float values: the draft's target log-probability lies within `margin` of
+ * the greedy token's). An accepted draft is emitted as itself; replacement
+ * and bonus are greedy tokens. topk = 1, margin = 0 is strict top-1. */
+#define VSV_MAX_PROTECTED 256
+typedef struct {
+  int32_t topk;                 /* >= 1; 1: no top-K relaxation                     */
+  float margin;                 /* >= 0, finite; 0: no margin relaxation            */
+  int32_t from_position;        /* >= 0: first draft position that may relax        */
+  int32_t after_tokens;         /* >= 0: generated[i] + j must reach it to relax    */
+  const int32_t* generated;     /* [B] device: tokens request i has generated so    */
+                                /* far; NULL counts 0 for every request             */
+  const int32_t* protected_ids; /* [num_protected] device, any order; NULL if none  */
+  int32_t num_protected;        /* 0 .. VSV_MAX_PROTECTED                           */
+} vsv_relax;
+
+/* Greedy verification with relaxed acceptance (vsv_relax above); the rest
+ * as vsv_verify_greedy, with the same workspace. Errors: as
+ * vsv_verify_greedy, plus VSV_EINVAL for a NULL relax, topk outside
+ * [1, vocab], a negative or non-finite margin, negative gates,
+ * num_protected outside [0, VSV_MAX_PROTECTED] or NULL protected_ids with
+ * num_protected > 0. */
+vsv_status vsv_verify_greedy_relaxed(const vsv_batch* batch, const vsv_relax* relax,
+                                     const vsv_outputs* out, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+
 /* Greedy verification that allocates nothing, for callers that cannot
  * allocate device memory or pass a workspace: code under HIP graph capture,
  * tight serving loops, harnesses that forbid allocation. Same arguments,

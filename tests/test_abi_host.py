@@ -178,3 +178,26 @@ def test_static_entry_point_rejects_batches_beyond_its_scratch(L):
     assert L.vsv_verify_greedy_static(None, 1, ctypes.byref(out), None) == 1
     text = open(HEADER).read()
     assert "#define VSV_STATIC_MAX_ROWS %d" % vsv.STATIC_MAX_ROWS in text
+
+
+def test_relaxed_validation(L):
+    """vsv_verify_greedy_relaxed refuses bad relaxation arguments before any
+    launch (the batch itself is valid, with dummy pointers)."""
+    ws = 0x100000
+    out = vsv.Outputs(0x50000, 0x60000, 0x70000, 0x80000, None, None, None, None)
+    b = _batch()
+    nbytes = L.vsv_workspace_bytes(4, 20, 0)
+
+    def call(**kw):
+        r = dict(topk=1, margin=0.0, from_position=0, after_tokens=0, generated=None, protected_ids=None,
+                 num_protected=0)
+        r.update(kw)
+        return L.vsv_verify_greedy_relaxed(ctypes.byref(b), ctypes.byref(vsv.Relax(**r)), ctypes.byref(out), ws,
+                                           nbytes, None)
+    assert L.vsv_verify_greedy_relaxed(ctypes.byref(b), None, ctypes.byref(out), ws, nbytes, None) == 1
+    assert call(topk=0) == 1 and call(topk=1025) == 1
+    assert call(margin=-1.0) == 1 and call(margin=float("nan")) == 1 and call(margin=float("inf")) == 1
+    assert call(from_position=-1) == 1 and call(after_tokens=-2) == 1
+    assert call(num_protected=vsv.MAX_PROTECTED + 1, protected_ids=0x90000) == 1
+    assert call(num_protected=3) == 1                    # ids missing
+    assert "#define VSV_MAX_PROTECTED %d" % vsv.MAX_PROTECTED in open(HEADER).read()
