@@ -416,7 +416,8 @@ struct RowStats {
 // per wave: the terms are positive, so the wave sum's relative error stays
 // below 64 float roundings; float64 across waves), and takes the lowest
 // index of the maximum, which only lanes holding the block maximum search
-// for in their kept group. Every thread receives the result.
+// for in their kept group (NoKeep: no index). Every thread receives the
+// result.
 template <typename E, int NT, int U, bool kRank, typename Keep>
 __device__ __forceinline__ RowStats finish_row_lean(const RowPartial& p, LeanScratch<NT>& sc, const Keep& keep,
                                                     const E* __restrict__ row, int V) {
@@ -438,11 +439,13 @@ __device__ __forceinline__ RowStats finish_row_lean(const RowPartial& p, LeanScr
     mg = fmaxf(mg, sc.mc[k]);
   }
   int idx = INT32_MAX;
-  if (p.best == m) {
-    const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
-    int head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(E));
-    if (head > V) head = V;
-    idx = lane_argmax<E, NT, U>(p, keep, head, (V - head) / N);
+  if constexpr (Keep::kOn) {
+    if (p.best == m) {
+      const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
+      int head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(E));
+      if (head > V) head = V;
+      idx = lane_argmax<E, NT, U>(p, keep, head, (V - head) / N);
+    }
   }
   float sl = (p.mc > -FLT_MAX) ? static_cast<float>(ldexp(p.s, static_cast<int>(fmaxf(p.mc - mg, -2000.f)))) : 0.f;
   if (p.bad) sl = __builtin_nanf("");   // the row is flagged through its sum

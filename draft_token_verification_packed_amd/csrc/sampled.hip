@@ -39,12 +39,13 @@ __device__ __forceinline__ void sampled_kernel_row(const VerifyArgs& a, uint32_t
     partial_init(p);
     GroupKeep<U> keep{};
     constexpr float kLog2e = 1.4426950408889634f;
-    stream_row<E, NT, U, false>(row, a.V, kLog2e, INFINITY, 0, p, keep);
+    stream_row<E, NT, U, false, GroupKeep<U>, NoHook, true>(row, a.V, kLog2e, INFINITY, 0, p, keep);
     after_stream();
-    const RowResult res = finish_row<E, NT, U, false, true>(p, L.rs, keep, row, a.V);
+    const RowStats res = finish_row_lean<E, NT, U, false>(p, L.ls, keep, row, a.V);
     token = res.argmax;
-    lse = res.lse;
-    if (!(res.max < INFINITY) || token == INT32_MAX || !isfinite(res.lse)) bits |= VSV_FLAG_LOGITS;
+    // float log2 of a sum holding the maximum's own term (at least 1/2)
+    lse = 0.69314718f * (res.mref + __log2f(static_cast<float>(res.sum)));
+    if (!(res.max < INFINITY) || token == INT32_MAX || !isfinite(lse)) bits |= VSV_FLAG_LOGITS;
     if (token == INT32_MAX) token = 0;
     if (m.req >= 0 && !(T >= 0.f)) bits |= VSV_FLAG_PARAMS;
   }

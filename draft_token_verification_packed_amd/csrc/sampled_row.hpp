@@ -93,6 +93,7 @@ template <int NT> struct SampledLds {
   int red_i[NW];
   double red_d[2 * NW];
   RowScratch<NT> rs;
+  LeanScratch<NT> ls;
   int row_next;  // the workgroup's next row (row queue)
   int last;      // this workgroup finished the call's last row
 };
@@ -1136,9 +1137,11 @@ __device__ __forceinline__ SampledOut sampled_row(const VerifyArgs& a, const E* 
   const VmPlan plan = stream_sampled<E, NT, U>(row, a.V, c, p, L);
   after_stream();
   const NoKeep nokeep;
-  const RowResult res = finish_row<E, NT, U, false, false>(p, L.rs, nokeep, row, a.V);
-  out.lse = res.lse;
-  if (!(res.max < INFINITY) || !(res.max > -INFINITY) || !isfinite(res.lse)) out.bits |= VSV_FLAG_LOGITS;
+  const RowStats res = finish_row_lean<E, NT, U, false>(p, L.ls, nokeep, row, a.V);
+  // the sum holds the maximum's own term (at least 1/2), so float log2
+  // keeps the log-sum-exp within a few units of float rounding
+  out.lse = 0.69314718f * (res.mref + __log2f(static_cast<float>(res.sum)));
+  if (!(res.max < INFINITY) || !(res.max > -INFINITY) || !isfinite(out.lse)) out.bits |= VSV_FLAG_LOGITS;
   const float m = res.max;
 
   // Capture threshold: T * kZcap below the maximum (weights under e^-kZcap
