@@ -400,6 +400,7 @@ def bench_probabilistic(args, vsv, torch):
     torch.cuda.synchronize()
     ms = ev[0].elapsed_time(ev[1]) / steps
     assert int(out["error_flag"].item()) == 0
+    slow = int(out["slow_rows"].item())     # rows of the last launch that took the whole-row path
     nbytes = (R + wl.D) * V * 2     # every target and draft row read once
     achieved = nbytes / (ms * 1e-3) / 1e9
     line = dict(metric="probabilistic-draft verified rows/sec, B=512 K=7 V=152064", value=R / (ms * 1e-3),
@@ -407,7 +408,7 @@ def bench_probabilistic(args, vsv, torch):
                 scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
                 config=dict(workload="probabilistic-draft verify, " + wl.name.split(", ", 1)[1], B=B, R=R, D=wl.D,
                             V=V, draft_temperature="the request's target temperature", data_seed=wl._spec["data_seed"],
-                            philox_seed=wl.seed),
+                            philox_seed=wl.seed, slow_rows_last_launch=slow),
                 roofline=dict(bound="hbm", kernel="verify_probabilistic_kernel", achieved=achieved,
                               peak=HBM_PEAK_GBPS, unit="GB/s", frac=achieved / HBM_PEAK_GBPS, traffic=None,
                               bytes_per_launch=nbytes, launch_us=ms * 1e3,

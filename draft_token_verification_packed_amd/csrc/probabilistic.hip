@@ -33,8 +33,6 @@ namespace vsv {
 
 namespace {
 
-constexpr int kBands = 64;  // bands of z = (x - m) / T, a quarter wide, for the top-p head
-
 // Visits every element e = threadIdx.x + k NT of a row as f(e, value),
 // with the loads of kBatch steps issued before any is used. These loops run
 // over rows already in the caches; with one load per iteration each thread
@@ -132,41 +130,101 @@ struct DraftLaw {
   }
 };
 
-// One pass over the draft row: each thread keeps a running maximum and the
-// float64 sum of exp((y - max) / Td) rescaled when its maximum grows (for
-// Td = 0, the lowest index of its maximum). Returns false when the row has
-// a NaN or no finite maximum.
-template <typename E, int NT>
-__device__ bool draft_law(const E* __restrict__ y, int V, double Td, SampledLds<NT>& L, DraftLaw& q) {
-  float mx = -INFINITY;
-  double sum = 0.0;
-  int h = INT32_MAX, nan = 0;
-  for_each_elem<E, NT>(y, V, [&](int e, float v) {
-    if (v != v) {
-      nan = 1;
-    } else if (v > mx) {
-      if (Td > 0.0) sum = sum * exp((static_cast<double>(mx) - static_cast<double>(v)) / Td) + 1.0;
-      mx = v;
-      h = e;
-    } else if (Td > 0.0 && mx > -INFINITY) {
-      sum += exp((static_cast<double>(v) - static_cast<double>(mx)) / Td);
-    }
-  });
-  nan = block_reduce<NT>(nan, MaxOp(), L.red_i);
-  const double md = block_reduce<NT>(static_cast<double>(mx), MaxOp(), L.red_d);
-  q.my = static_cast<float>(md);
+// The draft row's law in one streaming pass, float32 exponentials: for
+// Td > 0 each thread keeps a running maximum, an integer exponent reference
+// and the float64 sum of float32 group sums of exp2(y * c - mc), with
+// c = log2(e) / Td split into a float and its float remainder (so the
+// rounding of c adds no error proportional to |y|; what is left is the
+// float rounding of each exponent, random across elements); Z is that sum
+// rebased to the row maximum. For Td = 0 the row's lowest arg-max. Returns
+// false when the row has a NaN or no finite maximum.
+template <typename E, int NT, int U>
+__device__ bool draft_law_stream(const E* __restrict__ y, int V, double Td, SampledLds<NT>& L, DraftLaw& q) {
+  constexpr int N = Elem<E>::kVec;
   q.Td = Td;
   q.Z = 1.0;
   q.h = 0;
-  if (nan || !(md > -INFINITY) || !(md < INFINITY)) return false;
-  if (Td > 0.0) {
-    const double part = mx > -INFINITY ? sum * exp((static_cast<double>(mx) - md) / Td) : 0.0;
-    q.Z = block_reduce<NT>(part, SumOp(), L.red_d);
-  } else {
-    // each thread's first index of its maximum is its lowest (indices grow)
-    q.h = block_reduce<NT>(mx == q.my ? h : INT32_MAX, MinOp(), L.red_i);
+  if (!(Td > 0.0)) {
+    RowPartial p;
+    partial_init(p);
+    GroupKeep<U> keep{};
+    stream_row<E, NT, U, false, GroupKeep<U>, NoHook, true>(y, V, 1.4426950408889634f, INFINITY, 0, p, keep);
+    const RowStats st = finish_row_lean<E, NT, U, false>(p, L.ls, keep, y, V);
+    q.my = st.max;
+    q.h = st.argmax;
+    return !(st.sum != st.sum) && st.max > -INFINITY && st.max < INFINITY && st.argmax != INT32_MAX;
   }
-  return true;
+  const double cd = 1.4426950408889634074 / Td;
+  const float chi = static_cast<float>(cd);
+  const float clo = static_cast<float>(cd - static_cast<double>(chi));
+  float mx = -INFINITY, mc = -FLT_MAX;
+  double sum = 0.0;
+  int nan = 0;
+  auto rebase = [&](float vmax) {
+    const float yy = vmax * chi;
+    if (yy > mc && yy < FLT_MAX) {
+      const float nm = ceilf(yy);
+      sum = (mc > -FLT_MAX) ? ldexp(sum, static_cast<int>(fmaxf(mc - nm, -2000.f))) : 0.0;
+      mc = nm;
+    }
+  };
+  // -inf (a zero-probability logit, or a masked lane) is clamped to the
+  // lowest float first: with a negative remainder clo, -inf * clo would
+  // meet -inf * chi as inf - inf; the clamped term is exactly 0
+  auto term = [&](float v) {
+    const float w = fmaxf(v, -FLT_MAX);
+    return fast_exp2(fmaf(w, clo, fmaf(w, chi, -mc)));
+  };
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(y);
+  int head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(E));
+  if (head > V) head = V;
+  const int nvec = (V - head) / N;
+  const u32x4* __restrict__ vp = reinterpret_cast<const u32x4*>(y + head);
+  constexpr int G = U * NT;
+  for (int base = threadIdx.x; base < nvec; base += G) {
+    u32x4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = load_stream(vp + min(base + u * NT, nvec - 1));
+    float f[U][N];
+    float gmax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      Elem<E>::decode(w[u], f[u]);
+      const bool in = base + u * NT < nvec;
+#pragma unroll
+      for (int k = 0; k < N; ++k) {
+        if (!in) f[u][k] = -INFINITY;
+        nan |= f[u][k] != f[u][k] ? 1 : 0;
+        gmax = fmaxf(gmax, f[u][k]);
+      }
+    }
+    mx = fmaxf(mx, gmax);
+    rebase(gmax);
+    float e[U * N];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int k = 0; k < N; ++k) e[u * N + k] = term(f[u][k]);
+    sum += static_cast<double>(tree_sum<U * N>(e));
+  }
+  const int body_end = head + nvec * N;
+  auto scalar = [&](float v) {
+    nan |= v != v ? 1 : 0;
+    mx = fmaxf(mx, v);
+    rebase(v);
+    sum += static_cast<double>(term(v));
+  };
+  if (static_cast<int>(threadIdx.x) < head) scalar(Elem<E>::at(y, threadIdx.x));
+  if (static_cast<int>(threadIdx.x) < V - body_end) scalar(Elem<E>::at(y, body_end + threadIdx.x));
+  nan = block_reduce<NT>(nan, MaxOp(), L.red_i);
+  const float my = block_reduce<NT>(mx, MaxOp(), reinterpret_cast<float*>(L.red_d));
+  const float mg = block_reduce<NT>(mc, MaxOp(), reinterpret_cast<float*>(L.red_d));
+  q.my = my;
+  if (nan || !(my > -INFINITY) || !(my < INFINITY)) return false;
+  const double part = (mc > -FLT_MAX) ? ldexp(sum, static_cast<int>(fmaxf(mc - mg, -2000.f))) : 0.0;
+  const double tot = block_reduce<NT>(part, SumOp(), L.red_d);
+  q.Z = tot * exp2(static_cast<double>(mg) - static_cast<double>(my) * cd);
+  return q.Z > 0.0 && q.Z < INFINITY;
 }
 
 // The residual draw: the first token in rank order whose cumulative
@@ -285,26 +343,10 @@ __device__ int residual_draw(const E* __restrict__ x, const E* __restrict__ y, i
   return block_reduce<NT>(mylast, MaxOp(), L.red_i);
 }
 
-// When the survivors fit in the candidate buffer (the usual case: top-p
-// keeps a small head of the order) they are gathered into LDS and sorted
-// into rank order (bitonic; key descending, index ascending). The own draw
-// and the residual draw are then scans over that list. Returns n, the
-// entries c[0 .. n) of L.c.cand.
-template <typename E, int NT, typename Pred>
-__device__ int gather_sorted(const E* __restrict__ x, int V, int count, Pred keep, SampledLds<NT>& L) {
-  int P = 1;
-  while (P < count) P <<= 1;
-  Cand* c = L.c.cand;
-  if (threadIdx.x == 0) L.ncand = 0;
-  for (int k = threadIdx.x; k < P; k += NT) c[k] = Cand{-INFINITY, INT32_MAX};
-  lds_barrier();
-  for_each_elem<E, NT>(x, V, [&](int e, float xv) {
-    if (!keep(e, xv)) return;
-    const int slot = atomicAdd(&L.ncand, 1);
-    if (slot < P) c[slot] = Cand{xv, e};
-  });
-  lds_barrier();
-  // rank order; the padding (index INT32_MAX, lowest key) sorts last
+// Sort c[0 .. P) (P a power of two) into rank order: key descending, index
+// ascending; padding (index INT32_MAX) sorts last. Bitonic, in LDS.
+template <int NT>
+__device__ void sort_rank(Cand* c, int P) {
   auto before = [](const Cand& a, const Cand& b) {
     const uint32_t ka = a.idx == INT32_MAX ? 0u : ord_ukey(a.x) + 1u;
     const uint32_t kb = b.idx == INT32_MAX ? 0u : ord_ukey(b.x) + 1u;
@@ -325,6 +367,102 @@ __device__ int gather_sorted(const E* __restrict__ x, int V, int count, Pred kee
       lds_barrier();
     }
   }
+}
+
+// Rank order of the nc candidates c[0 .. nc) (every element >= tau, all at
+// most the maximum mx). bfloat16 rows: a counting sort over the values'
+// codes below the maximum's (a code is one value), then each entry takes
+// its place inside its code by counting the entries of that code with a
+// lower index. float32 rows, or codes spanning kCodeBins or more: the
+// bitonic sort. Scratch: the LDS union u (a Cand buffer and two code
+// arrays), free once the capture is done.
+constexpr int kCodeBins = 1024;
+template <typename E, int NT>
+__device__ void rank_candidates(SampledLds<NT>& L, int nc, float mx) {
+  Cand* c = L.c.cand;
+  static_assert(sizeof(L.u) >= kCand * sizeof(Cand) + 2 * (kCodeBins + 1) * sizeof(int), "sort scratch");
+  Cand* tmp = reinterpret_cast<Cand*>(&L.u);
+  int* start = reinterpret_cast<int*>(tmp + kCand);
+  int* cur = start + kCodeBins + 1;
+  bool counting = sizeof(E) == 2;
+  const int mcode = bf16_code(mx);
+  if (counting) {
+    int span = 0;
+    for (int k = threadIdx.x; k < nc; k += NT) span = max(span, mcode - bf16_code(c[k].x));
+    span = block_reduce<NT>(span, MaxOp(), L.red_i);
+    counting = span < kCodeBins;
+  }
+  if (!counting) {
+    int P = 1;
+    while (P < nc) P <<= 1;
+    for (int k = nc + static_cast<int>(threadIdx.x); k < P; k += NT) c[k] = Cand{-INFINITY, INT32_MAX};
+    lds_barrier();
+    sort_rank<NT>(c, P);
+    return;
+  }
+  for (int b = threadIdx.x; b <= kCodeBins; b += NT) start[b] = 0;
+  lds_barrier();
+  for (int k = threadIdx.x; k < nc; k += NT) atomicAdd(&start[mcode - bf16_code(c[k].x)], 1);
+  lds_barrier();
+  // exclusive scan of the counts, code below the maximum ascending (value
+  // descending); every thread owns kCodeBins / NT consecutive codes
+  constexpr int PER = kCodeBins / NT;
+  static_assert(kCodeBins % NT == 0, "codes per thread");
+  int own[PER];
+  int sum = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    own[q] = start[threadIdx.x * PER + q];
+    sum += own[q];
+  }
+  int total = 0;
+  int before = block_scan_incl<NT, int>(sum, L.red_i, total) - sum;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int b = threadIdx.x * PER + q;
+    start[b] = before;
+    cur[b] = before;
+    before += own[q];
+  }
+  if (threadIdx.x == 0) start[kCodeBins] = total;
+  lds_barrier();
+  for (int k = threadIdx.x; k < nc; k += NT) {
+    const Cand e = c[k];
+    tmp[atomicAdd(&cur[mcode - bf16_code(e.x)], 1)] = e;
+  }
+  lds_barrier();
+  // equal codes are equal values: their order is the index order
+  for (int q = threadIdx.x; q < nc; q += NT) {
+    const Cand e = tmp[q];
+    const int b = mcode - bf16_code(e.x);
+    const int s0 = start[b], s1 = start[b + 1];
+    int below = 0;
+    for (int t = s0; t < s1; ++t) below += tmp[t].idx < e.idx ? 1 : 0;
+    c[s0 + below] = e;
+  }
+  lds_barrier();
+}
+
+// When the survivors fit in the candidate buffer (the usual case: top-p
+// keeps a small head of the order) they are gathered into LDS and sorted
+// into rank order (bitonic; key descending, index ascending). The own draw
+// and the residual draw are then scans over that list. Returns n, the
+// entries c[0 .. n) of L.c.cand.
+template <typename E, int NT, typename Pred>
+__device__ int gather_sorted(const E* __restrict__ x, int V, int count, Pred keep, SampledLds<NT>& L) {
+  int P = 1;
+  while (P < count) P <<= 1;
+  Cand* c = L.c.cand;
+  if (threadIdx.x == 0) L.ncand = 0;
+  for (int k = threadIdx.x; k < P; k += NT) c[k] = Cand{-INFINITY, INT32_MAX};
+  lds_barrier();
+  for_each_elem<E, NT>(x, V, [&](int e, float xv) {
+    if (!keep(e, xv)) return;
+    const int slot = atomicAdd(&L.ncand, 1);
+    if (slot < P) c[slot] = Cand{xv, e};
+  });
+  lds_barrier();
+  sort_rank<NT>(c, P);
   return min(L.ncand, P);
 }
 
@@ -400,63 +538,85 @@ __global__ __launch_bounds__(NT) void verify_probabilistic_kernel(VerifyArgs a, 
     }
   }
 
-  // the target row's maximum and lowest arg-max
-  RowPartial p;
-  partial_init(p);
-  GroupKeep<U> keep{};
-  constexpr float kLog2e = 1.4426950408889634f;
-  stream_row<E, NT, U, false>(row, a.V, kLog2e, INFINITY, 0, p, keep);
-  const RowResult res = finish_row<E, NT, U, false, true>(p, L.rs, keep, row, a.V);
-  int token = res.argmax == INT32_MAX ? 0 : res.argmax;
-  if (!(res.max < INFINITY) || res.argmax == INT32_MAX || !isfinite(res.lse)) bits |= VSV_FLAG_LOGITS;
-
+  int token = 0;
   bool accept = false;
+  const bool sampled = m.req >= 0 && T > 0.f && T < INFINITY;
+  float fast_tau = -INFINITY;
+  double fast_wtot = 0.0, fast_c = 0.0;
+  VmPlan fast_plan{};
+  float mx = 0.f;
+  if (!sampled) {
+    // the target row's maximum and lowest arg-max
+    RowPartial p;
+    partial_init(p);
+    GroupKeep<U> keep{};
+    constexpr float kLog2e = 1.4426950408889634f;
+    stream_row<E, NT, U, false, GroupKeep<U>, NoHook, true>(row, a.V, kLog2e, INFINITY, 0, p, keep);
+    const RowStats st = finish_row_lean<E, NT, U, false>(p, L.ls, keep, row, a.V);
+    token = st.argmax == INT32_MAX ? 0 : st.argmax;
+    if (!(st.max < INFINITY) || st.argmax == INT32_MAX || st.sum != st.sum) bits |= VSV_FLAG_LOGITS;
+  } else {
+    // the sampled path's first pass: maximum, streamed total weight at
+    // scale c = log2(e) / T, and the vector-maximum codes for the capture
+    const float c = 1.4426950408889634f / T;
+    RowPartial p;
+    partial_init(p);
+    const VmPlan plan = stream_sampled<E, NT, SampledDepth<E>::kPass1>(row, a.V, c, p, L);
+    const NoKeep nk;
+    const RowStats st = finish_row_lean<E, NT, U, false>(p, L.ls, nk, row, a.V);
+    mx = st.max;
+    if (!(mx < INFINITY) || !(mx > -INFINITY) || !(st.sum > 0.0) || !(st.sum < INFINITY)) bits |= VSV_FLAG_LOGITS;
+    if (!(bits & VSV_FLAG_LOGITS)) {
+      // capture threshold as the sampled path takes it
+      const bool tk0 = top_k > 0 && top_k < a.V;
+      float tau = -INFINITY;
+      if (tk0) {
+        tau = capture_threshold<E, NT>(L, plan, mx, -INFINITY, top_k, true);
+      } else {
+        float dcap = T * kZcap;
+        if (min_p > 0.f && top_p >= 1.f) {
+          const float dm = static_cast<float>(-static_cast<double>(T) * log(static_cast<double>(min_p))) * 1.0001f +
+                           1e-6f;
+          dcap = fminf(dcap, dm);
+        }
+        tau = capture_threshold<E, NT>(L, plan, mx, (dcap < INFINITY) ? mx - dcap : -INFINITY, kCapVec, false);
+      }
+      fast_tau = tau;
+      fast_wtot = st.sum * exp2(static_cast<double>(st.mref) - static_cast<double>(mx) * static_cast<double>(c));
+      fast_c = static_cast<double>(c);
+      fast_plan = plan;
+    }
+  }
+
   const bool live = m.req >= 0 && !(bits & VSV_FLAG_LOGITS);
-  if (live && T > 0.f && T < INFINITY) {
+  if (live && sampled) {
     const double Td = static_cast<double>(T);
-    lds_barrier();
-    FullLocator<E, NT> fl(L, row, a.V, res.max, Td);
     const Cand* c = L.c.cand;
     Support s{0, 0.0, 0u, 0};
     bool listed = false;
     const bool tk = top_k > 0 && top_k < a.V;
-    if (tk ? top_k <= kCand : top_p < 1.f) {
-      // the survivors from a sorted head of the order: one pass counts the
-      // elements in bands of z = (x - m) / T (and, without top-k, takes the
-      // total weight); the widest head of whole bands that fits the list is
-      // gathered and sorted. Bands are monotone in x, so the head is a
-      // prefix of the rank order. It decides when it holds the top-k, or
-      // top_p of the total.
-      const float mx = res.max;
-      auto band = [&](float xv) {
-        const double z = (static_cast<double>(xv) - static_cast<double>(mx)) / Td;
-        return z > -16.0 ? min(static_cast<int>(-z * 4.0), kBands - 1) : kBands - 1;
-      };
-      for (int b = threadIdx.x; b < kBands; b += NT) L.u.radix.cnt[b] = 0;
-      lds_barrier();
-      double sw = 0.0;
-      for_each_elem<E, NT>(row, a.V, [&](int, float xv) {
-        if (!tk) sw += weight(xv, mx, Td);
-        atomicAdd(&L.u.radix.cnt[band(xv)], 1);
-      });
-      const double W = block_reduce<NT>(sw, SumOp(), L.red_d);
-      if (threadIdx.x == 0) {
-        int cum = 0, top = -1;
-        for (int b = 0; b < kBands && cum + L.u.radix.cnt[b] <= kCand; ++b) {
-          cum += L.u.radix.cnt[b];
-          top = b;
-        }
-        L.bi[0] = top;
-        L.bi[1] = cum;
+    // Fast path: every element >= tau captured into the candidate list
+    // (a complete head of the rank order), sorted into rank order; the
+    // streamed total with the candidates' share replaced by their exact
+    // weights. The survivor set is then a prefix of the list whenever its
+    // cut lies inside the list.
+    if (fast_tau > -INFINITY && capture_row<E, NT>(row, a.V, fast_tau, fast_plan, L)) {
+      const int nc = min(L.ncand, kCand);
+      double corr = 0.0;
+      for (int k = threadIdx.x; k < nc; k += NT) {
+        const double xv = static_cast<double>(c[k].x);
+        corr += weight(c[k].x, mx, Td) - exp2((xv - static_cast<double>(mx)) * fast_c);
       }
+      const double W = fast_wtot + block_reduce<NT>(corr, SumOp(), L.red_d);
+      rank_candidates<E, NT>(L, nc, mx);
+      // the candidates' weights, once, in LDS (the union u is free again)
+      double* wl = reinterpret_cast<double*>(&L.u);
+      for (int k = threadIdx.x; k < nc; k += NT) wl[k] = weight(c[k].x, mx, Td);
       lds_barrier();
-      const int top = L.bi[0], cnt = L.bi[1];
-      lds_barrier();
-      if (top >= 0 && cnt >= (tk ? top_k : 1)) {
-        const int nl = gather_sorted<E, NT>(row, a.V, cnt, [&](int, float xv) { return band(xv) <= top; }, L);
-        auto wt = [&](int k) { return weight(c[k].x, mx, Td); };
-        int n = -1;
-        if (tk) {
+      auto wt = [&](int k) { return wl[k]; };
+      int n = 0;
+      if (tk) {
+        if (top_k <= nc) {
           n = top_k;
           if (top_p < 1.f) {
             double s1 = 0.0;
@@ -464,33 +624,50 @@ __global__ __launch_bounds__(NT) void verify_probabilistic_kernel(VerifyArgs a, 
             const double W1 = block_reduce<NT>(s1, SumOp(), L.red_d);
             n = scan_pick<NT>(top_k, wt, static_cast<double>(top_p), L, false, W1, true) + 1;
           }
-        } else {
-          n = scan_pick<NT>(nl, wt, static_cast<double>(top_p), L, false, W, false) + 1;
         }
-        if (n > 0) {
-          if (min_p > 0.f) {
-            bool exact = false;
-            const int lm = fl.count_minp(log(static_cast<double>(min_p)), exact);
-            if (lm < n) n = lm > 0 ? lm : 1;
-          }
-          double sn = 0.0;
-          for (int q = threadIdx.x; q < n; q += NT) sn += wt(q);
-          const double w = block_reduce<NT>(sn, SumOp(), L.red_d);
-          s = Support{n, w, ord_ukey(c[n - 1].x), c[n - 1].idx};
-          listed = true;
-        }
+      } else if (top_p < 1.f) {
+        n = scan_pick<NT>(nc, wt, static_cast<double>(top_p), L, false, W, false) + 1;
+      } else if (min_p > 0.f) {
+        n = nc;   // min-p alone: its cut must lie inside the list (checked below)
+      }
+      if (n > 0 && min_p > 0.f) {
+        // min-p keeps the prefix with (x - m) / T >= ln(min_p)
+        const double lm = log(static_cast<double>(min_p));
+        int cnt = 0;
+        for (int q = threadIdx.x; q < n; q += NT)
+          cnt += ((static_cast<double>(c[q].x) - static_cast<double>(mx)) / Td >= lm) ? 1 : 0;
+        const int keep_n = block_reduce<NT>(cnt, SumOp(), L.red_i);
+        if (!tk && top_p >= 1.f && keep_n == nc) n = 0;   // the cut may lie below the list
+        else n = keep_n > 0 ? keep_n : 1;
+      }
+      if (n > 0) {
+        double sn = 0.0;
+        for (int q = threadIdx.x; q < n; q += NT) sn += wt(q);
+        const double w = block_reduce<NT>(sn, SumOp(), L.red_d);
+        s = Support{n, w, ord_ukey(c[n - 1].x), c[n - 1].idx};
+        listed = true;
       }
     }
+    lds_barrier();
+    FullLocator<E, NT> fl(L, row, a.V, mx, Td);
+    if (!listed && threadIdx.x == 0 && a.slow_rows) atomicAdd(a.slow_rows, 1);
     if (!listed) {
       s = support(fl, a.V, top_k, static_cast<double>(top_p), static_cast<double>(min_p));
       listed = s.n <= kCand;
-      if (listed) gather_sorted<E, NT>(row, a.V, s.n, [&](int e, float xv) { return in_support(ord_ukey(xv), e, s); }, L);
+      if (listed) {
+        gather_sorted<E, NT>(row, a.V, s.n, [&](int e, float xv) { return in_support(ord_ukey(xv), e, s); }, L);
+        // the locator is done with the union u: the list's weights go there
+        double* wl = reinterpret_cast<double*>(&L.u);
+        for (int k = threadIdx.x; k < s.n; k += NT) wl[k] = weight(c[k].x, mx, Td);
+        lds_barrier();
+      }
     }
     const int n = s.n;
+    double* wl = reinterpret_cast<double*>(&L.u);   // listed: the n weights in rank order
     double u, ua;
     prob_uniforms(a.seed, a.offset, m.req, m.j, u, ua);
     if (listed) {
-      const int k = scan_pick<NT>(n, [&](int k) { return weight(c[k].x, res.max, Td); }, u, L);
+      const int k = scan_pick<NT>(n, [&](int k) { return wl[k]; }, u, L);
       token = c[k < 0 ? 0 : k].idx;
     } else {
       Pick own = fl.by_mass(u * s.w, true);
@@ -501,24 +678,41 @@ __global__ __launch_bounds__(NT) void verify_probabilistic_kernel(VerifyArgs a, 
       const E* __restrict__ y = static_cast<const E*>(pa.draft_logits) + static_cast<int64_t>(r - m.req) * pa.dld;
       const double Tdq = (Tq >= 0.f && Tq < INFINITY) ? static_cast<double>(Tq) : 0.0;
       DraftLaw q;
-      if (!draft_law<E, NT>(y, a.V, Tdq, L, q)) {
+      if (!draft_law_stream<E, NT, U>(y, a.V, Tdq, L, q)) {
         bits |= VSV_FLAG_LOGITS;
       } else {
         const int d = m.draft;
         if (d >= 0 && d < a.V) {
           const float xd = Elem<E>::at(row, d);
-          const double pd = in_support(ord_ukey(xd), d, s) ? weight(xd, res.max, Td) / s.w : 0.0;
+          const double pd = in_support(ord_ukey(xd), d, s) ? weight(xd, mx, Td) / s.w : 0.0;
           accept = ua * q.q(Elem<E>::at(y, d), d) < pd;
         }
         int t = -1;
         if (listed) {
-          const int k = scan_pick<NT>(n, [&](int k) {
-            const double r = weight(c[k].x, res.max, Td) / s.w - q.q(Elem<E>::at(y, c[k].idx), c[k].idx);
-            return r > 0.0 ? r : 0.0;
-          }, u, L);
+          // residual masses over the list, in place of the weights; the
+          // draft row's values are gathered kResBatch at a time per thread
+          constexpr int kResBatch = 4;
+          for (int base = 0; base < n; base += NT * kResBatch) {
+            float yv[kResBatch];
+#pragma unroll
+            for (int b = 0; b < kResBatch; ++b) {
+              const int k = base + b * NT + static_cast<int>(threadIdx.x);
+              yv[b] = k < n ? Elem<E>::at(y, c[k].idx) : 0.f;
+            }
+#pragma unroll
+            for (int b = 0; b < kResBatch; ++b) {
+              const int k = base + b * NT + static_cast<int>(threadIdx.x);
+              if (k < n) {
+                const double r = wl[k] / s.w - q.q(yv[b], c[k].idx);
+                wl[k] = r > 0.0 ? r : 0.0;
+              }
+            }
+          }
+          lds_barrier();
+          const int k = scan_pick<NT>(n, [&](int k) { return wl[k]; }, u, L);
           if (k >= 0) t = c[k].idx;
         } else {
-          t = residual_draw<E, NT>(row, y, a.V, res.max, Td, s, q, u, L);
+          t = residual_draw<E, NT>(row, y, a.V, mx, Td, s, q, u, L);
         }
         if (t >= 0) token = t;
       }

@@ -221,9 +221,9 @@ vsv_status vsv_verify_sampled(const vsv_batch* batch, const float* temperature,
  * of max(0, p - q) in rank order at u (its own draw from p if that residual
  * has no mass); a request whose drafts all pass emits the bonus row's draw.
  * row_token holds each row's emitted-if-first-rejected token (the bonus
- * row's own draw); row_lse and slow_rows are not written. Exact, not yet
- * tuned: each sampled row takes several passes over its target row and one
- * over its draft row.
+ * row's own draw); row_lse is not written; slow_rows counts sampled rows
+ * whose survivor set reached below the captured head of the rank order and
+ * took the exact whole-row path (several more passes over the row).
  * Workspace: vsv_workspace_bytes(B, R, 0) or more.
  * Errors: as vsv_verify_sampled, plus VSV_EINVAL for NULL draft rows (when
  * R > B) or draft temperatures, draft_ld < vocab or misaligned draft rows.
