@@ -71,7 +71,7 @@ SYMBOLS = ("vsv_workspace_bytes", "vsv_workspace_init", "vsv_verify_greedy", "vs
            "vsv_verify_greedy_static",
            "vsv_verify_sampled",
            "vsv_verify_probabilistic", "vsv_draft_confidence", "vsv_allocate_verify", "vsv_goodput_init", "vsv_goodput_observe",
-           "vsv_goodput_step", "vsv_goodput_select", "vsv_status_string", "vsv_version")
+           "vsv_goodput_step", "vsv_goodput_select", "vsv_status_string", "vsv_test_withhold_row_word", "vsv_version")
 
 GOODPUT_MAX_STEPS = 32
 GOODPUT_MAX_WINDOW = 64
@@ -130,6 +130,8 @@ def lib():
     L.vsv_goodput_select.restype = i32
     L.vsv_status_string.argtypes = [ctypes.c_int]
     L.vsv_status_string.restype = ctypes.c_char_p
+    L.vsv_test_withhold_row_word.argtypes = [i32]
+    L.vsv_test_withhold_row_word.restype = ctypes.c_int
     L.vsv_version.argtypes = []
     L.vsv_version.restype = i32
     _lib = L
@@ -293,6 +295,13 @@ def verify_greedy_relaxed(logits, row_offsets, row_owner, draft_tokens, topk=1, 
     _check(lib().vsv_verify_greedy_relaxed(ctypes.byref(batch), ctypes.byref(relax), ctypes.byref(outs), _ptr(ws),
                                            ws.numel(), _stream(stream)))
     return out
+
+
+def withhold_row_word(row):
+    """Test hook (vsv_test_withhold_row_word): later row-per-workgroup verify
+    launches leave row `row`'s result word unpublished, so their scan waits
+    out its bounded poll and flags VSV_FLAG_STALLED; -1 turns it off."""
+    _check(lib().vsv_test_withhold_row_word(int(row)))
 
 
 def verify_greedy_static(logits, row_offsets, row_owner, draft_tokens, relaxed_topk=1, vocab=None, out=None,

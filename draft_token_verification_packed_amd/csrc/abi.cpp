@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "allocate.hpp"
 #include "kernels.hpp"
 #include "probabilistic.hpp"
@@ -17,6 +19,10 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 size_t elem_size(int32_t dtype) { return dtype == VSV_BF16 ? 2 : 4; }
 
 bool dtype_ok(int32_t dtype) { return dtype == VSV_F32 || dtype == VSV_BF16; }
+
+// Row whose result word the next launches leave unpublished (-1: none); set
+// only by vsv_test_withhold_row_word.
+std::atomic<int32_t> g_withheld_row{-1};
 
 // Persistent workgroups for greedy verification: one per CU of the current
 // device (cached per device), at most kMaxGroups; 0 if the count is unknown.
@@ -75,6 +81,7 @@ vsv_status prepare(const vsv_batch* b, const vsv_outputs* o, void* ws, size_t ws
   v.row_lse = o->row_lse;
   v.error_flag = o->error_flag;
   v.slow_rows = o->slow_rows;
+  v.withheld_row = g_withheld_row.load(std::memory_order_relaxed);
   char* w = static_cast<char*>(ws);
   v.ws_epoch = reinterpret_cast<uint32_t*>(w);
   v.ws_queue = reinterpret_cast<uint32_t*>(w + 64);
@@ -221,6 +228,12 @@ const char* vsv_status_string(vsv_status status) {
   return "unknown status";
 }
 
-int32_t vsv_version(void) { return 102; }
+vsv_status vsv_test_withhold_row_word(int32_t row) {
+  if (row < -1) return VSV_EINVAL;
+  g_withheld_row.store(row, std::memory_order_relaxed);
+  return VSV_OK;
+}
+
+int32_t vsv_version(void) { return 103; }
 
 }  // extern "C"

@@ -94,6 +94,9 @@ struct VerifyArgs {
   float* row_lse;
   int32_t* error_flag;
   int32_t* slow_rows;
+  // row whose result word the row-per-workgroup kernels leave unpublished
+  // (a host-set test hook for the scan's bounded wait); -1: none
+  int32_t withheld_row;
   // workspace (zero before its first use). Words handed between workgroups
   // carry the call's tag in their high half, so a call finds only its own
   // and nothing has to be cleared afterwards:

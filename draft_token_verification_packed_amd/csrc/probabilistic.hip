@@ -726,7 +726,7 @@ __global__ __launch_bounds__(NT) void verify_probabilistic_kernel(VerifyArgs a, 
     const uint32_t word = row_word(a, m, token, accept, bits);
     if (bits) set_flag(a, bits);
     if (a.row_token) a.row_token[r] = token;
-    store_agent64(a.ws_row + r, tagged(tag, word));
+    if (r != a.withheld_row) store_agent64(a.ws_row + r, tagged(tag, word));
     const uint32_t done = __hip_atomic_fetch_add(a.ws_queue + kQueueDone, 1u, __ATOMIC_ACQ_REL,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     L.last = done + 1 == gridDim.x;

@@ -55,7 +55,7 @@ __device__ __forceinline__ void sampled_kernel_row(const VerifyArgs& a, uint32_t
     if (slow && a.slow_rows) atomicAdd(a.slow_rows, 1);
     if (a.row_token) a.row_token[r] = token;
     if (a.row_lse) a.row_lse[r] = static_cast<float>(lse);
-    store_agent64(a.ws_row + r, tagged(tag, word));
+    if (r != a.withheld_row) store_agent64(a.ws_row + r, tagged(tag, word));
   }
 }
 

@@ -603,7 +603,7 @@ __global__ __launch_bounds__(NT) void verify_greedy_rows_kernel(VerifyArgs a) {
       if (bits) set_flag(a, bits);
       if (a.row_token) a.row_token[r] = token;
       if (a.row_lse) a.row_lse[r] = lse;
-      store_agent64(a.ws_row + r, tagged(tag, word));
+      if (r != a.withheld_row) store_agent64(a.ws_row + r, tagged(tag, word));
     }
   }
   if (blockIdx.x == gridDim.x - 1) words_tail<NT>(a, tag, tail);

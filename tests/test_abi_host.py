@@ -201,3 +201,11 @@ def test_relaxed_validation(L):
     assert call(num_protected=vsv.MAX_PROTECTED + 1, protected_ids=0x90000) == 1
     assert call(num_protected=3) == 1                    # ids missing
     assert "#define VSV_MAX_PROTECTED %d" % vsv.MAX_PROTECTED in open(HEADER).read()
+
+
+def test_withhold_hook_validation(L):
+    assert L.vsv_test_withhold_row_word(-2) == 1
+    assert L.vsv_test_withhold_row_word(5) == 0
+    assert L.vsv_test_withhold_row_word(-1) == 0
+    with pytest.raises(vsv.VSVError):
+        vsv.withhold_row_word(-3)
