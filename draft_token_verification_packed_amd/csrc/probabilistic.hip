@@ -15,17 +15,21 @@
 // speculative inference", DSpark section "Launch example"): their point-mass
 // drafts, which the sampled path verifies, are its special case.
 //
-// How: exact first. One workgroup per row streams the target row for its
-// maximum and arg-max. A sampled row then gathers a head of its rank order
-// (whole bands of z = (x - m) / T, up to 4096 entries) into LDS and sorts
-// it; when that head decides the top-k / top-p cut, the survivor set, the
-// own draw and the residual draw of max(0, p - q) are block scans over the
-// sorted list. Otherwise the sampled path's exact whole-row radix locator
-// settles them (several passes over the row, which stays in the caches).
-// The draft row is read once for its maximum and exponent sum. Each row
-// stores a tagged word; the workgroup that finishes last runs the
-// per-request scan.
+// How: rows come from the persistent row queue (row_queue.hpp), two
+// workgroups per CU. A sampled row takes the sampled path's first pass (its
+// maximum, streamed total weight and vector-maximum codes), captures every
+// element at or above the sampled path's capture threshold into LDS and
+// ranks them (a counting sort over bfloat16 codes, a bitonic sort for
+// float32); the streamed total is corrected with the captured elements'
+// exact float64 weights. When that head decides the top-k / top-p / min-p
+// cut, the survivor set, the own draw and the residual draw of max(0, p - q)
+// are block scans over LDS arrays of weights and residual masses.
+// Otherwise the sampled path's exact whole-row locator settles them, out of
+// line. A draft row is read once, in float32, for its maximum and exponent
+// sum. Each row stores a tagged word; the workgroup that finishes last runs
+// the per-request scan.
 #include "probabilistic.hpp"
+#include "row_queue.hpp"
 #include "sampled_row.hpp"
 #include "verify_common.hpp"
 
@@ -511,12 +515,39 @@ __device__ int scan_pick(int n, Mass mass, double u, SampledLds<NT>& L, bool str
 
 }  // namespace
 
-template <typename E, int NT, int U>
-__global__ __launch_bounds__(NT) void verify_probabilistic_kernel(VerifyArgs a, ProbArgs pa) {
-  __shared__ SampledLds<NT> L;
-  static_assert(sizeof(TailScratch) <= sizeof(L.c), "tail staging aliases the candidate buffer");
-  const uint32_t tag = call_tag(a);
-  const int r = static_cast<int>(blockIdx.x);
+// Survivor set of a sampled row whose cut the captured head did not decide,
+// by the sampled path's whole-row locator (several passes over the row,
+// which stays in the caches); the survivors are listed in rank order with
+// their weights when they fit the candidate buffer, else the own draw is
+// located directly. Out of line: the common path keeps its registers.
+template <typename E, int NT>
+__device__ __noinline__ void slow_support(const E* __restrict__ row, int V, float mx, double Td, int top_k,
+                                          double top_p, double min_p, double u, SampledLds<NT>& L, Support& s,
+                                          bool& listed, int& own) {
+  FullLocator<E, NT> fl(L, row, V, mx, Td);
+  s = support(fl, V, top_k, top_p, min_p);
+  listed = s.n <= kCand;
+  own = 0;
+  if (listed) {
+    const Support sv = s;
+    gather_sorted<E, NT>(row, V, sv.n, [&](int e, float xv) { return in_support(ord_ukey(xv), e, sv); }, L);
+    // the locator is done with the union u: the list's weights go there
+    double* wl = reinterpret_cast<double*>(&L.u);
+    const Cand* c = L.c.cand;
+    for (int k = threadIdx.x; k < sv.n; k += NT) wl[k] = weight(c[k].x, mx, Td);
+    lds_barrier();
+  } else {
+    Pick p = fl.by_mass(u * s.w, true);
+    if (p.rank >= s.n) p = fl.by_count(s.n);
+    own = p.idx;
+  }
+}
+
+// One row of the batch: its token, acceptance and word. `after_stream` is
+// called once the target row has been streamed.
+template <typename E, int NT, int U, typename Hook>
+__device__ __forceinline__ void prob_kernel_row(const VerifyArgs& a, const ProbArgs& pa, uint32_t tag, int r,
+                                                SampledLds<NT>& L, Hook after_stream) {
   const E* __restrict__ row = static_cast<const E*>(a.logits) + static_cast<int64_t>(r) * a.ld;
   const RowMeta m = load_meta(a, r, a.owner[r]);
   const int req = m.req < 0 ? 0 : m.req;
@@ -552,6 +583,7 @@ __global__ __launch_bounds__(NT) void verify_probabilistic_kernel(VerifyArgs a, 
     GroupKeep<U> keep{};
     constexpr float kLog2e = 1.4426950408889634f;
     stream_row<E, NT, U, false, GroupKeep<U>, NoHook, true>(row, a.V, kLog2e, INFINITY, 0, p, keep);
+    after_stream();
     const RowStats st = finish_row_lean<E, NT, U, false>(p, L.ls, keep, row, a.V);
     token = st.argmax == INT32_MAX ? 0 : st.argmax;
     if (!(st.max < INFINITY) || st.argmax == INT32_MAX || st.sum != st.sum) bits |= VSV_FLAG_LOGITS;
@@ -562,6 +594,7 @@ __global__ __launch_bounds__(NT) void verify_probabilistic_kernel(VerifyArgs a, 
     RowPartial p;
     partial_init(p);
     const VmPlan plan = stream_sampled<E, NT, SampledDepth<E>::kPass1>(row, a.V, c, p, L);
+    after_stream();
     const NoKeep nk;
     const RowStats st = finish_row_lean<E, NT, U, false>(p, L.ls, nk, row, a.V);
     mx = st.max;
@@ -649,30 +682,18 @@ __global__ __launch_bounds__(NT) void verify_probabilistic_kernel(VerifyArgs a, 
       }
     }
     lds_barrier();
-    FullLocator<E, NT> fl(L, row, a.V, mx, Td);
-    if (!listed && threadIdx.x == 0 && a.slow_rows) atomicAdd(a.slow_rows, 1);
+    double u, ua;
+    prob_uniforms(a.seed, a.offset, m.req, m.j, u, ua);
     if (!listed) {
-      s = support(fl, a.V, top_k, static_cast<double>(top_p), static_cast<double>(min_p));
-      listed = s.n <= kCand;
-      if (listed) {
-        gather_sorted<E, NT>(row, a.V, s.n, [&](int e, float xv) { return in_support(ord_ukey(xv), e, s); }, L);
-        // the locator is done with the union u: the list's weights go there
-        double* wl = reinterpret_cast<double*>(&L.u);
-        for (int k = threadIdx.x; k < s.n; k += NT) wl[k] = weight(c[k].x, mx, Td);
-        lds_barrier();
-      }
+      if (threadIdx.x == 0 && a.slow_rows) atomicAdd(a.slow_rows, 1);
+      slow_support<E, NT>(row, a.V, mx, Td, top_k, static_cast<double>(top_p), static_cast<double>(min_p), u, L, s,
+                          listed, token);
     }
     const int n = s.n;
     double* wl = reinterpret_cast<double*>(&L.u);   // listed: the n weights in rank order
-    double u, ua;
-    prob_uniforms(a.seed, a.offset, m.req, m.j, u, ua);
     if (listed) {
       const int k = scan_pick<NT>(n, [&](int k) { return wl[k]; }, u, L);
       token = c[k < 0 ? 0 : k].idx;
-    } else {
-      Pick own = fl.by_mass(u * s.w, true);
-      if (own.rank >= s.n) own = fl.by_count(s.n);
-      token = own.idx;
     }
     if (m.j < m.K) {
       const E* __restrict__ y = static_cast<const E*>(pa.draft_logits) + static_cast<int64_t>(r - m.req) * pa.dld;
@@ -727,21 +748,34 @@ __global__ __launch_bounds__(NT) void verify_probabilistic_kernel(VerifyArgs a, 
     if (bits) set_flag(a, bits);
     if (a.row_token) a.row_token[r] = token;
     if (r != a.withheld_row) store_agent64(a.ws_row + r, tagged(tag, word));
-    const uint32_t done = __hip_atomic_fetch_add(a.ws_queue + kQueueDone, 1u, __ATOMIC_ACQ_REL,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    L.last = done + 1 == gridDim.x;
-  }
-  lds_barrier();
-  if (L.last) {
-    if (threadIdx.x == 0) store_agent(a.ws_queue + kQueueDone, 0u);
-    words_tail<NT>(a, tag, *reinterpret_cast<TailScratch*>(&L.c));
   }
 }
 
+// Rows come from the persistent row queue (row_queue.hpp), in row order.
+template <typename E, int NT, int U>
+// two workgroups per CU (4 waves per SIMD): at most 128 VGPRs
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void verify_probabilistic_kernel(
+    VerifyArgs a, ProbArgs pa) {
+  __shared__ SampledLds<NT> L;
+  const uint32_t tag = call_tag(a);
+  row_queue_loop<NT>(a, tag, L, [&](int r, auto hook) { prob_kernel_row<E, NT, U>(a, pa, tag, r, L, hook); });
+}
+
 template <typename E>
-static hipError_t launch_probabilistic_t(const VerifyArgs& a, const ProbArgs& p, hipStream_t s) {
+static hipError_t launch_probabilistic_t(VerifyArgs a, const ProbArgs& p, hipStream_t s) {
+  static int cached[64];
+  int dev = 0, grid = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+    if (cached[dev] <= 0)
+      cached[dev] = resident_groups(verify_probabilistic_kernel<E, kVerifyThreads, SampledDepth<E>::kGreedy>,
+                                    kVerifyThreads, a.groups);
+    grid = cached[dev];
+  }
+  if (grid <= 0) grid = 256;
+  if (grid > a.R) grid = a.R;
+  a.ordered = 0;
   verify_probabilistic_kernel<E, kVerifyThreads, SampledDepth<E>::kGreedy>
-      <<<dim3(a.R), dim3(kVerifyThreads), 0, s>>>(a, p);
+      <<<dim3(grid), dim3(kVerifyThreads), 0, s>>>(a, p);
   return hipGetLastError();
 }
 

@@ -1,0 +1,79 @@
+// Persistent row queue shared by the sampled and probabilistic verification
+// kernels (gfx950).
+//
+// Their rows cost very different amounts (a sampled row several times a
+// greedy one), and the hardware's in-order workgroup dispatch would leave
+// CUs idle behind the uneven rows. So the grid is persistent (as many
+// workgroups as fit on the device at once) and each workgroup takes rows
+// from a queue in the workspace. It asks for its next row once the current
+// row has been read from memory (the row function calls the hook it is
+// given at that point), so the request's latency hides behind the row's
+// last steps while rows still go to the workgroups that free up first. The
+// workgroup that finishes last resets the queue and runs the per-request
+// scan.
+#pragma once
+
+#include "verify_common.hpp"
+
+namespace vsv {
+
+__device__ __forceinline__ uint32_t queue_take(const VerifyArgs& a) {
+  return __hip_atomic_fetch_add(a.ws_queue + kQueueNext, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Runs row(r, hook) for every row this workgroup is handed, then the end of
+// the call. Lds provides `row_next`, `last` and a candidate area `c` that
+// the per-request scan may use as staging once every row is done.
+template <int NT, typename Lds, typename RowFn>
+__device__ __forceinline__ void row_queue_loop(const VerifyArgs& a, uint32_t tag, Lds& L, RowFn row) {
+  static_assert(sizeof(TailScratch) <= sizeof(L.c), "tail staging aliases the candidate area");
+  // Tickets: a workgroup's first ticket is its own index when the rows come
+  // in ws_perm order (the grid has at most R workgroups), else it comes
+  // from the queue like every later one.
+  const uint32_t R = static_cast<uint32_t>(a.R);
+  const uint32_t P = a.ordered ? gridDim.x : 0u;
+  auto row_of = [&](uint32_t q) -> int {
+    return q < R ? (a.ordered ? a.ws_perm[q] : static_cast<int>(q)) : a.R;
+  };
+  if (threadIdx.x == 0) L.row_next = row_of(a.ordered ? blockIdx.x : queue_take(a));
+  lds_barrier();
+  int r = L.row_next;
+  while (r < a.R) {
+    // the next row's ticket is in flight during the row's last steps; the
+    // row's barriers separate this read of row_next from the write below
+    uint32_t next = 0;
+    row(r, [&]() {
+      if (threadIdx.x == 0) next = queue_take(a);
+    });
+    if (threadIdx.x == 0) L.row_next = row_of(next + P);
+    lds_barrier();
+    r = L.row_next;
+  }
+  // Every ticket of this workgroup has been taken and its rows published
+  // (release); the last workgroup to get here sees all rows (acquire).
+  if (threadIdx.x == 0) {
+    const uint32_t done = __hip_atomic_fetch_add(a.ws_queue + kQueueDone, 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    L.last = done + 1 == gridDim.x;
+  }
+  lds_barrier();
+  if (L.last) {
+    if (threadIdx.x == 0) {
+      store_agent(a.ws_queue + kQueueNext, 0u);
+      store_agent(a.ws_queue + kQueueDone, 0u);
+    }
+    words_tail<NT>(a, tag, *reinterpret_cast<TailScratch*>(&L.c));
+  }
+}
+
+// Workgroups of `kernel` (NT threads, static LDS only) that fit on the
+// current device at once, given its CU count; 0 if unknown.
+template <typename K>
+inline int resident_groups(K kernel, int NT, int cus) {
+  int per_cu = 0;
+  if (cus <= 0 || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, NT, 0) != hipSuccess || per_cu <= 0)
+    return 0;
+  return per_cu * cus;
+}
+
+}  // namespace vsv

@@ -2,6 +2,7 @@
 // > 0 draw their token (sampled_row.hpp), rows of greedy requests take the
 // arg-max, and the per-request scan (verify_common.hpp) ends the launch.
 #include "verify_common.hpp"
+#include "row_queue.hpp"
 #include "sampled_row.hpp"
 
 namespace vsv {
@@ -10,16 +11,8 @@ namespace vsv {
 
 // Rows of requests with temperature > 0 draw their token (sampled_row.hpp);
 // rows of greedy requests take the arg-max exactly as verify_greedy does.
-// Acceptance is strict: the draft must equal the row's token.
-//
-// A sampled row costs several times a greedy one, and the hardware's
-// in-order workgroup dispatch leaves CUs idle behind such uneven rows. So
-// the grid is persistent (as many workgroups as fit on the device at once)
-// and each workgroup takes rows from a queue in the workspace. It asks for
-// its next row once the current row has been read from memory, so the
-// request's latency hides behind the row's last steps while the rows still
-// go to the workgroups that free up first. The workgroup that finishes last
-// resets the queue and runs the per-request scan.
+// Acceptance is strict: the draft must equal the row's token. Rows come
+// from the persistent row queue (row_queue.hpp).
 template <typename E, int NT, int U, typename Hook>
 __device__ __forceinline__ void sampled_kernel_row(const VerifyArgs& a, uint32_t tag, int r, SampledLds<NT>& L,
                                                    Hook after_stream) {
@@ -95,53 +88,12 @@ __global__ __launch_bounds__(NT) void sampled_order_kernel(VerifyArgs a) {
   }
 }
 
-__device__ __forceinline__ uint32_t queue_take(const VerifyArgs& a) {
-  return __hip_atomic_fetch_add(a.ws_queue + kQueueNext, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 template <typename E, int NT, int U>
 // two workgroups per CU (4 waves per SIMD): at most 128 VGPRs
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void verify_sampled_kernel(VerifyArgs a) {
   __shared__ SampledLds<NT> L;
-  static_assert(sizeof(TailScratch) <= sizeof(L.c), "tail staging aliases the candidate buffer");
   const uint32_t tag = call_tag(a);
-  // Tickets: a workgroup's first ticket is its own index when the rows come
-  // in ws_perm order (the grid has at most R workgroups), else it comes
-  // from the queue like every later one.
-  const uint32_t R = static_cast<uint32_t>(a.R);
-  const uint32_t P = a.ordered ? gridDim.x : 0u;
-  auto row_of = [&](uint32_t q) -> int {
-    return q < R ? (a.ordered ? a.ws_perm[q] : static_cast<int>(q)) : a.R;
-  };
-  if (threadIdx.x == 0) L.row_next = row_of(a.ordered ? blockIdx.x : queue_take(a));
-  lds_barrier();
-  int r = L.row_next;
-  while (r < a.R) {
-    // the next row's ticket is in flight during the row's last steps; the
-    // row's barriers separate this read of row_next from the write below
-    uint32_t next = 0;
-    sampled_kernel_row<E, NT, U>(a, tag, r, L, [&]() {
-      if (threadIdx.x == 0) next = queue_take(a);
-    });
-    if (threadIdx.x == 0) L.row_next = row_of(next + P);
-    lds_barrier();
-    r = L.row_next;
-  }
-  // Every ticket of this workgroup has been taken and its rows published
-  // (release); the last workgroup to get here sees all rows (acquire).
-  if (threadIdx.x == 0) {
-    const uint32_t done = __hip_atomic_fetch_add(a.ws_queue + kQueueDone, 1u, __ATOMIC_ACQ_REL,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    L.last = done + 1 == gridDim.x;
-  }
-  lds_barrier();
-  if (L.last) {
-    if (threadIdx.x == 0) {
-      store_agent(a.ws_queue + kQueueNext, 0u);
-      store_agent(a.ws_queue + kQueueDone, 0u);
-    }
-    words_tail<NT>(a, tag, *reinterpret_cast<TailScratch*>(&L.c));
-  }
+  row_queue_loop<NT>(a, tag, L, [&](int r, auto hook) { sampled_kernel_row<E, NT, U>(a, tag, r, L, hook); });
 }
 
 // Workgroups of the sampled kernel that fit on the current device at once
@@ -152,13 +104,8 @@ static int sampled_resident(int cus) {
   int dev = 0;
   if (cus <= 0 || hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
   if (dev < 64 && cached[dev] > 0) return cached[dev];
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, verify_sampled_kernel<E, kVerifyThreads, SampledDepth<E>::kGreedy>,
-                                                   kVerifyThreads, 0) != hipSuccess ||
-      per_cu <= 0)
-    return 0;
-  const int n = per_cu * cus;
-  if (dev < 64) cached[dev] = n;
+  const int n = resident_groups(verify_sampled_kernel<E, kVerifyThreads, SampledDepth<E>::kGreedy>, kVerifyThreads, cus);
+  if (dev < 64 && n > 0) cached[dev] = n;
   return n;
 }
 
