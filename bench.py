@@ -31,7 +31,8 @@ HBM_PEAK_GBPS = 8000.0
 SPREAD_BLOCK = 10
 ROTATE_BYTES = 1 << 30
 KERNEL_SOURCES = ("csrc/device.hpp", "csrc/row_stream.hpp", "csrc/sampled_row.hpp", "csrc/verify_common.hpp",
-                  "csrc/verify.hip", "csrc/sampled.hip", "csrc/confidence.hip", "csrc/kernels.hpp")
+                  "csrc/verify.hip", "csrc/sampled.hip", "csrc/confidence.hip", "csrc/kernels.hpp",
+                  "csrc/row_queue.hpp", "csrc/probabilistic.hip", "csrc/probabilistic.hpp")
 
 
 def kernel_source_sha():
@@ -231,7 +232,8 @@ def pool_rate(wl, cores, budget_s):
                     temperature=wl.temperature, top_k=wl.top_k, top_p=wl.top_p, min_p=wl.min_p,
                     draft_logits=None)
         ctx = multiprocessing.get_context("spawn")
-        with ctx.Pool(cores, initializer=_pool_init, initargs=(meta, names)) as pool:
+        pool = ctx.Pool(cores, initializer=_pool_init, initargs=(meta, names))
+        try:
             pool.map(_pool_task, range(min(cores, wl.B)))          # start-up, not timed
             rows, n, nxt = 0, 0, 0
             t0 = time.perf_counter()
@@ -241,6 +243,14 @@ def pool_rate(wl, cores, budget_s):
                 rows += sum(pool.map(_pool_task, chunk, chunksize=1))
                 n += len(chunk)
             dt = time.perf_counter() - t0
+            # workers leave on their own (no signal): under a profiler that
+            # hooks signals, terminated workers have failed to exit
+            pool.close()
+        except BaseException:
+            pool.terminate()
+            raise
+        finally:
+            pool.join()
     finally:
         for shm in shms:
             shm.close()
@@ -410,9 +420,11 @@ def bench_probabilistic(args, vsv, torch):
                             V=V, draft_temperature="the request's target temperature", data_seed=wl._spec["data_seed"],
                             philox_seed=wl.seed, slow_rows_last_launch=slow),
                 roofline=dict(bound="hbm", kernel="verify_probabilistic_kernel", achieved=achieved,
-                              peak=HBM_PEAK_GBPS, unit="GB/s", frac=achieved / HBM_PEAK_GBPS, traffic=None,
+                              peak=HBM_PEAK_GBPS, unit="GB/s", frac=achieved / HBM_PEAK_GBPS,
+                              traffic=measured_traffic("verify_probabilistic_kernel", "probabilistic"),
                               bytes_per_launch=nbytes, launch_us=ms * 1e3,
-                              note="exact multi-pass kernel: bound by its passes over rows held in the caches"))
+                              note="each verify row streamed once, then its draft row; sampled rows re-read "
+                                   "their candidate vectors"))
     if not args.no_cpu_baseline:
         from oracle.probabilistic import verify_probabilistic
         t0 = time.perf_counter()
