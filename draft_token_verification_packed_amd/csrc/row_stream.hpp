@@ -246,6 +246,30 @@ __device__ __forceinline__ void load_group(u32x4* dst, const u32x4* __restrict__
   for (int u = 0; u < U; ++u) dst[u] = load_stream(vp + min(base + u * NT, nvec - 1));
 }
 
+// Cache policy of a buffer load: 0 normal, 2 nontemporal.
+constexpr int kLoadNormal = 0;
+constexpr int kLoadStream = 2;
+
+// The same group through a buffer resource over the row's nvec body
+// vectors: the lane's byte offset is fixed and the group's is uniform (a
+// scalar offset), so a load costs no vector address arithmetic. Vectors
+// past the body read as zero without touching memory; the partial group is
+// reduced with those vectors masked.
+template <int NT, int U, int kAux>
+__device__ __forceinline__ void load_group_rsrc(u32x4* dst, __amdgpu_buffer_rsrc_t rsrc, int h) {
+  const int lane_off = static_cast<int>(threadIdx.x) * 16;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    dst[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rsrc, lane_off, (h * (U * NT) + u * NT) * 16, kAux));
+}
+
+// Buffer resource over n 16-byte vectors at p (nothing when n is 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t vec_rsrc(const void* p, int n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, n * 16, 0x00020000);
+}
+
+
 // Stream row[0 .. V) into this thread's partial. c = log2(e) / T. `hook` runs
 // once, right after the first group's loads are issued, so loads it issues
 // overlap the stream instead of trailing it. `keep` receives the thread's
@@ -260,7 +284,7 @@ __device__ __forceinline__ void stream_row(const E* __restrict__ row, int V, flo
   if (head > V) head = V;
   const int nvec = (V - head) / N;
   const int body_end = head + nvec * N;
-  const u32x4* __restrict__ vp = reinterpret_cast<const u32x4*>(row + head);
+  const __amdgpu_buffer_rsrc_t rsrc = vec_rsrc(row + head, nvec);
 
   // Full groups of U vectors per thread, two buffers in turn: while one
   // group is reduced the next one's loads are in flight. The group after the
@@ -270,17 +294,17 @@ __device__ __forceinline__ void stream_row(const E* __restrict__ row, int V, flo
   const int nfull = nvec / G;
   if (nvec > 0) {
     u32x4 a[U], b[U];
-    load_group<NT, U>(a, vp, 0, nvec);
+    load_group_rsrc<NT, U, kLoadStream>(a, rsrc, 0);
     hook();
     int g = 0;
     for (; g + 2 <= nfull; g += 2) {
-      load_group<NT, U>(b, vp, g + 1, nvec);
+      load_group_rsrc<NT, U, kLoadStream>(b, rsrc, g + 1);
       take_group<E, U, NT, kRank, false, Keep, NoCapture, kMax3>(p, a, g * G + tid, head, c, xd, d, keep);
-      load_group<NT, U>(a, vp, g + 2, nvec);
+      load_group_rsrc<NT, U, kLoadStream>(a, rsrc, g + 2);
       take_group<E, U, NT, kRank, false, Keep, NoCapture, kMax3>(p, b, (g + 1) * G + tid, head, c, xd, d, keep);
     }
     if (g < nfull) {
-      load_group<NT, U>(b, vp, g + 1, nvec);
+      load_group_rsrc<NT, U, kLoadStream>(b, rsrc, g + 1);
       take_group<E, U, NT, kRank, false, Keep, NoCapture, kMax3>(p, a, g * G + tid, head, c, xd, d, keep);
       take_group<E, U, NT, kRank, true, Keep, NoCapture, kMax3>(p, b, nfull * G + tid, head, c, xd, d, keep, nvec);
     } else {

@@ -676,6 +676,22 @@ struct VmPlan {
   int blocks;  // blocks of eight entry rows (blocks * NT of them)
 };
 
+// The code of a vector maximum: for bfloat16 rows the maximum is a bfloat16
+// value, so its code is exact and needs no rounding (-0 is first made +0);
+// float32 maxima are rounded up (up_code).
+template <typename E>
+__device__ __forceinline__ int vmax_code(float v) {
+  if constexpr (sizeof(E) == 2) {
+    const uint32_t b = __float_as_uint(v + 0.0f);
+    const uint32_t flip = (static_cast<uint32_t>(static_cast<int32_t>(b) >> 31) & 0x7FFFu) | 0x8000u;
+    return static_cast<int>((b >> 16) ^ flip);
+  } else {
+    return up_code(v);
+  }
+}
+
+template <bool B> struct BoolC { static constexpr bool value = B; };
+
 // Pass 1: stream one sampled row for the statistics of stream_row, and leave
 // the code of every vector's maximum in L.u.vm. Loads use the caches' normal
 // policy so that pass 2's reads of a few vectors find them there.
@@ -690,12 +706,18 @@ __device__ __forceinline__ VmPlan stream_sampled(const E* __restrict__ row, int 
   if (head > V) head = V;
   const int nvec = (V - head) / N;
   const int body_end = head + nvec * N;
-  const u32x4* __restrict__ vp = reinterpret_cast<const u32x4*>(row + head);
+  // Body vectors through a buffer resource: the lane's byte offset is fixed
+  // and a step's is uniform (a scalar offset), so loads cost no vector
+  // address arithmetic; vectors past the body read as zero.
+  const __amdgpu_buffer_rsrc_t rsrc = vec_rsrc(row + head, nvec);
+  const int lane_off = tid * 16;
+  auto load = [&](int first) {   // vector first + tid
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_off, first * 16, kLoadNormal));
+  };
   // Rolling slots: slot u holds vector g*G + u*NT + tid of group g; it is
   // decoded, then reloaded at once with the same vector of group g+1, so
   // U-1 vectors per lane are always in flight and the loop carries no
-  // register copies (a copy at the latch would wait for every load). Loads
-  // are unconditional (clamped to the row's last vector).
+  // register copies (a copy at the latch would wait for every load).
   constexpr int G = U * NT;
   const int nfull = nvec / G;
   const int steps = nvec > 0 ? (nvec > nfull * G ? nfull + 1 : nfull) * U : 0;
@@ -706,13 +728,10 @@ __device__ __forceinline__ VmPlan stream_sampled(const E* __restrict__ row, int 
   u32x4 slot[U];
   if (nvec > 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) slot[u] = vp[min(tid + u * NT, nvec - 1)];
+    for (int u = 0; u < U; ++u) slot[u] = load(u * NT);
   }
   if (has_head) take_scalar<false>(p, xh, tid, c, INFINITY, 0);
 
-  // the running maximum of the current entry (uniform countdown of steps)
-  float run = -INFINITY;
-  int left = plan.S;
   int bmax = 0;   // the largest code of the current block
   auto push = [&](int code) {
     L.u.vm.l1[plan.rows * NT + tid] = static_cast<uint16_t>(code);
@@ -723,22 +742,31 @@ __device__ __forceinline__ VmPlan stream_sampled(const E* __restrict__ row, int 
       bmax = 0;
     }
   };
-  auto note = [&](float vmax) {
-    run = fmaxf(run, vmax);
-    if (--left == 0) {
-      push(up_code(run));
-      run = -INFINITY;
-      left = plan.S;
-    }
-  };
-  if (nvec > 0) {
+  // kOne: one entry per vector (S = 1), its code straight from the vector's
+  // maximum; otherwise the running maximum of S slot steps (uniform
+  // countdown) makes one entry
+  auto body = [&](auto one) {
+    constexpr bool kOne = decltype(one)::value;
+    float run = -INFINITY;
+    int left = plan.S;
+    auto note = [&](float vmax) {
+      if constexpr (kOne) {
+        push(vmax_code<E>(vmax));
+      } else {
+        run = fmaxf(run, vmax);
+        if (--left == 0) {
+          push(up_code(run));
+          run = -INFINITY;
+          left = plan.S;
+        }
+      }
+    };
     for (int g = 0; g < nfull; ++g) {
-      const int v = g * G + tid;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float f[N];
         const float vmax = vec_max<E>(slot[u], f);
-        slot[u] = vp[min(v + G + u * NT, nvec - 1)];
+        slot[u] = load((g + 1) * G + u * NT);
         take_floats<N>(p, f, vmax, c);
         note(vmax);
       }
@@ -757,7 +785,15 @@ __device__ __forceinline__ VmPlan stream_sampled(const E* __restrict__ row, int 
         note(vmax);
       }
     }
-    if (left != plan.S) push(up_code(run));
+    if constexpr (!kOne) {
+      if (left != plan.S) push(up_code(run));
+    }
+  };
+  if (nvec > 0) {
+    if (plan.S == 1)
+      body(BoolC<true>{});
+    else
+      body(BoolC<false>{});
     if (plan.rows & 7) {
       L.u.vm.l2[plan.blocks * NT + tid] = static_cast<uint16_t>(bmax);
       ++plan.blocks;
