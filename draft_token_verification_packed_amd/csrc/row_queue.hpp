@@ -37,7 +37,10 @@ __device__ __forceinline__ void row_queue_loop(const VerifyArgs& a, uint32_t tag
   };
   if (threadIdx.x == 0) L.row_next = row_of(a.ordered ? blockIdx.x : queue_take(a));
   lds_barrier();
-  int r = L.row_next;
+  // the row is the same for every lane: read it as a scalar, so that what is
+  // derived from it (row pointers, buffer resources) stays in scalar
+  // registers
+  int r = __builtin_amdgcn_readfirstlane(L.row_next);
   while (r < a.R) {
     // the next row's ticket is in flight during the row's last steps; the
     // row's barriers separate this read of row_next from the write below
@@ -47,7 +50,7 @@ __device__ __forceinline__ void row_queue_loop(const VerifyArgs& a, uint32_t tag
     });
     if (threadIdx.x == 0) L.row_next = row_of(next + P);
     lds_barrier();
-    r = L.row_next;
+    r = __builtin_amdgcn_readfirstlane(L.row_next);
   }
   // Every ticket of this workgroup has been taken and its rows published
   // (release); the last workgroup to get here sees all rows (acquire).
