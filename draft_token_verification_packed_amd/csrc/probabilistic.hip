@@ -151,8 +151,8 @@ __device__ bool draft_law_stream(const E* __restrict__ y, int V, double Td, Samp
   if (!(Td > 0.0)) {
     RowPartial p;
     partial_init(p);
-    GroupKeep<U> keep{};
-    stream_row<E, NT, U, false, GroupKeep<U>, NoHook, true>(y, V, 1.4426950408889634f, INFINITY, 0, p, keep);
+    QueueKeep<E, U> keep{};
+    stream_row<E, NT, U, false, QueueKeep<E, U>, NoHook, true>(y, V, 1.4426950408889634f, INFINITY, 0, p, keep);
     const RowStats st = finish_row_lean<E, NT, U, false>(p, L.ls, keep, y, V);
     q.my = st.max;
     q.h = st.argmax;
@@ -580,9 +580,9 @@ __device__ __forceinline__ void prob_kernel_row(const VerifyArgs& a, const ProbA
     // the target row's maximum and lowest arg-max
     RowPartial p;
     partial_init(p);
-    GroupKeep<U> keep{};
+    QueueKeep<E, U> keep{};
     constexpr float kLog2e = 1.4426950408889634f;
-    stream_row<E, NT, U, false, GroupKeep<U>, NoHook, true>(row, a.V, kLog2e, INFINITY, 0, p, keep);
+    stream_row<E, NT, U, false, QueueKeep<E, U>, NoHook, true>(row, a.V, kLog2e, INFINITY, 0, p, keep);
     after_stream();
     const RowStats st = finish_row_lean<E, NT, U, false>(p, L.ls, keep, row, a.V);
     token = st.argmax == INT32_MAX ? 0 : st.argmax;

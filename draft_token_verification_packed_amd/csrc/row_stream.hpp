@@ -59,11 +59,29 @@ template <int NT> struct RowScratch {
 // rows), or nothing.
 struct NoKeep {
   static constexpr bool kOn = false;
+  static constexpr bool kReload = false;
 };
 template <int U> struct GroupKeep {
   static constexpr bool kOn = true;
+  static constexpr bool kReload = false;
   u32x4 w[U];
 };
+// The stream keeps no vectors: the few lanes whose best group holds the
+// block maximum read that group again at the end (one load round trip)
+// instead of every lane copying a group into registers whenever its best
+// improves.
+struct ReloadKeep {
+  static constexpr bool kOn = false;
+  static constexpr bool kReload = true;
+};
+// Greedy rows inside the persistent sampled and probabilistic kernels:
+// bfloat16 rows, whose stream is bound by its vector instructions, drop the
+// per-group copies and read the best group again; float32 rows keep it
+// (their stream is not, and the extra round trip would lengthen the rows
+// that end a launch).
+template <typename E, int U> struct QueueKeepT { using type = GroupKeep<U>; };
+template <int U> struct QueueKeepT<uint16_t, U> { using type = ReloadKeep; };
+template <typename E, int U> using QueueKeep = typename QueueKeepT<E, U>::type;
 
 __device__ __forceinline__ void partial_init(RowPartial& p) {
   p.best = -INFINITY;
@@ -463,12 +481,25 @@ __device__ __forceinline__ RowStats finish_row_lean(const RowPartial& p, LeanScr
     mg = fmaxf(mg, sc.mc[k]);
   }
   int idx = INT32_MAX;
-  if constexpr (Keep::kOn) {
+  if constexpr (Keep::kOn || Keep::kReload) {
     if (p.best == m) {
       const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
       int head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(E));
       if (head > V) head = V;
-      idx = lane_argmax<E, NT, U>(p, keep, head, (V - head) / N);
+      const int nvec = (V - head) / N;
+      if constexpr (Keep::kReload) {
+        GroupKeep<U> again;
+        if (p.bvec == 2) {
+          const __amdgpu_buffer_rsrc_t rsrc = vec_rsrc(row + head, nvec);
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            again.w[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       rsrc, (p.bpos + u * NT) * 16, 0, kLoadNormal));
+        }
+        idx = lane_argmax<E, NT, U>(p, again, head, nvec);
+      } else {
+        idx = lane_argmax<E, NT, U>(p, keep, head, nvec);
+      }
     }
   }
   float sl = (p.mc > -FLT_MAX) ? static_cast<float>(ldexp(p.s, static_cast<int>(fmaxf(p.mc - mg, -2000.f)))) : 0.f;

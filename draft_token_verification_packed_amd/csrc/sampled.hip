@@ -30,9 +30,9 @@ __device__ __forceinline__ void sampled_kernel_row(const VerifyArgs& a, uint32_t
   } else {
     RowPartial p;
     partial_init(p);
-    GroupKeep<U> keep{};
+    QueueKeep<E, U> keep{};
     constexpr float kLog2e = 1.4426950408889634f;
-    stream_row<E, NT, U, false, GroupKeep<U>, NoHook, true>(row, a.V, kLog2e, INFINITY, 0, p, keep);
+    stream_row<E, NT, U, false, QueueKeep<E, U>, NoHook, true>(row, a.V, kLog2e, INFINITY, 0, p, keep);
     after_stream();
     const RowStats res = finish_row_lean<E, NT, U, false>(p, L.ls, keep, row, a.V);
     token = res.argmax;

@@ -122,6 +122,29 @@ __device__ __forceinline__ void take_floats(RowPartial& p, const float* f, float
   p.s += static_cast<double>(tree_sum<N>(e));
 }
 
+// The same for one vector of a group whose exponentials are summed in float
+// before they reach the float64 sum: `gs` is the group's running float sum,
+// rescaled with p.s when the exponent reference moves (both by an exact
+// power of two). The caller adds gs to p.s once per group and keeps the
+// group's maximum.
+template <int N>
+__device__ __forceinline__ void take_floats_group(RowPartial& p, const float* f, float vmax, float c, float& gs) {
+  const float y = vmax * c;
+  if (y > p.mc && y < FLT_MAX) {
+    const float nm = ceilf(y);
+    const bool had = p.mc > -FLT_MAX;
+    const int d = static_cast<int>(fmaxf(p.mc - nm, -2000.f));
+    p.s = had ? ldexp(p.s, d) : 0.0;
+    gs = had ? ldexpf(gs, d) : 0.f;
+    p.mc = nm;
+  }
+  const float nmc = -p.mc;
+  float e[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) e[k] = fast_exp2(fmaf(f[k], c, nmc));
+  gs += tree_sum<N>(e);
+}
+
 // ---------------------------------------------------------------- deciding
 
 struct Pick {
@@ -762,13 +785,33 @@ __device__ __forceinline__ VmPlan stream_sampled(const E* __restrict__ row, int 
       }
     };
     for (int g = 0; g < nfull; ++g) {
+      if constexpr (sizeof(E) == 2) {
+        // a bfloat16 group's U vectors: maxima by IEEE maximum (a NaN
+        // propagates and is remembered), exponentials summed in float, one
+        // float64 add (float32 rows, with deeper slots, keep the per-vector
+        // form: the group form spills there)
+        float gmax = -INFINITY, gs = 0.f;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float f[N];
-        const float vmax = vec_max<E>(slot[u], f);
-        slot[u] = load((g + 1) * G + u * NT);
-        take_floats<N>(p, f, vmax, c);
-        note(vmax);
+        for (int u = 0; u < U; ++u) {
+          float f[N];
+          const float vmax = vec_max<E, true>(slot[u], f);
+          slot[u] = load((g + 1) * G + u * NT);
+          take_floats_group<N>(p, f, vmax, c, gs);
+          note(vmax);
+          gmax = __builtin_elementwise_maximum(gmax, vmax);
+        }
+        p.s += static_cast<double>(gs);
+        p.best = __builtin_elementwise_maximum(p.best, gmax);
+        p.bad |= (gmax != gmax) ? 1 : 0;
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float f[N];
+          const float vmax = vec_max<E>(slot[u], f);
+          slot[u] = load((g + 1) * G + u * NT);
+          take_floats<N>(p, f, vmax, c);
+          note(vmax);
+        }
       }
     }
     if (nvec > nfull * G) {
