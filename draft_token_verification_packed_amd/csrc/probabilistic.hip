@@ -544,7 +544,8 @@ __device__ __noinline__ void slow_support(const E* __restrict__ row, int V, floa
 }
 
 // One row of the batch: its token, acceptance and word. `after_stream` is
-// called once the target row has been streamed.
+// called once the target row has been streamed, with true when the row's
+// remaining work is long (a sampled target).
 template <typename E, int NT, int U, typename Hook>
 __device__ __forceinline__ void prob_kernel_row(const VerifyArgs& a, const ProbArgs& pa, uint32_t tag, int r,
                                                 SampledLds<NT>& L, Hook after_stream) {
@@ -583,7 +584,7 @@ __device__ __forceinline__ void prob_kernel_row(const VerifyArgs& a, const ProbA
     QueueKeep<E, U> keep{};
     constexpr float kLog2e = 1.4426950408889634f;
     stream_row<E, NT, U, false, QueueKeep<E, U>, NoHook, true>(row, a.V, kLog2e, INFINITY, 0, p, keep);
-    after_stream();
+    after_stream(false);
     const RowStats st = finish_row_lean<E, NT, U, false>(p, L.ls, keep, row, a.V);
     token = st.argmax == INT32_MAX ? 0 : st.argmax;
     if (!(st.max < INFINITY) || st.argmax == INT32_MAX || st.sum != st.sum) bits |= VSV_FLAG_LOGITS;
@@ -594,7 +595,7 @@ __device__ __forceinline__ void prob_kernel_row(const VerifyArgs& a, const ProbA
     RowPartial p;
     partial_init(p);
     const VmPlan plan = stream_sampled<E, NT, SampledDepth<E>::kPass1>(row, a.V, c, p, L);
-    after_stream();
+    after_stream(true);
     const NoKeep nk;
     const RowStats st = finish_row_lean<E, NT, U, false>(p, L.ls, nk, row, a.V);
     mx = st.max;

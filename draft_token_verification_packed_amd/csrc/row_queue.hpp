@@ -22,8 +22,15 @@ __device__ __forceinline__ uint32_t queue_take(const VerifyArgs& a) {
 }
 
 // Runs row(r, hook) for every row this workgroup is handed, then the end of
-// the call. Lds provides `row_next`, `last` and a candidate area `c` that
-// the per-request scan may use as staging once every row is done.
+// the call. The row function calls hook(long_tail) once its row has been
+// streamed; long_tail says that the row's work after the stream is long (a
+// sampled row's selection and draw). The next ticket is taken then, unless
+// the row's tail is long and the queue is near its end: a workgroup that
+// commits to a row while it still has tens of microseconds of work would
+// leave that row waiting while other workgroups run out of rows. Such a
+// ticket is taken when the row is done. Lds provides `row_next`, `ticket`,
+// `last` and a candidate area `c` that the per-request scan may use as
+// staging once every row is done.
 template <int NT, typename Lds, typename RowFn>
 __device__ __forceinline__ void row_queue_loop(const VerifyArgs& a, uint32_t tag, Lds& L, RowFn row) {
   static_assert(sizeof(TailScratch) <= sizeof(L.c), "tail staging aliases the candidate area");
@@ -35,22 +42,40 @@ __device__ __forceinline__ void row_queue_loop(const VerifyArgs& a, uint32_t tag
   auto row_of = [&](uint32_t q) -> int {
     return q < R ? (a.ordered ? a.ws_perm[q] : static_cast<int>(q)) : a.R;
   };
-  if (threadIdx.x == 0) L.row_next = row_of(a.ordered ? blockIdx.x : queue_take(a));
+  if (threadIdx.x == 0) {
+    const uint32_t q = a.ordered ? blockIdx.x : queue_take(a);
+    L.ticket = static_cast<int>(q < R ? q : R);
+    L.row_next = row_of(q);
+  }
   lds_barrier();
   // the row is the same for every lane: read it as a scalar, so that what is
   // derived from it (row pointers, buffer resources) stays in scalar
   // registers
   int r = __builtin_amdgcn_readfirstlane(L.row_next);
+  uint32_t q = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(L.ticket));
   while (r < a.R) {
-    // the next row's ticket is in flight during the row's last steps; the
-    // row's barriers separate this read of row_next from the write below
+    // the next ticket is in flight during the row's last steps; the row's
+    // barriers separate these reads of row_next and ticket from the writes
+    // below
     uint32_t next = 0;
-    row(r, [&]() {
-      if (threadIdx.x == 0) next = queue_take(a);
+    bool taken = false;
+    // uniform: more than two rows per workgroup are still to be handed out
+    const bool plenty = q + 2 * gridDim.x < R;
+    row(r, [&](bool long_tail) {
+      if (!taken && (plenty || !long_tail)) {
+        if (threadIdx.x == 0) next = queue_take(a);
+        taken = true;
+      }
     });
-    if (threadIdx.x == 0) L.row_next = row_of(next + P);
+    if (threadIdx.x == 0) {
+      if (!taken) next = queue_take(a);
+      const uint32_t nq = next + P;
+      L.ticket = static_cast<int>(nq < R ? nq : R);
+      L.row_next = row_of(nq);
+    }
     lds_barrier();
     r = __builtin_amdgcn_readfirstlane(L.row_next);
+    q = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(L.ticket));
   }
   // Every ticket of this workgroup has been taken and its rows published
   // (release); the last workgroup to get here sees all rows (acquire).

@@ -33,7 +33,7 @@ __device__ __forceinline__ void sampled_kernel_row(const VerifyArgs& a, uint32_t
     QueueKeep<E, U> keep{};
     constexpr float kLog2e = 1.4426950408889634f;
     stream_row<E, NT, U, false, QueueKeep<E, U>, NoHook, true>(row, a.V, kLog2e, INFINITY, 0, p, keep);
-    after_stream();
+    after_stream(false);
     const RowStats res = finish_row_lean<E, NT, U, false>(p, L.ls, keep, row, a.V);
     token = res.argmax;
     // float log2 of a sum holding the maximum's own term (at least 1/2)

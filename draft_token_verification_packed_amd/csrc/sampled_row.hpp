@@ -95,6 +95,7 @@ template <int NT> struct SampledLds {
   RowScratch<NT> rs;
   LeanScratch<NT> ls;
   int row_next;  // the workgroup's next row (row queue)
+  int ticket;    // its ticket (position in the queue)
   int last;      // this workgroup finished the call's last row
 };
 
@@ -1195,7 +1196,8 @@ struct SampledOut {
 };
 
 // One workgroup samples row `row` of request `req` (local row j) at
-// temperature T > 0. `after_stream` runs once the row has been read.
+// temperature T > 0. `after_stream(true)` runs once the row has been read
+// (true: a long tail of work follows).
 template <typename E, int NT, int U, typename Hook>
 __device__ __forceinline__ SampledOut sampled_row(const VerifyArgs& a, const E* __restrict__ row, int req, int j, float T,
                                   SampledLds<NT>& L, Hook after_stream) {
@@ -1214,7 +1216,7 @@ __device__ __forceinline__ SampledOut sampled_row(const VerifyArgs& a, const E* 
   RowPartial p;
   partial_init(p);
   const VmPlan plan = stream_sampled<E, NT, U>(row, a.V, c, p, L);
-  after_stream();
+  after_stream(true);   // selection and draw follow
   const NoKeep nokeep;
   const RowStats res = finish_row_lean<E, NT, U, false>(p, L.ls, nokeep, row, a.V);
   // the sum holds the maximum's own term (at least 1/2), so float log2
