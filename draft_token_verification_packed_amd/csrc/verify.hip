@@ -444,12 +444,6 @@ __global__ __launch_bounds__(NT) void verify_greedy_kernel(VerifyArgs a) {
   if (p == plan.P - 1) greedy_tail<NT, kRelaxed>(a, plan, tag, tail, s_lo);
 }
 
-// Words of a part's statistics (row-major in the workspace's partials area,
-// parts 0 .. P - 2 of row r at slots r * (P - 1) + p, kPartStatWords words
-// per slot): max, its lowest index, exponent reference, the float64 sum as
-// two halves, rank count.
-constexpr int kPartStatWords = 6;
-
 // One workgroup per row part (a.parts = P parts per row, 1 <= P <=
 // kMaxRowParts), for batches with more rows than CUs. The parts of a row
 // are consecutive workgroups, each streaming an equal share of the row's
@@ -466,22 +460,14 @@ __global__ __launch_bounds__(NT) void verify_greedy_rows_kernel(VerifyArgs a) {
   __shared__ int s_prot[VSV_MAX_PROTECTED];
   static_assert(VSV_MAX_PROTECTED % NT == 0 || NT % VSV_MAX_PROTECTED == 0, "protected ids per thread");
   constexpr int kProtPer = VSV_MAX_PROTECTED >= NT ? VSV_MAX_PROTECTED / NT : 1;
-  constexpr int N = Elem<E>::kVec;
   const int P = a.parts;
   const int r = static_cast<int>(blockIdx.x) / P;
   const int part = static_cast<int>(blockIdx.x) - r * P;
   const uint32_t tag = call_tag(a);
   const E* __restrict__ row = static_cast<const E*>(a.logits) + static_cast<int64_t>(r) * a.ld;
   // the part's elements [e0, e1): equal shares of the row's 16-byte body
-  int e0 = 0, e1 = a.V;
-  if (P > 1) {
-    const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
-    int head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(E));
-    if (head > a.V) head = a.V;
-    const int64_t nv = (a.V - head) / N;
-    e0 = part == 0 ? 0 : head + static_cast<int>(nv * part / P) * N;
-    e1 = part == P - 1 ? a.V : head + static_cast<int>(nv * (part + 1) / P) * N;
-  }
+  int e0, e1;
+  part_range<E>(row, a.V, P, part, e0, e1);
   const bool last = part == P - 1;
   const int owner = a.owner[r];
   RowMeta m{-1, 0, 0, -1};
@@ -529,18 +515,9 @@ __global__ __launch_bounds__(NT) void verify_greedy_rows_kernel(VerifyArgs a) {
   }
   const RowStats st = finish_row_lean<E, NT, U, kRelaxed>(p, scr, keep, row + e0, e1 - e0);
   const int idx = st.argmax == INT32_MAX ? INT32_MAX : e0 + st.argmax;
-  uint64_t* slots = a.ws_part + static_cast<size_t>(r) * (P - 1) * kPartStatWords;
+  uint64_t* slots = part_slots(a, r, P);
   if (!last) {
-    if (threadIdx.x < kPartStatWords) {
-      const uint64_t sb = __builtin_bit_cast(uint64_t, st.sum);
-      const uint32_t v[kPartStatWords] = {__float_as_uint(st.max), static_cast<uint32_t>(idx),
-                                          __float_as_uint(st.mref), static_cast<uint32_t>(sb),
-                                          static_cast<uint32_t>(sb >> 32), static_cast<uint32_t>(st.rank)};
-      uint32_t mine = v[0];
-#pragma unroll
-      for (int f = 1; f < kPartStatWords; ++f) mine = threadIdx.x == f ? v[f] : mine;
-      store_agent64(slots + static_cast<size_t>(part) * kPartStatWords + threadIdx.x, tagged(tag, mine));
-    }
+    put_part_stats(slots, part, st, idx, tag);
   } else if (threadIdx.x < kWave) {
     // wave 0: lane q < P - 1 gathers part q's words, lane P - 1 holds this
     // part's result, and one wave reduction merges them (largest max,
@@ -550,30 +527,7 @@ __global__ __launch_bounds__(NT) void verify_greedy_rows_kernel(VerifyArgs a) {
     RowRed mine{0.0, -INFINITY, INT32_MAX, -FLT_MAX, 0};
     int stalled = 0;
     if (lane < P - 1) {
-      const uint64_t* hw = slots + static_cast<size_t>(lane) * kPartStatWords;
-      uint64_t w[kPartStatWords];
-      auto load_all = [&]() {
-#pragma unroll
-        for (int f = 0; f < kPartStatWords; ++f) w[f] = load_agent64(hw + f);
-      };
-      auto complete = [&]() {
-        bool ok = true;
-#pragma unroll
-        for (int f = 0; f < kPartStatWords; ++f) ok = ok && static_cast<uint32_t>(w[f] >> 32) == tag;
-        return ok;
-      };
-      int budget = kPollBudget;
-      load_all();
-      while (!complete() && budget > 0) {
-        --budget;
-        __builtin_amdgcn_s_sleep(2);
-        load_all();
-      }
-      stalled = complete() ? 0 : 1;
-      const uint64_t sb = (static_cast<uint64_t>(static_cast<uint32_t>(w[4])) << 32) | static_cast<uint32_t>(w[3]);
-      mine = RowRed{__builtin_bit_cast(double, sb), __uint_as_float(static_cast<uint32_t>(w[0])),
-                    static_cast<int>(static_cast<uint32_t>(w[1])), __uint_as_float(static_cast<uint32_t>(w[2])),
-                    static_cast<int>(static_cast<uint32_t>(w[5]))};
+      mine = get_part_stats(slots, lane, tag, stalled);
     } else if (lane == P - 1) {
       mine = RowRed{st.sum, st.max, idx, st.mref, st.rank};
     }

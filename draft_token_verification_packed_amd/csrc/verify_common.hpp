@@ -51,6 +51,78 @@ __device__ __forceinline__ void end_call(const VerifyArgs& a, uint32_t tag) {
   if (threadIdx.x == 0) store_agent(a.ws_epoch, tag & 0x7FFFFFFFu);
 }
 
+// ---------------------------------------------------------------- row parts
+
+// A row streamed in P parts by P workgroups: its 16-byte body cut into
+// equal shares (the first part also takes the elements before the body, the
+// last those after it). Part p holds elements [e0, e1).
+template <typename E>
+__device__ __forceinline__ void part_range(const E* row, int V, int P, int part, int& e0, int& e1) {
+  constexpr int N = Elem<E>::kVec;
+  e0 = 0;
+  e1 = V;
+  if (P > 1) {
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
+    int head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(E));
+    if (head > V) head = V;
+    const int64_t nv = (V - head) / N;
+    e0 = part == 0 ? 0 : head + static_cast<int>(nv * part / P) * N;
+    e1 = part == P - 1 ? V : head + static_cast<int>(nv * (part + 1) / P) * N;
+  }
+}
+
+// Words of a part's statistics (row-major in the workspace's partials area,
+// parts 0 .. P - 2 of row r at slots r * (P - 1) + p, kPartStatWords words
+// per slot): max, its lowest index, exponent reference, the float64 sum as
+// two halves, rank count.
+constexpr int kPartStatWords = 6;
+__device__ __forceinline__ uint64_t* part_slots(const VerifyArgs& a, int r, int P) {
+  return a.ws_part + static_cast<size_t>(r) * (P - 1) * kPartStatWords;
+}
+// Store part `part`'s statistics (threads 0 .. kPartStatWords - 1, one
+// tagged word each); idx is the row-relative index of the part's maximum.
+__device__ __forceinline__ void put_part_stats(uint64_t* slots, int part, const RowStats& st, int idx, uint32_t tag) {
+  if (threadIdx.x < kPartStatWords) {
+    const uint64_t sb = __builtin_bit_cast(uint64_t, st.sum);
+    const uint32_t v[kPartStatWords] = {__float_as_uint(st.max), static_cast<uint32_t>(idx),
+                                        __float_as_uint(st.mref), static_cast<uint32_t>(sb),
+                                        static_cast<uint32_t>(sb >> 32), static_cast<uint32_t>(st.rank)};
+    uint32_t mine = v[0];
+#pragma unroll
+    for (int f = 1; f < kPartStatWords; ++f) mine = threadIdx.x == f ? v[f] : mine;
+    store_agent64(slots + static_cast<size_t>(part) * kPartStatWords + threadIdx.x, tagged(tag, mine));
+  }
+}
+// Lane q < P - 1 of the merging wave: part q's statistics, polled until
+// they carry the call's tag (within the poll budget; `stalled` records a
+// give-up).
+__device__ __forceinline__ RowRed get_part_stats(const uint64_t* slots, int q, uint32_t tag, int& stalled) {
+  const uint64_t* hw = slots + static_cast<size_t>(q) * kPartStatWords;
+  uint64_t w[kPartStatWords];
+  auto load_all = [&]() {
+#pragma unroll
+    for (int f = 0; f < kPartStatWords; ++f) w[f] = load_agent64(hw + f);
+  };
+  auto complete = [&]() {
+    bool ok = true;
+#pragma unroll
+    for (int f = 0; f < kPartStatWords; ++f) ok = ok && static_cast<uint32_t>(w[f] >> 32) == tag;
+    return ok;
+  };
+  int budget = kPollBudget;
+  load_all();
+  while (!complete() && budget > 0) {
+    --budget;
+    __builtin_amdgcn_s_sleep(2);
+    load_all();
+  }
+  stalled = complete() ? 0 : 1;
+  const uint64_t sb = (static_cast<uint64_t>(static_cast<uint32_t>(w[4])) << 32) | static_cast<uint32_t>(w[3]);
+  return RowRed{__builtin_bit_cast(double, sb), __uint_as_float(static_cast<uint32_t>(w[0])),
+                static_cast<int>(static_cast<uint32_t>(w[1])), __uint_as_float(static_cast<uint32_t>(w[2])),
+                static_cast<int>(static_cast<uint32_t>(w[5]))};
+}
+
 // ---------------------------------------------------------------- rows
 
 // Per-row metadata: request, local row, draft token.
