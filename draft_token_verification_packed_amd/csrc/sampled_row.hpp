@@ -22,7 +22,9 @@
 // window of 10 T (or the min-p cut), or, for a top-k row, the k-th largest
 // vector maximum (a lower bound of the k-th largest element). A second pass
 // over the codes picks the vectors that may hold an element >= tau, reads
-// them again (they are still in the device's caches) and keeps those
+// them again (from the device's last-level cache when the batch is small,
+// mostly past the XCD's L2 otherwise: scattered 16-byte reads that cost one
+// round trip of latency and whole lines of traffic) and keeps those
 // elements in one candidate buffer. A 1024-bin histogram of (count, float64
 // weight) over the candidates then locates each cut; only the bin a cut
 // falls in is gathered and sorted. When the candidates cannot decide
