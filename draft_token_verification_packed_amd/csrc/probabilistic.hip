@@ -637,10 +637,8 @@ __device__ __forceinline__ void prob_kernel_row(const VerifyArgs& a, const ProbA
     if (fast_tau > -INFINITY && capture_row<E, NT>(row, a.V, fast_tau, fast_plan, L)) {
       const int nc = min(L.ncand, kCand);
       double corr = 0.0;
-      for (int k = threadIdx.x; k < nc; k += NT) {
-        const double xv = static_cast<double>(c[k].x);
-        corr += weight(c[k].x, mx, Td) - exp2((xv - static_cast<double>(mx)) * fast_c);
-      }
+      const double dc = c_gap(fast_c, Td);
+      for (int k = threadIdx.x; k < nc; k += NT) corr += stream_gap(c[k].x, mx, weight(c[k].x, mx, Td), dc);
       const double W = fast_wtot + block_reduce<NT>(corr, SumOp(), L.red_d);
       rank_candidates<E, NT>(L, nc, mx);
       // the candidates' weights, once, in LDS (the union u is free again)

@@ -164,6 +164,19 @@ __device__ __forceinline__ double weight(float x, float m, double T) {
   return exp((static_cast<double>(x) - static_cast<double>(m)) / T);
 }
 
+// The stream weighs an element with exp2((x - m) c), c = log2(e) / T rounded
+// to float; w = weight(x, m, T). The gap w - exp2((x - m) c) is
+// -w (delta + delta^2 / 2 + ...) with delta = (x - m) dc and
+// dc = c ln 2 - 1 / T (c_gap below). The float rounding of c bounds
+// |delta| by 6e-8 |x - m| / T, so the first omitted term, w delta^3 / 6, is
+// under float64 rounding of the total for every weight that is not itself
+// negligible (|x - m| / T up to thousands).
+__device__ __forceinline__ double c_gap(double c, double T) { return c * 0.69314718055994530942 - 1.0 / T; }
+__device__ __forceinline__ double stream_gap(float x, float m, double w, double dc) {
+  const double delta = (static_cast<double>(x) - static_cast<double>(m)) * dc;
+  return -w * (delta + 0.5 * delta * delta);
+}
+
 // Block-wide inclusive scans (every thread one value; NT <= 1024).
 template <int NT, typename T>
 __device__ __forceinline__ T block_scan_incl(T v, T* scr, T& total) {
@@ -239,6 +252,7 @@ struct CandLocator {
     // the stream summed every element with the rounded scale c; the
     // candidates' share is replaced by their exact weights
     double corr = 0.0;
+    const double dc = c_gap(c, T);
     const int n = L.ncand;
     for (int j = threadIdx.x; j < n; j += NT) {
       const float x = L.c.cand[j].x;
@@ -248,7 +262,7 @@ struct CandLocator {
       if (!kCode) {
         const double we = weight(x, m, T);
         atomicAdd(&L.u.post.mass[b], we);
-        corr += we - exp2((static_cast<double>(x) - static_cast<double>(m)) * c);
+        corr += stream_gap(x, m, we, dc);
       }
     }
     lds_barrier();
@@ -267,7 +281,7 @@ struct CandLocator {
         if (lc[k]) {
           const float v = bin_value(b);
           wb = weight(v, m, T);
-          corr += lc[k] * (wb - exp2((static_cast<double>(v) - static_cast<double>(m)) * c));
+          corr += lc[k] * stream_gap(v, m, wb, dc);
           lm[k] = lc[k] * wb;
           L.u.post.mass[b] = wb;   // per-element weight of the bin's value
         } else {
