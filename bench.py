@@ -411,12 +411,16 @@ def bench_probabilistic(args, vsv, torch):
     ms = ev[0].elapsed_time(ev[1]) / steps
     assert int(out["error_flag"].item()) == 0
     slow = int(out["slow_rows"].item())     # rows of the last launch that took the whole-row path
-    nbytes = (R + wl.D) * V * 2     # every target and draft row read once
+    # every target row read once, and the draft rows of sampled requests (a
+    # greedy target's law is a point mass: its drafts are decided without q)
+    d_sampled = int(sum(int(wl.offsets[i + 1] - wl.offsets[i]) - 1 for i in range(B) if wl.temperature[i] > 0))
+    nbytes = (R + d_sampled) * V * 2
     achieved = nbytes / (ms * 1e-3) / 1e9
     line = dict(metric="probabilistic-draft verified rows/sec, B=512 K=7 V=152064", value=R / (ms * 1e-3),
                 unit="rows/s", n_gpus=1, steps=steps, warmup=warm, ms_per_step=ms, higher_is_better=True,
                 scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
                 config=dict(workload="probabilistic-draft verify, " + wl.name.split(", ", 1)[1], B=B, R=R, D=wl.D,
+                            draft_rows_read=d_sampled,
                             V=V, draft_temperature="the request's target temperature", data_seed=wl._spec["data_seed"],
                             philox_seed=wl.seed, slow_rows_last_launch=slow),
                 roofline=dict(bound="hbm", kernel="verify_probabilistic_kernel", achieved=achieved,
