@@ -106,12 +106,7 @@ def build_steps(vsv, torch, wl):
             ccall, _ = vsv.prepare_confidence(dl, sel)
             calls.append(ccall)
         steps.append(calls)
-    # greedy batches with between half as many rows as CUs and as many run
-    # one persistent workgroup per CU, the others one workgroup per row or
-    # half row (the library's launch rule)
-    cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
-    greedy = "verify_greedy_kernel" if 2 * wl.R >= cus and wl.R <= cus else "verify_greedy_rows_kernel"
-    kernels = [("verify_sampled_kernel" if wl.sampled else greedy, verify_bytes)]
+    kernels = [("verify_sampled_kernel" if wl.sampled else "verify_greedy_rows_kernel", verify_bytes)]
     if wl.D:
         kernels.append(("confidence_kernel", conf_bytes))
     return steps, kernels, ncopy, step_bytes

@@ -24,18 +24,16 @@ bool dtype_ok(int32_t dtype) { return dtype == VSV_F32 || dtype == VSV_BF16; }
 // only by vsv_test_withhold_row_word.
 std::atomic<int32_t> g_withheld_row{-1};
 
-// Persistent workgroups for greedy verification: one per CU of the current
-// device (cached per device), at most kMaxGroups; 0 if the count is unknown.
-int persistent_groups() {
+// CUs of the current device (cached per device); 0 if the count is unknown.
+int device_cus() {
   static int cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
   if (dev < 64 && cached[dev] > 0) return cached[dev];
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
-  const int g = cus < vsv::kMaxGroups ? cus : vsv::kMaxGroups;
-  if (dev < 64) cached[dev] = g;
-  return g;
+  if (dev < 64) cached[dev] = cus;
+  return cus;
 }
 
 // Common checks of a batch and its outputs; fills the shared launch args.
@@ -90,7 +88,7 @@ vsv_status prepare(const vsv_batch* b, const vsv_outputs* o, void* ws, size_t ws
   v.ws_perm = sampled ? reinterpret_cast<int32_t*>(w + vsv::kWsAlign + vsv::ws_row_bytes(b->num_rows) +
                                                    vsv::ws_part_bytes(b->num_rows))
                       : nullptr;
-  v.groups = persistent_groups();
+  v.cus = device_cus();
   return VSV_OK;
 }
 

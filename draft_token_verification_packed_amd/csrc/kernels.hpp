@@ -15,9 +15,6 @@ namespace vsv {
 #ifndef VSV_VERIFY_THREADS
 #define VSV_VERIFY_THREADS 512
 #endif
-#ifndef VSV_GREEDY_THREADS
-#define VSV_GREEDY_THREADS 1024
-#endif
 #ifndef VSV_ROW_THREADS
 #define VSV_ROW_THREADS 256
 #endif
@@ -34,7 +31,6 @@ namespace vsv {
 #define VSV_UNROLL_ROWS 2
 #endif
 constexpr int kVerifyThreads = VSV_VERIFY_THREADS;
-constexpr int kGreedyThreads = VSV_GREEDY_THREADS;
 constexpr int kRowThreads = VSV_ROW_THREADS;
 constexpr int kConfThreads = VSV_CONF_THREADS;     // draft-confidence rows
 constexpr int kOrderThreads = VSV_ORDER_THREADS;   // sampled row order
@@ -76,9 +72,8 @@ struct VerifyArgs {
   const int32_t* generated;
   const int32_t* prot;
   int32_t nprot;
-  int32_t groups;       // greedy: persistent workgroups (one per CU)
-  int32_t cpr;          // greedy: chunks per row (set at launch)
-  int32_t parts;        // greedy, one workgroup per row part: 1 or 2 parts per row
+  int32_t cus;          // CUs of the device (0 if unknown)
+  int32_t parts;        // greedy: workgroups per row (set at launch)
   // sampled only
   const float* temperature;
   const int32_t* top_k;
@@ -107,9 +102,9 @@ struct VerifyArgs {
   //           call resets both to 0
   //  ws_row   [R] 64-bit words; a row handled by one workgroup stores the
   //           token it emits | kAcceptBit if its draft was accepted
-  //  ws_part  [kPartWords][R + kMaxGroups] 64-bit words, field-major; slot
-  //           r + p holds the partial statistics persistent workgroup p
-  //           gathered for row r
+  //  ws_part  [part_slot_count(R)][kPartWords] 64-bit words; with P parts
+  //           per row, slot r * (P - 1) + p holds the statistics part p of
+  //           row r gathered (p < P - 1)
   //  ws_perm  [R] (sampled launches) the order in which the row queue hands
   //           out rows, written by the ordering kernel before the launch
   uint32_t* ws_epoch;
@@ -130,21 +125,17 @@ struct ConfidenceArgs {
   int32_t* error_flag;
 };
 
-// Greedy verification of a batch with between half as many rows as CUs and
-// as many runs one persistent workgroup per CU (at most kMaxGroups): the
-// batch's rows are cut into chunks of 64 * kUnroll 16-byte vectors, each
-// workgroup takes an equal contiguous range of the chunk list and its waves
-// pull chunks from it one at a time, so every CU streams the same number of
-// bytes however few the rows. Other batches use one kRowThreads workgroup
-// per row (or per half row): each row then streams at the same share of the
-// memory system and no row's statistics cross more than two workgroups.
-// Timed on EAGLE-shaped bf16 batches on MI355X (256 CUs), the persistent
-// kernel won only from about 128 to 256 rows; below, its fixed cost of 256
-// large workgroups and the merge across them dominates (20 rows: 20.7 us
-// against 14.1), and above, the row kernel wins up to 3000 rows.
-constexpr int kMaxGroups = 1024;
-// Row kernel: parts per row (one per about kPartBytes of logits, at most
-// kMaxRowParts), and the partial slots the workspace holds for them.
+// Greedy verification runs one workgroup per row part. Rows of more than
+// about 1.5 kPartBytes are cut into parts of about kPartBytes, so no
+// workgroup streams a whole fp32 row alone; a batch too small to give every
+// CU a few workgroups cuts its rows further, into enough parts for about
+// kPartsPerCU / 2 workgroups per CU (parts of at least kMinPartBytes). Timed
+// on EAGLE-shaped bf16 batches (V=152064) on MI355X (256 CUs): 20 rows take
+// 8.6 us in 16 parts each against 14.6 in two, 160 rows 15.4 us in four
+// parts against 19.8 for one workgroup per CU streaming an equal share of
+// the batch, and from about 320 rows on two parts per row is the rule's own
+// choice.
+// Parts per row: one per about kPartBytes of logits, at most kMaxRowParts.
 #ifndef VSV_PART_BYTES
 #define VSV_PART_BYTES 152064
 #endif
@@ -152,12 +143,25 @@ constexpr int kMaxGroups = 1024;
 #define VSV_FORCE_PARTS 0
 #endif
 constexpr int64_t kPartBytes = VSV_PART_BYTES;
+// Small batches: parts per row aim at kPartsPerCU / 2 workgroups per CU in
+// all, with parts of at least kMinPartBytes.
+#ifndef VSV_PARTS_PER_CU
+#define VSV_PARTS_PER_CU 5
+#endif
+constexpr int kPartsPerCU = VSV_PARTS_PER_CU;
+constexpr int64_t kMinPartBytes = 16384;
 constexpr int kMaxRowParts = 16;
+// Partial slots (kPartWords words each: max, its index, exponent reference,
+// the float64 sum as two halves, rank count) the workspace holds for the
+// parts of a batch of R rows: max(R + kSpareSlots, kPartSlots), so a batch
+// of any size can cut its rows in two.
 constexpr int kPartSlots = 8192;
-constexpr int kMaxLocalRows = 32;
-constexpr int kPartWords = 6;   // best, index, exponent ref, sum, rank, row info
-inline bool greedy_persistent(int32_t R, int32_t groups) {
-  return groups > 0 && 2 * static_cast<int64_t>(R) >= groups && R <= groups;
+constexpr int kSpareSlots = 1024;
+constexpr int kPartWords = 6;
+constexpr size_t part_slot_count(int32_t R) {
+  return static_cast<size_t>(R > 0 ? R : 0) + kSpareSlots > static_cast<size_t>(kPartSlots)
+             ? static_cast<size_t>(R > 0 ? R : 0) + kSpareSlots
+             : static_cast<size_t>(kPartSlots);
 }
 
 // Workspace layout (bytes, 256-aligned pieces). The first piece holds the
@@ -169,14 +173,8 @@ constexpr int kQueueDone = 16;
 constexpr int kQueueWords = 17;
 constexpr size_t ws_align(size_t b) { return (b + kWsAlign - 1) / kWsAlign * kWsAlign; }
 constexpr size_t ws_row_bytes(int32_t R) { return ws_align(static_cast<size_t>(R > 0 ? R : 1) * 8); }
-// The partials area serves the persistent kernel (kPartWords per (row,
-// workgroup) slot, R + kMaxGroups slots) and the row kernel (6 words for
-// each part but a row's last, at most max(R + kMaxGroups, kPartSlots)).
-constexpr size_t ws_part_bytes(int32_t R) {
-  return ws_align(((static_cast<size_t>(R > 0 ? R : 0) + kMaxGroups) > static_cast<size_t>(kPartSlots)
-                       ? (static_cast<size_t>(R > 0 ? R : 0) + kMaxGroups)
-                       : static_cast<size_t>(kPartSlots)) * kPartWords * 8);
-}
+// The partials area: one slot for each part but a row's last.
+constexpr size_t ws_part_bytes(int32_t R) { return ws_align(part_slot_count(R) * kPartWords * 8); }
 constexpr size_t ws_bytes(int32_t B, int32_t R, int32_t sampled) {
   (void)B;
   return kWsAlign + ws_row_bytes(R) + ws_part_bytes(R) + (sampled ? ws_align(static_cast<size_t>(R > 0 ? R : 1) * 4) : 0);

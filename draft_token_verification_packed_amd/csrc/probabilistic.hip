@@ -767,7 +767,7 @@ static hipError_t launch_probabilistic_t(VerifyArgs a, const ProbArgs& p, hipStr
   if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
     if (cached[dev] <= 0)
       cached[dev] = resident_groups(verify_probabilistic_kernel<E, kVerifyThreads, SampledDepth<E>::kGreedy>,
-                                    kVerifyThreads, a.groups);
+                                    kVerifyThreads, a.cus);
     grid = cached[dev];
   }
   if (grid <= 0) grid = 256;

@@ -111,7 +111,7 @@ static int sampled_resident(int cus) {
 
 template <typename E>
 static hipError_t launch_sampled_t(const VerifyArgs& a, hipStream_t s) {
-  int grid = sampled_resident<E>(a.groups);
+  int grid = sampled_resident<E>(a.cus);
   if (grid <= 0) grid = 256;
   if (grid > a.R) grid = a.R;
   // Longest rows first only where the batch has at most two rows per

@@ -75,7 +75,7 @@ __device__ __forceinline__ void part_range(const E* row, int V, int P, int part,
 // parts 0 .. P - 2 of row r at slots r * (P - 1) + p, kPartStatWords words
 // per slot): max, its lowest index, exponent reference, the float64 sum as
 // two halves, rank count.
-constexpr int kPartStatWords = 6;
+constexpr int kPartStatWords = kPartWords;
 __device__ __forceinline__ uint64_t* part_slots(const VerifyArgs& a, int r, int P) {
   return a.ws_part + static_cast<size_t>(r) * (P - 1) * kPartStatWords;
 }

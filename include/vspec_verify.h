@@ -362,14 +362,13 @@ const char* vsv_status_string(vsv_status status);
 
 /* Test hook for the batch scan's bounded wait (VSV_FLAG_STALLED), which a
  * dedicated GPU never reaches. Until called again with -1, every later
- * verify launch that gives each row its own workgroup (the row kernels of
- * vsv_verify_greedy, _relaxed and _static, vsv_verify_sampled and
- * vsv_verify_probabilistic; not the persistent greedy kernel, whose own
- * tail computes every word) computes row `row` as usual but leaves its
- * result word unpublished. The launch's scan then spends its poll budget
- * on that word (well under a second), sets VSV_FLAG_STALLED, uses the stale
- * word and completes: outputs stay inside their buffers and the workspace
- * serves the next call as usual. Process-wide; read when a call is made.
+ * verify launch (vsv_verify_greedy, _relaxed and _static,
+ * vsv_verify_sampled and vsv_verify_probabilistic) computes row `row` as
+ * usual but leaves its result word unpublished. The launch's scan then
+ * spends its poll budget on that word (well under a second), sets
+ * VSV_FLAG_STALLED, uses the stale word and completes: outputs stay inside
+ * their buffers and the workspace serves the next call as usual.
+ * Process-wide; read when a call is made.
  * Returns VSV_EINVAL for row < -1. */
 vsv_status vsv_test_withhold_row_word(int32_t row);
 

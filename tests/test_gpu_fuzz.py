@@ -3,8 +3,8 @@ and a run-twice bit comparison of the sampled path (a race smoke test).
 
 Each case draws the batch size, ragged draft counts, vocabulary size,
 element type, row alignment and per-request parameters from its seed, so
-the launch rules (persistent or one workgroup per row or half row; ordered
-or plain sampled queue) and the filters all get exercised on shapes nobody
+the launch rules (a row whole or cut into parts; ordered or plain sampled
+queue) and the filters all get exercised on shapes nobody
 picked by hand."""
 import numpy as np
 import pytest

@@ -36,9 +36,9 @@ def test_tiny_greedy_closed_form(vsv):
     assert_same(out, oracle_of(wl))
 
 
-# 16 and 128 requests (80, 640 rows) run one workgroup per row or half row,
-# 32 (160 rows) the persistent kernel
-@pytest.mark.parametrize("B", [16, 32, 128])
+# 4, 16, 32 and 128 requests (20, 80, 160, 640 rows) cut each row into 16,
+# 8, 4 and 2 parts
+@pytest.mark.parametrize("B", [4, 16, 32, 128])
 def test_eagle_greedy_k4(vsv, B):
     wl = synth.make("eagle", B=B)
     assert_same(run_greedy(vsv, wl), oracle_of(wl))
@@ -201,9 +201,9 @@ def test_confidence_edge_rows(vsv):
 def test_max_tied_between_head_and_body(vsv, dtype, B):
     """Rows misaligned by one element start with elements outside the 16-byte
     body; the row maximum is planted in one of them and again deep in the
-    body, so the lowest index is a head element. 6, 60 and 300 requests take
-    the row kernel with halves, the persistent kernel and the row kernel;
-    the sampled entry point with T = 0 streams the same rows as greedy rows."""
+    body, so the lowest index is a head element. 6, 60 and 300 requests cut
+    the rows into halves, keep them whole and (bf16) halve them again; the
+    sampled entry point with T = 0 streams the same rows as greedy rows."""
     import torch
     rng = np.random.default_rng(600 + B + dtype)
     V = 5000
@@ -224,3 +224,56 @@ def test_max_tied_between_head_and_body(vsv, dtype, B):
                            device="cuda"), torch.ones(B, device="cuda"), z, 1, vocab=V)
     torch.cuda.synchronize()
     assert_same(s, ref)
+
+
+@pytest.mark.parametrize("dtype", [oracle.F32, oracle.BF16])
+@pytest.mark.parametrize("B", [1, 3, 24])
+def test_many_parts_ties_across_parts(vsv, dtype, B):
+    """Small batches over a 152064-token vocabulary cut each row into up to
+    16 parts; rows are misaligned by one element, so each has head and tail
+    elements outside its 16-byte body. The row maximum is planted by rows in
+    turn: twice in distant parts (the lower index must win the merge), once
+    at the very last element (a tail element), at the first and the last
+    element, and as a run of 81 equal values across the middle part boundary
+    for every even part count. Drafts alternate, from one round of the four
+    plantings to the next, between the lowest tied index and the highest (a
+    tie that is not the greedy token is rejected)."""
+    import torch
+    rng = np.random.default_rng(7700 + B + dtype)
+    V, shift = 152064, 1
+    store, off, owner, _ = _custom_quick(rng, B, 6, V, dtype, ld=V + 3, shift=shift)
+    R = int(off[-1])
+    top = synth.f32_to_bf16_bits(np.array([40.0], dtype=np.float32))[0] if dtype == oracle.BF16 else np.float32(40.0)
+    mid = V // 2
+    plants = [[V // 3, 2 * V // 3], [V - 1], [0, V - 1], list(range(mid - 40, mid + 41))]
+    chosen = []
+    for r in range(R):
+        idx = plants[r % len(plants)]
+        store[r, shift + np.array(idx)] = top
+        chosen.append(idx)
+    drafts = np.empty(R - B, dtype=np.int32)
+    for i in range(B):
+        for j in range(int(off[i + 1] - off[i]) - 1):
+            r = int(off[i]) + j
+            idx = chosen[r]
+            drafts[r - i] = idx[0] if (r // len(plants)) % 2 == 0 else idx[-1]
+    print("many parts B=%d R=%d dtype=%d" % (B, R, dtype), flush=True)
+    t = to_dev(store)[:, shift:]
+    out = vsv.verify_greedy(t, to_dev(off), to_dev(owner), to_dev(drafts), vocab=V)
+    torch.cuda.synchronize()
+    ref = oracle.verify_greedy(store[:, shift:], dtype, V, off, owner, drafts)
+    assert ref["row_token"].tolist() == [c[0] for c in chosen]
+    assert_same(out, ref)
+
+
+def _custom_quick(rng, B, Kmax, V, dtype, ld, shift):
+    """A ragged batch of normal(0, 3) logits (drafts left to the caller)."""
+    Ks = rng.integers(0, Kmax + 1, size=B)
+    off = np.zeros(B + 1, dtype=np.int32)
+    off[1:] = np.cumsum(Ks + 1)
+    R = int(off[-1])
+    owner = np.repeat(np.arange(B, dtype=np.int32), Ks + 1)
+    full = np.zeros((R, ld + shift), dtype=np.float32)
+    full[:, shift:shift + V] = (rng.standard_normal((R, V)) * 3).astype(np.float32)
+    store = synth.f32_to_bf16_bits(full) if dtype == oracle.BF16 else full
+    return store, off, owner, None

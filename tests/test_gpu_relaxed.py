@@ -87,8 +87,8 @@ def test_relaxed_variants_full_c4_shape(vsv, case):
 def test_relaxed_margin_ties_and_shapes(vsv, B):
     """Integer-valued fp32 rows (many ties, and gaps equal to the margin
     exactly, which must be rejected on both sides), misaligned rows, drafts
-    near the top; 40 requests fall in the range the persistent kernel takes
-    for plain greedy verification."""
+    near the top; 6 and 300 requests cut each row in two, 40 keep rows
+    whole."""
     rng = np.random.default_rng(9100 + B)
     V, ld, shift = 3001, 3010, 1
     Ks = rng.integers(0, 6, size=B)

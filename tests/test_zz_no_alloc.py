@@ -40,8 +40,8 @@ def _both(vsv, wl, relaxed=1):
 
 
 def test_static_scratch_two_calls(vsv):
-    # first call: 200 rows, the persistent kernel (per-(row, workgroup)
-    # partials in the scratch); second: 20 rows, one workgroup per half row
+    # first call: 200 rows in three parts each (the parts' statistics in
+    # the scratch); second: 20 rows, one workgroup per half row
     wl = synth.make("eagle", B=40)
     assert_same(_both(vsv, wl), oracle_of(wl))
     small = synth.make("tiny")
