@@ -85,9 +85,6 @@ vsv_status prepare(const vsv_batch* b, const vsv_outputs* o, void* ws, size_t ws
   v.ws_queue = reinterpret_cast<uint32_t*>(w + 64);
   v.ws_row = reinterpret_cast<uint64_t*>(w + vsv::kWsAlign);
   v.ws_part = reinterpret_cast<uint64_t*>(w + vsv::kWsAlign + vsv::ws_row_bytes(b->num_rows));
-  v.ws_perm = sampled ? reinterpret_cast<int32_t*>(w + vsv::kWsAlign + vsv::ws_row_bytes(b->num_rows) +
-                                                   vsv::ws_part_bytes(b->num_rows))
-                      : nullptr;
   v.cus = device_cus();
   return VSV_OK;
 }

@@ -21,9 +21,6 @@ namespace vsv {
 #ifndef VSV_CONF_THREADS
 #define VSV_CONF_THREADS 512
 #endif
-#ifndef VSV_ORDER_THREADS
-#define VSV_ORDER_THREADS 128
-#endif
 #ifndef VSV_UNROLL
 #define VSV_UNROLL 2
 #endif
@@ -33,7 +30,6 @@ namespace vsv {
 constexpr int kVerifyThreads = VSV_VERIFY_THREADS;
 constexpr int kRowThreads = VSV_ROW_THREADS;
 constexpr int kConfThreads = VSV_CONF_THREADS;     // draft-confidence rows
-constexpr int kOrderThreads = VSV_ORDER_THREADS;   // sampled row order
 constexpr int kUnroll = VSV_UNROLL;
 constexpr int kUnrollRows = VSV_UNROLL_ROWS;
 
@@ -54,6 +50,11 @@ template <> struct SampledDepth<float> {
 template <> struct SampledDepth<uint16_t> {
   static constexpr int kPass1 = 3, kGreedy = 2;
 };
+// Sampled launches hand out the sampled requests' rows first where a batch
+// has more rows than CUs but at most two per workgroup; each workgroup keeps
+// the rows of the tickets past the grid in LDS (16-bit row numbers), at
+// most kLateRows of them.
+constexpr int kLateRows = 1024;
 
 // Everything a verify launch needs, passed by value as the kernel argument.
 struct VerifyArgs {
@@ -105,14 +106,13 @@ struct VerifyArgs {
   //  ws_part  [part_slot_count(R)][kPartWords] 64-bit words; with P parts
   //           per row, slot r * (P - 1) + p holds the statistics part p of
   //           row r gathered (p < P - 1)
-  //  ws_perm  [R] (sampled launches) the order in which the row queue hands
-  //           out rows, written by the ordering kernel before the launch
   uint32_t* ws_epoch;
   uint32_t* ws_queue;
   uint64_t* ws_row;
   uint64_t* ws_part;
-  int32_t* ws_perm;
-  int32_t ordered;      // sampled: the queue hands out rows in ws_perm order
+  // sampled: the queue hands out the sampled requests' rows first (each
+  // workgroup derives the order at its start, row_queue.hpp)
+  int32_t ordered;
 };
 
 struct ConfidenceArgs {
@@ -175,9 +175,11 @@ constexpr size_t ws_align(size_t b) { return (b + kWsAlign - 1) / kWsAlign * kWs
 constexpr size_t ws_row_bytes(int32_t R) { return ws_align(static_cast<size_t>(R > 0 ? R : 1) * 8); }
 // The partials area: one slot for each part but a row's last.
 constexpr size_t ws_part_bytes(int32_t R) { return ws_align(part_slot_count(R) * kPartWords * 8); }
+// Greedy and sampled calls need the same workspace.
 constexpr size_t ws_bytes(int32_t B, int32_t R, int32_t sampled) {
   (void)B;
-  return kWsAlign + ws_row_bytes(R) + ws_part_bytes(R) + (sampled ? ws_align(static_cast<size_t>(R > 0 ? R : 1) * 4) : 0);
+  (void)sampled;
+  return kWsAlign + ws_row_bytes(R) + ws_part_bytes(R);
 }
 // Tokens travel in the low 30 bits of a row word.
 constexpr int32_t kMaxVocab = 0x3FFFFFFF;

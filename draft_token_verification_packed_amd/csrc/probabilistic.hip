@@ -757,7 +757,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void ve
     VerifyArgs a, ProbArgs pa) {
   __shared__ SampledLds<NT> L;
   const uint32_t tag = call_tag(a);
-  row_queue_loop<NT>(a, tag, L, [&](int r, auto hook) { prob_kernel_row<E, NT, U>(a, pa, tag, r, L, hook); });
+  row_queue_loop<NT, false>(a, tag, L, [&](int r, auto hook) { prob_kernel_row<E, NT, U>(a, pa, tag, r, L, hook); });
 }
 
 template <typename E>

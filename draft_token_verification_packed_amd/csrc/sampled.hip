@@ -52,48 +52,12 @@ __device__ __forceinline__ void sampled_kernel_row(const VerifyArgs& a, uint32_t
   }
 }
 
-// The order in which the queue hands out rows. A sampled row costs several
-// times a greedy one, and when a batch has few rows per workgroup slot the
-// rows handed out last decide when the launch ends. So the sampled
-// requests' rows go first and the greedy rows last (longest first), each
-// group in request order. One workgroup writes the order into the
-// workspace before the verification launch. A layout it cannot trust
-// (offsets not 0 = off[0] < off[1] < ... < off[B] = R) keeps the plain row
-// order; the verification launch flags such a layout as before.
-template <int NT>
-__global__ __launch_bounds__(NT) void sampled_order_kernel(VerifyArgs a) {
-  __shared__ int scan[NT / kWave];
-  const int t = threadIdx.x;
-  const int per = (a.B + NT - 1) / NT;
-  const int i0 = min(a.B, t * per), i1 = min(a.B, i0 + per);
-  int ns = 0, ng = 0, bad = 0;
-  for (int i = i0; i < i1; ++i) {
-    const int r0 = a.offsets[i], r1 = a.offsets[i + 1];
-    bad |= !(r0 >= 0 && r1 > r0 && r1 <= a.R) || (i == 0 && r0 != 0) || (i == a.B - 1 && r1 != a.R);
-    const int n = bad ? 0 : r1 - r0;
-    if (a.temperature[i] > 0.f) ns += n; else ng += n;
-  }
-  int ns_total, ng_total;
-  const int s_before = block_exclusive_scan<NT>(ns, scan, ns_total);
-  const int g_before = block_exclusive_scan<NT>(ng, scan, ng_total);
-  if (__syncthreads_or(bad) || ns_total + ng_total != a.R) {
-    for (int q = t; q < a.R; q += NT) a.ws_perm[q] = q;
-    return;
-  }
-  int ps = s_before, pg = ns_total + g_before;
-  for (int i = i0; i < i1; ++i) {
-    const int r0 = a.offsets[i], r1 = a.offsets[i + 1];
-    int& pos = a.temperature[i] > 0.f ? ps : pg;
-    for (int r = r0; r < r1; ++r) a.ws_perm[pos++] = r;
-  }
-}
-
 template <typename E, int NT, int U>
 // two workgroups per CU (4 waves per SIMD): at most 128 VGPRs
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void verify_sampled_kernel(VerifyArgs a) {
   __shared__ SampledLds<NT> L;
   const uint32_t tag = call_tag(a);
-  row_queue_loop<NT>(a, tag, L, [&](int r, auto hook) { sampled_kernel_row<E, NT, U>(a, tag, r, L, hook); });
+  row_queue_loop<NT, true>(a, tag, L, [&](int r, auto hook) { sampled_kernel_row<E, NT, U>(a, tag, r, L, hook); });
 }
 
 // Workgroups of the sampled kernel that fit on the current device at once
@@ -114,16 +78,14 @@ static hipError_t launch_sampled_t(const VerifyArgs& a, hipStream_t s) {
   int grid = sampled_resident<E>(a.cus);
   if (grid <= 0) grid = 256;
   if (grid > a.R) grid = a.R;
-  // Longest rows first only where the batch has at most two rows per
-  // workgroup slot: with more, the rows handed out last are a small part of
-  // the launch, and the order's lookup would add a load to every row.
+  // A sampled row costs several times a greedy one. Where the batch has more
+  // rows than CUs but at most two rows per workgroup, the sampled requests'
+  // rows go first (row_queue.hpp): CUs then pair a sampled row with a greedy
+  // one, and the rows handed out last are greedy. With more rows, those
+  // handed out last are a small part of the launch; with at most one row
+  // per CU, no CU holds two rows.
   VerifyArgs b = a;
-  b.ordered = (a.ws_perm && a.R <= 2 * grid) ? 1 : 0;
-  if (b.ordered) {
-    sampled_order_kernel<kOrderThreads><<<dim3(1), dim3(kOrderThreads), 0, s>>>(b);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  b.ordered = (a.R > a.cus && a.R <= 2 * grid && a.R - grid <= kLateRows && a.R <= 0x7FFF) ? 1 : 0;
   verify_sampled_kernel<E, kVerifyThreads, SampledDepth<E>::kGreedy><<<dim3(grid), dim3(kVerifyThreads), 0, s>>>(b);
   return hipGetLastError();
 }

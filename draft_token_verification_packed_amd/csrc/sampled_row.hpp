@@ -99,6 +99,7 @@ template <int NT> struct SampledLds {
   int row_next;  // the workgroup's next row (row queue)
   int ticket;    // its ticket (position in the queue)
   int last;      // this workgroup finished the call's last row
+  uint16_t late[kLateRows];  // ordered queue: rows of the tickets past the grid
 };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }

@@ -100,8 +100,8 @@ typedef struct {
 /* Bytes of device workspace a verify call needs (B requests, R rows): the
  * words through which rows and workgroups hand their results to the
  * batch-wide scan, a call counter, and the row queue of sampled and
- * probabilistic verification (with sampled != 0, also the order in which
- * the sampled kernel's queue hands out rows). The workspace
+ * probabilistic verification. `sampled` is accepted for compatibility; the
+ * size is the same for every entry point. The workspace
  * must be zero-filled before its first use (vsv_workspace_init or any
  * zeroed allocation); after that every call leaves it ready for the next
  * one, so one workspace serves any later call on the same stream. Two calls

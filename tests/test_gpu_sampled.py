@@ -139,24 +139,30 @@ def test_large_mixed_draft_confidence(vsv):
     np.testing.assert_allclose(host(conf), rc, rtol=1e-5, atol=0)
 
 
-def test_many_requests_in_longest_first_order(vsv):
-    """A batch with at most two rows per workgroup slot goes out longest
-    first (sampled requests' rows, then greedy ones); here with more requests
-    than the ordering workgroup has threads, and a third of them greedy."""
-    rng = np.random.default_rng(4242)
+@pytest.mark.parametrize("B,Kmax", [(300, 2), (600, 1)])
+def test_many_requests_in_longest_first_order(vsv, B, Kmax):
+    """A batch with more rows than CUs and at most two rows per workgroup
+    slot goes out in the ordered queue (sampled requests' rows, then greedy
+    ones), whose order each workgroup derives at its start: 300 requests
+    give its 512 threads one request each, 600 give them two; a third of the
+    requests are greedy."""
+    rng = np.random.default_rng(4242 + B)
     params = lambda i: [(0.0, 0, 1.0, 0.0), (0.8, 40, 0.9, 0.0), (1.0, 0, 0.95, 0.05)][i % 3]
-    b = custom_sampled(rng, 300, 2, 4099, oracle.BF16, params, seed=17, offset=3)
-    assert int(b["offsets"][-1]) <= 1024
+    b = custom_sampled(rng, B, Kmax, 4099, oracle.BF16, params, seed=17, offset=3)
+    assert 256 < int(b["offsets"][-1]) <= 1024
     out = run_custom(vsv, b)
     assert_same(out, oracle_custom(b))
     assert int(host(out["error_flag"])[0]) == 0
 
 
-def test_layout_errors_are_flagged(vsv):
+@pytest.mark.parametrize("B", [12, 80])
+def test_layout_errors_are_flagged(vsv, B):
     """Inconsistent owner maps and offsets set the layout flag; the launch
-    (with its row-order pass) still completes and writes inside the buffers."""
+    still completes and writes inside the buffers. 80 requests (351 rows)
+    take the ordered queue, whose order falls back to the plain row order
+    for offsets that do not rise."""
     import torch
-    wl = synth.make("ragged", B=12, V=1000)
+    wl = synth.make("ragged", B=B, V=1000)
     d = upload(wl)
     own = d["owner"].clone()
     own[3] = (own[3] + 1) % wl.B
