@@ -550,13 +550,14 @@ template <typename E, int NT, int U, typename Hook>
 __device__ __forceinline__ void prob_kernel_row(const VerifyArgs& a, const ProbArgs& pa, uint32_t tag, int r,
                                                 SampledLds<NT>& L, Hook after_stream) {
   const E* __restrict__ row = static_cast<const E*>(a.logits) + static_cast<int64_t>(r) * a.ld;
-  const RowMeta m = load_meta(a, r, a.owner[r]);
-  const int req = m.req < 0 ? 0 : m.req;
-  const float T = a.temperature[req];
-  const float Tq = pa.draft_temperature[req];
-  int top_k = a.top_k[req];
-  float top_p = a.top_p[req];
-  float min_p = a.min_p[req];
+  const int own = a.owner[r];
+  const ReqParams q = load_params(a, own);
+  const float Tq = pa.draft_temperature[(own >= 0 && own < a.B) ? own : 0];
+  const RowMeta m = load_meta(a, r, own);
+  const float T = q.T;
+  int top_k = q.top_k;
+  float top_p = q.top_p;
+  float min_p = q.min_p;
   int bits = 0;
   if (m.req >= 0) {
     if (!(T >= 0.f && T < INFINITY) || !(Tq >= 0.f && Tq < INFINITY)) bits |= VSV_FLAG_PARAMS;

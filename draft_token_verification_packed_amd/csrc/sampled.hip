@@ -17,12 +17,27 @@ template <typename E, int NT, int U, typename Hook>
 __device__ __forceinline__ void sampled_kernel_row(const VerifyArgs& a, uint32_t tag, int r, SampledLds<NT>& L,
                                                    Hook after_stream) {
   const E* __restrict__ row = static_cast<const E*>(a.logits) + static_cast<int64_t>(r) * a.ld;
-  const RowMeta m = load_meta(a, r, a.owner[r]);
-  const float T = a.temperature[m.req < 0 ? 0 : m.req];
+  const int own = a.owner[r];
+  // The request's parameters go out with the row's metadata: all of them
+  // for fp32 rows, the temperature alone for bf16 rows, whose filter
+  // parameters are loaded once the row is known to be sampled (timed on the
+  // ragged fp32 and large mixed bf16 batches, each choice was the faster
+  // for its element type).
+  constexpr bool kAll = sizeof(E) == 4;
+  ReqParams q{};
+  if constexpr (kAll) q = load_params(a, own);
+  else q.T = a.temperature[(own >= 0 && own < a.B) ? own : 0];
+  const RowMeta m = load_meta(a, r, own);
+  const float T = q.T;
   int token = 0, bits = 0, slow = 0;
   double lse = 0.0;
   if (m.req >= 0 && T > 0.f) {
-    const SampledOut o = sampled_row<E, NT, SampledDepth<E>::kPass1>(a, row, m.req, m.j, T, L, after_stream);
+    if constexpr (!kAll) {
+      q.top_k = a.top_k[m.req];
+      q.top_p = a.top_p[m.req];
+      q.min_p = a.min_p[m.req];
+    }
+    const SampledOut o = sampled_row<E, NT, SampledDepth<E>::kPass1>(a, row, m.req, m.j, q, L, after_stream);
     token = o.token;
     lse = o.lse;
     bits = o.bits;

@@ -1212,16 +1212,17 @@ struct SampledOut {
   int slow;   // 1 if the exact whole-row path decided
 };
 
-// One workgroup samples row `row` of request `req` (local row j) at
-// temperature T > 0. `after_stream(true)` runs once the row has been read
-// (true: a long tail of work follows).
+// One workgroup samples row `row` of request `req` (local row j) with the
+// request's parameters q (temperature q.T > 0). `after_stream(true)` runs
+// once the row has been read (true: a long tail of work follows).
 template <typename E, int NT, int U, typename Hook>
-__device__ __forceinline__ SampledOut sampled_row(const VerifyArgs& a, const E* __restrict__ row, int req, int j, float T,
-                                  SampledLds<NT>& L, Hook after_stream) {
+__device__ __forceinline__ SampledOut sampled_row(const VerifyArgs& a, const E* __restrict__ row, int req, int j,
+                                                  const ReqParams& q, SampledLds<NT>& L, Hook after_stream) {
   SampledOut out{0, 0.0, 0, 0};
-  int top_k = a.top_k[req];
-  float top_p = a.top_p[req];
-  float min_p = a.min_p[req];
+  const float T = q.T;
+  int top_k = q.top_k;
+  float top_p = q.top_p;
+  float min_p = q.min_p;
   if (!(top_p > 0.f && top_p <= 1.f) || !(min_p >= 0.f && min_p <= 1.f) || !(T < INFINITY)) {
     out.bits |= VSV_FLAG_PARAMS;
     if (!(top_p > 0.f && top_p <= 1.f)) top_p = 1.f;

@@ -149,6 +149,21 @@ __device__ __forceinline__ RowMeta load_meta(const VerifyArgs& a, int r, int i) 
   return m;
 }
 
+// A row's request parameters, loaded at the owner entry's request (request
+// 0 if the entry is out of range) together with the row's metadata: both
+// depend only on the owner entry, so the loads go out in one round trip.
+// They are the request's own wherever the metadata confirms the owner
+// (m.req >= 0, and then m.req == owner).
+struct ReqParams {
+  float T;
+  int top_k;
+  float top_p, min_p;
+};
+__device__ __forceinline__ ReqParams load_params(const VerifyArgs& a, int owner) {
+  const int i = (owner >= 0 && owner < a.B) ? owner : 0;
+  return ReqParams{a.temperature[i], a.top_k[i], a.top_p[i], a.min_p[i]};
+}
+
 __device__ __forceinline__ void set_flag(const VerifyArgs& a, int bits) {
   if (a.error_flag) atomicOr(a.error_flag, bits);
 }
