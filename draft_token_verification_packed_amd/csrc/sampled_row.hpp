@@ -35,6 +35,7 @@
 
 #include "kernels.hpp"
 #include "row_stream.hpp"
+#include "verify_common.hpp"
 
 namespace vsv {
 
@@ -44,6 +45,7 @@ constexpr int kCapVec = 3072;   // most vectors a window capture reads again (ab
 constexpr int kTopBins = 1024;  // top-k threshold: codes within this many of the maximum's
 constexpr int kNB = 1024;       // histogram bins over the candidates
 constexpr int kGather = 256;    // most elements one bin may hold
+constexpr int kGatherFull = 512;  // the same for the whole-row locator
 constexpr float kZcap = 10.0f;  // capture window below the row maximum, in units of T
 
 struct Cand {
@@ -62,7 +64,8 @@ __device__ __forceinline__ uint32_t ord_ukey(float x) { return static_cast<uint3
 
 template <int NT> struct SampledLds {
   static constexpr int NW = NT / kWave;
-  static_assert(NT >= kGather && NT <= 1024 && kNB % NT == 0 && kTopBins % NT == 0, "one gathered element per thread");
+  static_assert(NT >= kGatherFull && kGatherFull >= kGather && NT <= 1024 && kNB % NT == 0 && kTopBins % NT == 0,
+                "one gathered element per thread");
   union {
     struct {
       alignas(16) uint16_t l1[kVM];  // pass 1: entry codes; pass 2: indices of the picked entries
@@ -73,10 +76,10 @@ template <int NT> struct SampledLds {
       double mass[kNB + 1];
       union {
         double wbin[kNB];     // bfloat16 rows: weight of each bin's value
-        double gpm[kGather];  // float32 rows: weight prefix of the gathered bin
+        double gpm[kGatherFull];  // float32 rows: weight prefix of the gathered bin
       };
-      Cand g[kGather];
-      Cand gs[kGather];
+      Cand g[kGatherFull];
+      Cand gs[kGatherFull];
     } post;
     struct {
       int cnt[256];
@@ -481,160 +484,433 @@ struct CandLocator {
   }
 };
 
-// Exact locator over the whole row: radix select on the order-preserving
-// key (four 8-bit digits, most significant first), then the tie of the
-// located value in index order. Reads the row several times; used only when
-// the candidates cannot decide.
+// Every element of a row, in 16-byte loads (its 16-byte-aligned body) and
+// single loads (the elements before and after it): f(x, index) runs once
+// per element, on some thread, in no particular order. Loads go out
+// kRowEachB at a time per thread (the whole-row passes below are paced by
+// their arithmetic, not by their loads).
+constexpr int kRowEachB = 2;
+template <typename E, int NT, typename F>
+__device__ __forceinline__ void row_each(const E* __restrict__ row, int V, F f) {
+  constexpr int N = Elem<E>::kVec;
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
+  int head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(E));
+  if (head > V) head = V;
+  const int nvec = (V - head) / N;
+  const int body_end = head + nvec * N;
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<E*>(row + head), 0, nvec * 16, 0x00020000);
+  for (int v0 = threadIdx.x; v0 < nvec; v0 += NT * kRowEachB) {
+    u32x4 w[kRowEachB];
+#pragma unroll
+    for (int b = 0; b < kRowEachB; ++b) {
+      const int q = v0 + b * NT;
+      w[b] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, q < nvec ? static_cast<uint32_t>(q) * 16u : 0xFFFFFFF0u, 0, 0);
+    }
+#pragma unroll
+    for (int b = 0; b < kRowEachB; ++b) {
+      const int q = v0 + b * NT;
+      if (q < nvec) {
+        float x[N];
+        Elem<E>::decode(w[b], x);
+#pragma unroll
+        for (int k = 0; k < N; ++k) f(x[k], head + q * N + k);
+      }
+    }
+  }
+  const int t = static_cast<int>(threadIdx.x);
+  if (t < head) f(Elem<E>::at(row, t), t);
+  if (body_end + t < V) f(Elem<E>::at(row, body_end + t), body_end + t);
+}
+
+// Float64 2^a by Tang's table-driven method (ACM TOMS 15(2), 1989):
+// a = n + j / 64 + r with integer n, 0 <= j < 64 and 0 <= r < 1/64, so
+// 2^a = 2^n * 2^(j/64) * 2^r, with 2^(j/64) from a 64-entry table and 2^r
+// from the Taylor series of e^(r ln 2) to degree 6 (the first omitted term
+// is under 4e-18 relative). Arguments below -1100 give 0.
+struct Exp2Table {
+  static constexpr double kL = 0.69314718055994530942;   // ln 2
+  static constexpr double k1 = kL, k2 = k1 * kL / 2, k3 = k2 * kL / 3, k4 = k3 * kL / 4, k5 = k4 * kL / 5,
+                          k6 = k5 * kL / 6;
+  double* t;
+  // every thread calls it; the caller's barrier publishes the table
+  __device__ void fill() const {
+    if (threadIdx.x < 64) t[threadIdx.x] = exp2(static_cast<double>(threadIdx.x) / 64.0);
+  }
+  __device__ double operator()(double a) const {
+    a = a > -1100.0 ? a : -1100.0;
+    const double s = floor(a * 64.0);
+    const int n = static_cast<int>(s);
+    const double r = a - s * (1.0 / 64.0);
+    const double p = 1.0 + r * (k1 + r * (k2 + r * (k3 + r * (k4 + r * (k5 + r * k6)))));
+    return ldexp(t[n & 63] * p, n >> 6);
+  }
+};
+
+// Exact locator over the whole row: a search of the rank order (value
+// desc, index asc) by count or by float64 mass, on the elements'
+// order-preserving keys. A level bins a key range (lo, hi] by (hi - k) >> s
+// into kNB bins, the last one taking everything further below. Level 0
+// starts at the row maximum's key with s = 16 (one bfloat16 value per bin)
+// and its counts and weights serve every query of the row. A query finds
+// the bin that holds its answer: a bin of at most kGatherFull elements is
+// gathered and ranked in LDS, a bin of one value resolves its ties in index
+// order, and any other bin is binned again, 2^10 times finer (the last bin:
+// the next kNB - 1 steps below). Each level reads the row once; most
+// elements of a row land in the last bin, so each lane sums that bin's
+// share itself and adds it once. Bins weigh their elements with the
+// table-driven float64 exponential below (a few units in the last place of
+// exp((x - m) / T)); ranked bins and ties use exp itself.
 template <typename E, int NT>
 struct FullLocator {
+  static constexpr int NW = NT / kWave;
+  static constexpr int kS0 = 16;
+  // finer levels' counts and weights live in the candidate area
+  static constexpr size_t kFineMass = ((kNB + 1) * sizeof(int) + 7) / 8 * 8;
+  static constexpr size_t kTable = kFineMass + (kNB + 1) * sizeof(double);
+  static_assert(sizeof(Cand) * kCand >= kTable + 64 * sizeof(double),
+                "finer levels and the table fit the candidate area");
   SampledLds<NT>& L;
   const E* __restrict__ row;
   int V;
   float m;
   double T;
   double wtot;
+  uint32_t kmax;
+  uint32_t kmin0;   // lowest key of the row
+  bool built;
 
-  __device__ FullLocator(SampledLds<NT>& l, const E* r, int V_, float m_, double T_)
-      : L(l), row(r), V(V_), m(m_), T(T_), wtot(0.0) {}
+  struct Level {
+    uint32_t hi, lo;  // keys in (lo, hi]; no lower bound unless has_lo
+    bool has_lo;
+    int s;
+    int base_c;       // elements ranked above the range
+    double base_m;    // and their weight
+  };
 
-  __device__ float at(int e) const { return Elem<E>::at(row, e); }
+  __device__ __forceinline__ FullLocator(SampledLds<NT>& l, const E* r, int V_, float m_, double T_)
+      : L(l), row(r), V(V_), m(m_), T(T_), wtot(0.0), kmax(ord_ukey(m_)), kmin0(0u), built(false) {}
 
-  __device__ double total_mass() {
-    double s = 0.0;
-    for (int e = threadIdx.x; e < V; e += NT) s += weight(at(e), m, T);
-    wtot = block_reduce<NT>(s, SumOp(), L.red_d);
+  __device__ __forceinline__ float at(int e) const { return Elem<E>::at(row, e); }
+  __device__ __forceinline__ int* cnt(bool fine) { return fine ? reinterpret_cast<int*>(&L.c) : L.u.post.cnt; }
+  __device__ __forceinline__ double* mass(bool fine) {
+    return fine ? reinterpret_cast<double*>(reinterpret_cast<char*>(&L.c) + kFineMass) : L.u.post.mass;
+  }
+  __device__ __forceinline__ static bool in_range(const Level& lv, uint32_t k) {
+    return k <= lv.hi && (!lv.has_lo || k > lv.lo);
+  }
+
+  // Counts and weights of the level's bins, as exclusive prefixes (totals
+  // at index kNB); returns the range's lowest key.
+  __device__ __forceinline__ uint32_t histogram(const Level& lv, bool fine) {
+    int* c = cnt(fine);
+    double* ms = mass(fine);
+    for (int b = threadIdx.x; b <= kNB; b += NT) {
+      c[b] = 0;
+      ms[b] = 0.0;
+    }
+    if (threadIdx.x == 0) L.bi[2] = -1;   // as unsigned: the largest key
+    lds_barrier();
+    const Exp2Table ex{reinterpret_cast<double*>(reinterpret_cast<char*>(&L.c) + kTable)};
+    ex.fill();
+    lds_barrier();
+    int oc = 0;
+    double om = 0.0;
+    uint32_t lowest = 0xFFFFFFFFu;
+    const double c2 = 1.4426950408889634074 / T;
+    row_each<E, NT>(row, V, [&](float x, int) {
+      const uint32_t k = ord_ukey(x);
+      if (!in_range(lv, k)) return;
+      lowest = k < lowest ? k : lowest;
+      const uint32_t d = (lv.hi - k) >> lv.s;
+      const double w = ex((static_cast<double>(x) - static_cast<double>(m)) * c2);
+      if (d < static_cast<uint32_t>(kNB - 1)) {
+        atomicAdd(&c[d], 1);
+        atomicAdd(&ms[d], w);
+      } else {
+        ++oc;
+        om += w;
+      }
+    });
+    oc = wave_all(oc, SumOp());
+    om = wave_sum_f64(om);
+    lowest = wave_all(lowest, MinOp());
+    if (lane_id() == 0) {
+      if (oc) {
+        atomicAdd(&c[kNB - 1], oc);
+        atomicAdd(&ms[kNB - 1], om);
+      }
+      atomicMin(reinterpret_cast<unsigned int*>(&L.bi[2]), lowest);
+    }
+    lds_barrier();
+    const uint32_t kmin = static_cast<uint32_t>(L.bi[2]);
+    constexpr int PER = kNB / NT;
+    int lc[PER];
+    double lm[PER];
+    int sc = 0;
+    double sm = 0.0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int b = threadIdx.x * PER + k;
+      lc[k] = c[b];
+      lm[k] = ms[b];
+      sc += lc[k];
+      sm += lm[k];
+    }
+    int tc;
+    double tm;
+    const int ic = block_scan_incl<NT, int>(sc, L.red_i, tc);
+    const double im = block_scan_incl<NT, double>(sm, L.red_d, tm);
+    int ec = ic - sc;
+    double em = im - sm;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int b = threadIdx.x * PER + k;
+      c[b] = ec;
+      ms[b] = em;
+      ec += lc[k];
+      em += lm[k];
+    }
+    if (threadIdx.x == 0) {
+      c[kNB] = tc;
+      ms[kNB] = tm;
+    }
+    lds_barrier();
+    return kmin;
+  }
+
+  __device__ __forceinline__ void build() {
+    if (built) return;
+    kmin0 = histogram(Level{kmax, 0u, false, kS0, 0, 0.0}, false);
+    wtot = L.u.post.mass[kNB];
+    built = true;
+  }
+
+  __device__ __forceinline__ double total_mass() {
+    build();
     return wtot;
   }
 
-  // The located value's key and the count / weight strictly above it.
-  __device__ void radix(bool by_weight, double target, int rank, bool strict, uint32_t& key, int& above_c,
-                        double& above_m, int& tie_c, double& tie_w) {
-    // by_weight: locate the first rank whose cumulative weight reaches
-    // target; otherwise locate rank `rank`. Weights are accumulated either way.
-    uint32_t prefix = 0;
-    above_c = 0;
-    above_m = 0.0;
-    for (int d = 0; d < 4; ++d) {
-      const int shift = 24 - 8 * d;
-      for (int b = threadIdx.x; b < 256; b += NT) {
-        L.u.radix.cnt[b] = 0;
-        L.u.radix.mass[b] = 0.0;
-      }
-      lds_barrier();
-      for (int e = threadIdx.x; e < V; e += NT) {
-        const float x = at(e);
-        const uint32_t k = ord_ukey(x);
-        if (d > 0 && (k >> (shift + 8)) != prefix) continue;
-        const int dig = (k >> shift) & 255;
-        atomicAdd(&L.u.radix.cnt[dig], 1);
-        atomicAdd(&L.u.radix.mass[dig], weight(x, m, T));
-      }
-      lds_barrier();
-      if (threadIdx.x == 0) {
-        int dsel = 0, c = above_c;
-        double w = above_m;
-        for (int dig = 255; dig >= 0; --dig) {
-          const int nc2 = c + L.u.radix.cnt[dig];
-          const double nw = w + L.u.radix.mass[dig];
-          const bool hit = by_weight ? (strict ? nw > target : nw >= target) : (rank < nc2);
-          if (hit && L.u.radix.cnt[dig] > 0) {
-            dsel = dig;
-            break;
-          }
-          c = nc2;
-          w = nw;
-          dsel = dig;
-        }
-        L.bi[0] = dsel;
-        L.bi[1] = c;
-        L.bd[0] = w;
-        L.bi[2] = L.u.radix.cnt[dsel];
-      }
-      lds_barrier();
-      prefix = (prefix << 8) | static_cast<uint32_t>(L.bi[0]);
-      above_c = L.bi[1];
-      above_m = L.bd[0];
-      tie_c = L.bi[2];
-      lds_barrier();
-    }
-    key = prefix;
-    const int kk = static_cast<int>(prefix ^ 0x80000000u);
-    tie_w = weight(key_float(kk), m, T);
+  // Does rank position r, with cumulative weight cw through it, reach the
+  // query?
+  __device__ __forceinline__ static bool reached(bool by_weight, double target, int rank, bool strict, int r,
+                                                 double cw) {
+    return by_weight ? (strict ? cw > target : cw >= target) : r >= rank;
   }
 
-  // Index of the (n+1)-th element (0-based n) whose key equals `key`,
-  // scanning the row in index order in chunks of 8 per thread.
-  __device__ int nth_tie(uint32_t key, int n) {
-    int need = n;
-    for (int base = 0; base < V; base += NT * 8) {
-      const int lo = base + static_cast<int>(threadIdx.x) * 8;
-      int c = 0;
-      for (int e = lo; e < lo + 8 && e < V; ++e) c += (ord_ukey(at(e)) == key) ? 1 : 0;
-      int tot;
-      const int incl = block_scan_incl<NT, int>(c, L.red_i, tot);
-      const int excl = incl - c;
-      if (threadIdx.x == 0) L.bi[3] = -1;
-      lds_barrier();
-      if (need >= excl && need < incl) {
-        int k = need - excl;
-        for (int e = lo; e < lo + 8 && e < V; ++e) {
-          if (ord_ukey(at(e)) == key) {
-            if (k == 0) {
-              L.bi[3] = e;
-              break;
-            }
-            --k;
-          }
-        }
-      }
-      lds_barrier();
-      const int found = L.bi[3];
-      lds_barrier();
-      if (found >= 0) return found;
-      need -= tot;
+  // First non-empty bin of the level whose inclusive prefix reaches the
+  // query; kNB if none.
+  __device__ __forceinline__ int first_bin(const Level& lv, bool fine, bool by_weight, double target, int rank,
+                                           bool strict) {
+    const int* c = cnt(fine);
+    const double* ms = mass(fine);
+    if (threadIdx.x == 0) L.bi[0] = kNB;
+    lds_barrier();
+    constexpr int PER = kNB / NT;
+    int mine = kNB;
+#pragma unroll
+    for (int k = PER - 1; k >= 0; --k) {
+      const int b = threadIdx.x * PER + k;
+      if (c[b + 1] > c[b] &&
+          reached(by_weight, target, rank, strict, lv.base_c + c[b + 1] - 1, lv.base_m + ms[b + 1]))
+        mine = b;
     }
-    return 0;
+    const uint64_t bal = __ballot(mine < kNB);
+    if (bal && lane_id() == __builtin_ctzll(bal)) atomicMin(&L.bi[0], mine);
+    lds_barrier();
+    const int b = L.bi[0];
+    lds_barrier();
+    return b;
   }
 
-  __device__ Pick by_count(int k) {
-    Pick p{0, k - 1, 0.0, false, 0, 0};
-    if (k < 1 || k > V) return p;
-    uint32_t key;
-    int ac, tc;
-    double am, tw;
-    radix(false, 0.0, k - 1, false, key, ac, am, tc, tw);
-    const int j = k - 1 - ac;
-    p.idx = nth_tie(key, j);
-    p.cum = am + static_cast<double>(j + 1) * tw;
-    p.ok = true;
+  // The bin's elements ranked in LDS (nb <= kGatherFull): the answer's position
+  // among them, with their exact weights.
+  __device__ __forceinline__ Pick gather_pick(const Level& bl, int nb, bool by_weight, double target, int rank,
+                                              bool strict) {
+    if (threadIdx.x == 0) L.gn = 0;
+    lds_barrier();
+    row_each<E, NT>(row, V, [&](float x, int e) {
+      if (!in_range(bl, ord_ukey(x))) return;
+      const int pos = atomicAdd(&L.gn, 1);
+      if (pos < kGatherFull) L.u.post.g[pos] = Cand{x, e};
+    });
+    lds_barrier();
+    const int cb = min(L.gn, kGatherFull);
+    lds_barrier();
+    for (int q = threadIdx.x; q < cb; q += NT) {
+      const Cand e = L.u.post.g[q];
+      int r = 0;
+      for (int o = 0; o < cb; ++o) {
+        const Cand d = L.u.post.g[o];
+        r += (d.x > e.x || (d.x == e.x && d.idx < e.idx)) ? 1 : 0;
+      }
+      L.u.post.gs[r] = e;
+    }
+    lds_barrier();
+    double wv = 0.0;
+    if (static_cast<int>(threadIdx.x) < cb) wv = weight(L.u.post.gs[threadIdx.x].x, m, T);
+    double tot;
+    const double incl = block_scan_incl<NT, double>(wv, L.red_d, tot);
+    // the first position that reaches the query (the last one if none does)
+    if (threadIdx.x == 0) L.bi[1] = cb - 1;
+    lds_barrier();
+    const int j = static_cast<int>(threadIdx.x);
+    if (j < cb && reached(by_weight, target, rank, strict, bl.base_c + j, bl.base_m + incl)) atomicMin(&L.bi[1], j);
+    if (j < cb) L.u.post.gpm[j] = incl;
+    lds_barrier();
+    const int jj = max(L.bi[1], 0);
+    Pick p{0, bl.base_c + jj, 0.0, cb > 0 && cb == nb, 0, 0};
+    if (cb > 0) {
+      p.idx = L.u.post.gs[jj].idx;
+      p.cum = bl.base_m + L.u.post.gpm[jj];
+    }
+    lds_barrier();
     return p;
   }
 
-  __device__ Pick by_mass(double target, bool strict) {
-    Pick p{0, 0, 0.0, false, 0, 0};
-    uint32_t key;
-    int ac, tc;
-    double am, tw;
-    radix(true, target, 0, strict, key, ac, am, tc, tw);
-    int j = 0;
-    if (tw > 0.0) {
-      const double q = (target - am) / tw;
-      j = strict ? static_cast<int>(floor(q)) : static_cast<int>(ceil(q)) - 1;
-      // settle rounding against the exact comparison
-      while (j > 0 && (strict ? am + j * tw > target : am + j * tw >= target)) --j;
-      while (j < tc - 1 && !(strict ? am + (j + 1) * tw > target : am + (j + 1) * tw >= target)) ++j;
+  // A bin whose nb elements all hold one value: the answer's position
+  // among the ties, then that tie in index order (each wave counts the
+  // ties of its contiguous share of the row; the share holding the answer
+  // is read again).
+  __device__ __forceinline__ Pick tie_pick(const Level& bl, int nb, bool by_weight, double target, int rank,
+                                           bool strict) {
+    const int w = wave_id(), lane = lane_id();
+    const int seg = (V + NW - 1) / NW;
+    const int e0 = min(V, w * seg), e1 = min(V, e0 + seg);
+    int mine = 0;
+    float val = 0.f;
+    bool have = false;
+    for (int base = e0; base < e1; base += kWave) {
+      const int e = base + lane;
+      const float x = e < e1 ? at(e) : 0.f;
+      const bool hit = e < e1 && in_range(bl, ord_ukey(x));
+      const uint64_t bal = __ballot(hit);
+      if (bal && !have) {
+        val = __shfl(x, __builtin_ctzll(bal));
+        have = true;
+      }
+      mine += __popcll(bal);
     }
-    j = j < 0 ? 0 : (j >= tc ? tc - 1 : j);
-    p.idx = nth_tie(key, j);
-    p.rank = ac + j;
-    p.cum = am + static_cast<double>(j + 1) * tw;
-    p.ok = true;
+    if (lane == 0) {
+      L.red_i[w] = mine;
+      if (have) L.bd[1] = static_cast<double>(val);   // any tie's value
+    }
+    lds_barrier();
+    const double tw = weight(static_cast<float>(L.bd[1]), m, T);
+    int j;
+    if (by_weight) {
+      j = 0;
+      if (tw > 0.0) {
+        const double q = (target - bl.base_m) / tw;
+        j = strict ? static_cast<int>(floor(q)) : static_cast<int>(ceil(q)) - 1;
+        j = j < 0 ? 0 : (j >= nb ? nb - 1 : j);
+        // settle rounding against the exact comparison
+        while (j > 0 && reached(true, target, 0, strict, 0, bl.base_m + j * tw)) --j;
+        while (j < nb - 1 && !reached(true, target, 0, strict, 0, bl.base_m + (j + 1) * tw)) ++j;
+      }
+    } else {
+      j = rank - bl.base_c;
+    }
+    j = j < 0 ? 0 : (j >= nb ? nb - 1 : j);
+    // the share holding tie j, and the tie's place in it
+    int before = 0, ws = -1;
+    for (int k = 0; k < NW; ++k) {
+      const int ck = L.red_i[k];
+      if (ws < 0 && j < before + ck) ws = k;
+      if (ws < 0) before += ck;
+    }
+    if (threadIdx.x == 0) L.bi[3] = 0;
+    lds_barrier();
+    if (w == ws) {
+      int need = j - before;
+      for (int base = e0; base < e1; base += kWave) {
+        const int e = base + lane;
+        const bool hit = e < e1 && in_range(bl, ord_ukey(at(e)));
+        const uint64_t bal = __ballot(hit);
+        const int n = __popcll(bal);
+        if (need < n) {
+          // the (need + 1)-th set bit of bal
+          uint64_t bb = bal;
+          for (int k = 0; k < need; ++k) bb &= bb - 1;
+          if (lane == 0) L.bi[3] = base + __builtin_ctzll(bb);
+          break;
+        }
+        need -= n;
+      }
+    }
+    lds_barrier();
+    Pick p{L.bi[3], bl.base_c + j, bl.base_m + static_cast<double>(j + 1) * tw, ws >= 0, 0, 0};
+    lds_barrier();
     return p;
   }
 
-  __device__ int token(const Pick& p) const { return p.idx; }
+  // The rank reached by the query: by weight, the first rank whose
+  // cumulative weight passes `target` (strictly if `strict`); else rank
+  // `rank`. A weight query beyond the row answers with the row's last rank.
+  __device__ __forceinline__ Pick locate(bool by_weight, double target, int rank, bool strict) {
+    build();
+    Level lv{kmax, 0u, false, kS0, 0, 0.0};
+    bool fine = false;
+    uint32_t kmin = kmin0;   // the level's lowest key
+    for (int depth = 0; depth < 12; ++depth) {
+      int b = first_bin(lv, fine, by_weight, target, rank, strict);
+      if (b >= kNB) {
+        if (!by_weight || depth > 0) break;
+        by_weight = false;   // past the total: the row's last rank
+        rank = V - 1;
+        b = first_bin(lv, fine, false, 0.0, rank, false);
+        if (b >= kNB) break;
+      }
+      const int* c = cnt(fine);
+      const double* ms = mass(fine);
+      const int nb = c[b + 1] - c[b];
+      Level bl;
+      bl.hi = lv.hi - (static_cast<uint32_t>(b) << lv.s);
+      if (b < kNB - 1) {
+        const int64_t lo = static_cast<int64_t>(lv.hi) - (static_cast<int64_t>(b + 1) << lv.s);
+        bl.has_lo = lo >= 0;
+        bl.lo = bl.has_lo ? static_cast<uint32_t>(lo) : 0u;
+      } else {
+        bl.lo = lv.lo;
+        bl.has_lo = lv.has_lo;
+      }
+      bl.base_c = lv.base_c + c[b];
+      bl.base_m = lv.base_m + ms[b];
+      // one value per bin: a key step (s = 0), or a bfloat16 row's level-0
+      // step (2^16 keys from a bfloat16 key hold one bfloat16 key)
+      const bool one_value = b < kNB - 1 && (lv.s == 0 || (sizeof(E) == 2 && lv.s == kS0));
+      lds_barrier();
+      if (nb <= kGatherFull) return gather_pick(bl, nb, by_weight, target, rank, strict);
+      if (one_value) return tie_pick(bl, nb, by_weight, target, rank, strict);
+      if (b < kNB - 1) {
+        bl.s = lv.s >= 10 ? lv.s - 10 : 0;
+      } else {
+        // the rest of the range, down to its lowest key: steps that cover
+        // it in kNB bins
+        bl.has_lo = kmin > 0u;
+        bl.lo = bl.has_lo ? kmin - 1u : 0u;
+        const uint32_t span = bl.hi - kmin;
+        int sw = 0;
+        while (sw < 31 && (span >> sw) >= static_cast<uint32_t>(kNB)) ++sw;
+        bl.s = sw;
+      }
+      lv = bl;
+      fine = true;
+      kmin = histogram(lv, true);
+    }
+    return Pick{0, 0, 0.0, false, 0, 0};
+  }
 
-  __device__ int count_minp(double lnmp, bool& exact) {
+  __device__ __forceinline__ Pick by_count(int k) {
+    if (k < 1 || k > V) return Pick{0, k - 1, 0.0, false, 0, 0};
+    return locate(false, 0.0, k - 1, false);
+  }
+
+  __device__ __forceinline__ Pick by_mass(double target, bool strict) { return locate(true, target, 0, strict); }
+
+  __device__ __forceinline__ int token(const Pick& p) const { return p.idx; }
+
+  __device__ __forceinline__ int count_minp(double lnmp, bool& exact) {
     int c = 0;
     for (int e = threadIdx.x; e < V; e += NT)
       c += ((static_cast<double>(at(e)) - static_cast<double>(m)) / T >= lnmp) ? 1 : 0;
@@ -646,7 +922,7 @@ struct FullLocator {
 // The filtered draw, given a locator. Returns false if the locator cannot
 // decide.
 template <class Loc>
-__device__ bool decide(Loc& loc, int V, int top_k, double top_p, double min_p, double u, int& token) {
+__device__ __forceinline__ bool decide(Loc& loc, int V, int top_k, double top_p, double min_p, double u, int& token) {
   const bool tk = top_k > 0 && top_k < V;
   const bool tp = top_p < 1.0;
   const bool mp = min_p > 0.0;
@@ -1204,6 +1480,21 @@ __device__ bool capture_row(const E* __restrict__ row, int V, float tau, const V
   return ok;
 }
 
+// The filtered draw decided over the whole row (FullLocator). Out of line,
+// so that its registers do not count against the common path, with the
+// locator inlined into it: every call level adds stack that the launch
+// must reserve for every wave (with about 380 bytes per lane the ragged
+// fp32 batch ran 1.3 us slower even with no row taking this path; with
+// about 220, 0.9 us).
+template <typename E, int NT>
+__device__ __noinline__ int full_decide(const E* __restrict__ row, int V, float m, double Td, int top_k, double top_p,
+                                        double min_p, double u, SampledLds<NT>& L) {
+  FullLocator<E, NT> fl(L, row, V, m, Td);
+  int t = 0;
+  decide(fl, V, top_k, top_p, min_p, u, t);
+  return t;
+}
+
 // Outcome of one sampled row.
 struct SampledOut {
   int token;
@@ -1281,10 +1572,7 @@ __device__ __forceinline__ SampledOut sampled_row(const VerifyArgs& a, const E* 
   }
   if (!done && !(out.bits & VSV_FLAG_LOGITS)) {
     lds_barrier();
-    FullLocator<E, NT> fl(L, row, a.V, m, Td);
-    int t = 0;
-    decide(fl, a.V, top_k, static_cast<double>(top_p), static_cast<double>(min_p), u, t);
-    token = t;
+    token = full_decide<E, NT>(row, a.V, m, Td, top_k, static_cast<double>(top_p), static_cast<double>(min_p), u, L);
     out.slow = 1;
   }
   lds_barrier();
