@@ -1010,8 +1010,11 @@ __device__ __forceinline__ int vmax_code(float v) {
 template <bool B> struct BoolC { static constexpr bool value = B; };
 
 // Pass 1: stream one sampled row for the statistics of stream_row, and leave
-// the code of every vector's maximum in L.u.vm. Loads use the caches' normal
-// policy so that pass 2's reads of a few vectors find them there.
+// the code of every vector's maximum in L.u.vm. bf16 rows load with the
+// caches' normal policy, so that pass 2's reads of a few vectors find them
+// there; fp32 rows stream past the caches like greedy rows (timed on the
+// large mixed bf16 batch, streaming loads made the launch 285 -> 306 us; on
+// the ragged fp32 batch they took it from 92.8 to 90.4 us).
 template <typename E, int NT, int U>
 __device__ __forceinline__ VmPlan stream_sampled(const E* __restrict__ row, int V, float c, RowPartial& p,
                                                  SampledLds<NT>& L) {
@@ -1029,7 +1032,8 @@ __device__ __forceinline__ VmPlan stream_sampled(const E* __restrict__ row, int 
   const __amdgpu_buffer_rsrc_t rsrc = vec_rsrc(row + head, nvec);
   const int lane_off = tid * 16;
   auto load = [&](int first) {   // vector first + tid
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_off, first * 16, kLoadNormal));
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_off, first * 16,
+                                                                           sizeof(E) == 4 ? kLoadStream : kLoadNormal));
   };
   // Rolling slots: slot u holds vector g*G + u*NT + tid of group g; it is
   // decoded, then reloaded at once with the same vector of group g+1, so
