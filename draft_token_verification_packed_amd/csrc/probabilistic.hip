@@ -349,12 +349,21 @@ __device__ bool draft_law_stream(const E* __restrict__ y, int V, double Td, Samp
   int head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(E));
   if (head > V) head = V;
   const int nvec = (V - head) / N;
-  const u32x4* __restrict__ vp = reinterpret_cast<const u32x4*>(y + head);
+  // Groups of U vectors per thread (vector g * G + u * NT + tid of group g),
+  // two groups in turn: one group's loads are in flight while the other is
+  // reduced. Loads go through a buffer resource over the body (vectors past
+  // it read as zero and are masked) with the streaming policy.
   constexpr int G = U * NT;
-  for (int base = threadIdx.x; base < nvec; base += G) {
-    u32x4 w[U];
+  const __amdgpu_buffer_rsrc_t rsrc = vec_rsrc(y + head, nvec);
+  const int lane_off = static_cast<int>(threadIdx.x) * 16;
+  const int ngroups = (nvec + G - 1) / G;
+  auto load_group = [&](u32x4* w, int g) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) w[u] = load_stream(vp + min(base + u * NT, nvec - 1));
+    for (int u = 0; u < U; ++u)
+      w[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_off, (g * G + u * NT) * 16,
+                                                                             kLoadStream));
+  };
+  auto reduce_group = [&](const u32x4* w, int base) {
     float f[U][N];
     float gmax = -INFINITY;
 #pragma unroll
@@ -376,6 +385,19 @@ __device__ bool draft_law_stream(const E* __restrict__ y, int V, double Td, Samp
 #pragma unroll
       for (int k = 0; k < N; ++k) e[u * N + k] = term(f[u][k]);
     sum += static_cast<double>(tree_sum<U * N>(e));
+  };
+  u32x4 A[U], B[U];
+  if (ngroups > 0) load_group(A, 0);
+  if (ngroups > 1) load_group(B, 1);
+  for (int g = 0; g < ngroups; g += 2) {
+    const int ba = g * G + static_cast<int>(threadIdx.x);
+    if (ba < nvec) reduce_group(A, ba);
+    if (g + 2 < ngroups) load_group(A, g + 2);
+    if (g + 1 < ngroups) {
+      const int bb = ba + G;
+      if (bb < nvec) reduce_group(B, bb);
+      if (g + 3 < ngroups) load_group(B, g + 3);
+    }
   }
   const int body_end = head + nvec * N;
   auto scalar = [&](float v) {
