@@ -50,6 +50,10 @@ template <> struct SampledDepth<float> {
 template <> struct SampledDepth<uint16_t> {
   static constexpr int kPass1 = 3, kGreedy = 2;
 };
+// Wave priorities inside the queue kernels: row streams run at kStreamPrio,
+// a sampled row's selection and draw at kSelectPrio.
+constexpr int kStreamPrio = 1;
+constexpr int kSelectPrio = 0;
 // Sampled launches hand out the sampled requests' rows first where a batch
 // has more rows than CUs but at most two per workgroup; each workgroup keeps
 // the rows of the tickets past the grid in LDS (16-bit row numbers), at

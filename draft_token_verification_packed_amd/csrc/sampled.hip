@@ -17,6 +17,15 @@ template <typename E, int NT, int U, typename Hook>
 __device__ __forceinline__ void sampled_kernel_row(const VerifyArgs& a, uint32_t tag, int r, SampledLds<NT>& L,
                                                    Hook after_stream) {
   const E* __restrict__ row = static_cast<const E*>(a.logits) + static_cast<int64_t>(r) * a.ld;
+  // Streams run at a higher wave priority than a sampled row's selection
+  // and draw, which lower it once the row is read when the batch has more
+  // rows than workgroups: a CU's issue slots go first to the waves that keep
+  // loads in flight, and the selection fills the rest. On the ragged fp32
+  // batch this took the launch from 90.4 to 85.4 us (its late greedy rows
+  // stream beside selecting workgroups), on the large mixed bf16 batch from
+  // 284.3 to 282.5. With one row per workgroup every selection is on the
+  // launch's critical path, and lowering it cost 1.5 us (mixed, 512 rows).
+  __builtin_amdgcn_s_setprio(kStreamPrio);
   const int own = a.owner[r];
   // The request's parameters go out with the row's metadata: all of them
   // for fp32 rows, the temperature alone for bf16 rows, whose filter

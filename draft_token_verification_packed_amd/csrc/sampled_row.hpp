@@ -1530,6 +1530,8 @@ __device__ __forceinline__ SampledOut sampled_row(const VerifyArgs& a, const E* 
   partial_init(p);
   const VmPlan plan = stream_sampled<E, NT, U>(row, a.V, c, p, L);
   after_stream(true);   // selection and draw follow
+  // with more rows than workgroups, other rows' streams go first (sampled.hip)
+  if (a.R > static_cast<int>(gridDim.x)) __builtin_amdgcn_s_setprio(kSelectPrio);
   const NoKeep nokeep;
   const RowStats res = finish_row_lean<E, NT, U, false>(p, L.ls, nokeep, row, a.V);
   // the sum holds the maximum's own term (at least 1/2), so float log2
