@@ -13,6 +13,9 @@ namespace vsv {
 // rows of greedy requests take the arg-max exactly as verify_greedy does.
 // Acceptance is strict: the draft must equal the row's token. Rows come
 // from the persistent row queue (row_queue.hpp).
+// A compile-time int as a value (template arguments of generic lambdas).
+template <int V_> struct IntC { static constexpr int value = V_; };
+
 template <typename E, int NT, int U, typename Hook>
 __device__ __forceinline__ void sampled_kernel_row(const VerifyArgs& a, uint32_t tag, int r, SampledLds<NT>& L,
                                                    Hook after_stream) {
@@ -52,13 +55,25 @@ __device__ __forceinline__ void sampled_kernel_row(const VerifyArgs& a, uint32_t
     bits = o.bits;
     slow = o.slow;
   } else {
-    RowPartial p;
-    partial_init(p);
-    QueueKeep<E, U> keep{};
-    constexpr float kLog2e = 1.4426950408889634f;
-    stream_row<E, NT, U, false, QueueKeep<E, U>, NoHook, true>(row, a.V, kLog2e, INFINITY, 0, p, keep);
-    after_stream(false);
-    const RowStats res = finish_row_lean<E, NT, U, false>(p, L.ls, keep, row, a.V);
+    auto greedy = [&](auto uc) {
+      constexpr int UG = decltype(uc)::value;
+      RowPartial p;
+      partial_init(p);
+      QueueKeep<E, UG> keep{};
+      constexpr float kLog2e = 1.4426950408889634f;
+      stream_row<E, NT, UG, false, QueueKeep<E, UG>, NoHook, true>(row, a.V, kLog2e, INFINITY, 0, p, keep);
+      after_stream(false);
+      return finish_row_lean<E, NT, UG, false>(p, L.ls, keep, row, a.V);
+    };
+    // fp32 greedy rows stream in groups of U when the batch has more rows
+    // than workgroups (the rows that start late then stream beside selecting
+    // workgroups and need their loads in flight), in groups of two when every
+    // row starts at once (the sampled rows' streams, which end the launch,
+    // then keep a larger share of the memory system: ragged fp32 batches of
+    // 64 and 100 requests went from 64.3 to 58.6 us and from 78.4 to 76.1)
+    RowStats res;
+    if (sizeof(E) == 4 && U != 2 && a.R <= static_cast<int>(gridDim.x)) res = greedy(IntC<2>{});
+    else res = greedy(IntC<U>{});
     token = res.argmax;
     // float log2 of a sum holding the maximum's own term (at least 1/2)
     lse = 0.69314718f * (res.mref + __log2f(static_cast<float>(res.sum)));
