@@ -324,6 +324,9 @@ struct CandLocator {
 
   __device__ double total_mass() const { return wtotal; }
 
+  // More than the weight of any element below the candidates (all < tau).
+  __device__ double beyond_weight() const { return weight(tau, m, T); }
+
   // First bin b whose inclusive prefix satisfies pred; kNB if none.
   template <typename Pred>
   __device__ int first_bin(Pred pred) {
@@ -691,6 +694,9 @@ struct FullLocator {
     return wtot;
   }
 
+  // The whole row is held: nothing lies beyond it.
+  __device__ __forceinline__ double beyond_weight() const { return 0.0; }
+
   // Does rank position r, with cumulative weight cw through it, reach the
   // query?
   __device__ __forceinline__ static bool reached(bool by_weight, double target, int rank, bool strict, int r,
@@ -941,7 +947,21 @@ __device__ __forceinline__ bool decide(Loc& loc, int V, int top_k, double top_p,
   double Ws = W1;
   if (tp) {
     const Pick p = loc.by_mass(top_p * W1, false);
-    if (!p.ok) return false;
+    if (!p.ok) {
+      // The cut lies beyond what the locator holds (a candidate locator's
+      // prefix of the rank order): every element it holds survives, and
+      // the survivors weigh top_p * W1 plus less than the weight of one
+      // element below it. A draw that reaches the same held element for
+      // every such weight is decided; any other is left to the caller.
+      if (tk || mp) return false;
+      const double lo = top_p * W1, hi = lo + loc.beyond_weight();
+      const Pick a = loc.by_mass(u * lo, true);
+      if (!a.ok) return false;
+      const Pick b = loc.by_mass(u * hi, true);
+      if (!b.ok || b.rank != a.rank) return false;
+      token = loc.token(a);
+      return true;
+    }
     Ls = p.rank + 1;
     Ws = p.cum;
   }
