@@ -179,3 +179,19 @@ def test_layout_errors_are_flagged(vsv, B):
     # the next well-formed call on the same workspace is unaffected
     good = run_sampled(vsv, with_margins(wl))
     assert_same(good, oracle_of(wl))
+
+
+@pytest.mark.parametrize("dtype", [oracle.F32, oracle.BF16])
+def test_top_p_cut_beyond_the_candidates(vsv, dtype):
+    """Top-p alone over flat rows: the cut lies below the captured
+    candidates in every row. Draws that land among the candidates for every
+    survivor weight the cut allows are decided there; the rest take the
+    whole-row path. Both happen here, and every row matches the oracle."""
+    rng = np.random.default_rng(8080 + dtype)
+    b = custom_sampled(rng, 24, 1, 152064, dtype, lambda i: (1.0, 0, 0.95, 0.0), seed=21, offset=2, sigma=3.0)
+    R = int(b["offsets"][-1])
+    out = run_custom(vsv, b)
+    assert_same(out, oracle_custom(b))
+    slow = int(host(out["slow_rows"])[0])
+    print("top-p beyond the candidates: R=%d, whole-row path %d" % (R, slow), flush=True)
+    assert 0 < slow < R
