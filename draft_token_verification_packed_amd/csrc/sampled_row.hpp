@@ -210,6 +210,49 @@ __device__ __forceinline__ T block_scan_incl(T v, T* scr, T& total) {
   return before + v;
 }
 
+// Block-wide inclusive scans of an int and one or two doubles at once: the
+// same wave scans and the same sums over the waves as block_scan_incl, so
+// the same results, behind one pair of barriers instead of one per value.
+// si holds NT / kWave ints, sd twice that many doubles.
+template <int NT, bool kTwo>
+__device__ __forceinline__ void block_scan_incl_n(int& a, double& b, double& c, int* si, double* sd, int& ta, double& tb,
+                                                  double& tc) {
+  constexpr int NW = NT / kWave;
+  const int lane = lane_id(), w = wave_id();
+  a = wave_scan_incl(a);
+  b = wave_scan_incl(b);
+  if (kTwo) c = wave_scan_incl(c);
+  lds_barrier();
+  if (lane == kWave - 1) {
+    si[w] = a;
+    sd[w] = b;
+    if (kTwo) sd[NW + w] = c;
+  }
+  lds_barrier();
+  int ba = 0, sa = 0;
+  double bb = 0, sb = 0, bc = 0, sc = 0;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) {
+    const int xa = si[k];
+    const double xb = sd[k];
+    ba += (k < w) ? xa : 0;
+    sa += xa;
+    bb += (k < w) ? xb : 0.0;
+    sb += xb;
+    if (kTwo) {
+      const double xc = sd[NW + k];
+      bc += (k < w) ? xc : 0.0;
+      sc += xc;
+    }
+  }
+  ta = sa;
+  tb = sb;
+  tc = sc;
+  a = ba + a;
+  b = bb + b;
+  if (kTwo) c = bc + c;
+}
+
 // Order-preserving 16-bit code of a bfloat16 value (-0 mapped to +0), and back.
 __device__ __forceinline__ int bf16_code(float x) {
   const uint32_t h = __float_as_uint(x == 0.0f ? 0.0f : x) >> 16;
@@ -307,11 +350,9 @@ struct CandLocator {
       sc += lc[k];
       sm += lm[k];
     }
-    int tc;
-    double tm, tcorr;
-    const int ic = block_scan_incl<NT, int>(sc, L.red_i, tc);
-    const double im = block_scan_incl<NT, double>(sm, L.red_d, tm);
-    block_scan_incl<NT, double>(corr, L.red_d + NW, tcorr);
+    int tc, ic = sc;
+    double tm, tcorr, im = sm;
+    block_scan_incl_n<NT, true>(ic, im, corr, L.red_i, L.red_d, tc, tm, tcorr);
     wtotal += tcorr;
     int ec = ic - sc;
     double em = im - sm;
@@ -670,10 +711,9 @@ struct FullLocator {
       sc += lc[k];
       sm += lm[k];
     }
-    int tc;
-    double tm;
-    const int ic = block_scan_incl<NT, int>(sc, L.red_i, tc);
-    const double im = block_scan_incl<NT, double>(sm, L.red_d, tm);
+    int tc, ic = sc;
+    double tm, unused = 0.0, im = sm;
+    block_scan_incl_n<NT, false>(ic, im, unused, L.red_i, L.red_d, tc, tm, unused);
     int ec = ic - sc;
     double em = im - sm;
 #pragma unroll
@@ -1403,10 +1443,9 @@ __device__ float mass_code_threshold(SampledLds<NT>& L, const VmPlan& plan, floa
     sw += wb[q];
   }
   if (tid == 0) L.bi[0] = kTopBins;
-  int tc;
-  double tw;
-  const int ic = block_scan_incl<NT, int>(sc, L.red_i, tc);
-  const double iw = block_scan_incl<NT, double>(sw, L.red_d, tw);
+  int tc, ic = sc;
+  double tw, unused = 0.0, iw = sw;
+  block_scan_incl_n<NT, false>(ic, iw, unused, L.red_i, L.red_d, tc, tw, unused);
   int rc = ic - sc;
   double rw = iw - sw;
   int found = kTopBins;
