@@ -37,18 +37,20 @@ constexpr int kUnrollRows = VSV_UNROLL_ROWS;
 // keeps kPass1 rolling 16-byte vectors per lane (kPass1 - 1 loads in flight);
 // greedy rows stream in groups of kGreedy vectors, two groups in turn. Each
 // workgroup takes rows one after another, so a launch is paced by its rows'
-// latencies. fp32 rows (608 KB each) gain from deeper loads: on the ragged
-// fp32 batch (B=128, 586 rows) eight pass-1 slots cut the launch from 118 to
-// 112 us, and greedy groups of four shorten the greedy rows that the queue
-// hands out last. bf16 gained nothing from deeper loads on the large mixed
-// batch (B=512, 4096 rows), whose sampled rows are paced by their selection
-// work, and deeper greedy groups there spill registers.
+// latencies and by how long its workgroups spend selecting instead of
+// streaming. Swept over pass-1 depths 2 to 8 and greedy groups 2 to 5 (fp32
+// and bf16 separately) on the ragged fp32 batch (B=128, 586 rows), the
+// large mixed bf16 batch (B=512, 4096 rows) and 64-request versions of both:
+// fp32 5 / 3 took the ragged batch from 83.8 to 79.4 us (8 / 4 before; 6 / 5
+// and 5 / 2 made it 98 and 89 us); bf16 3 / 3 took the mixed batch from
+// 262.4 to 260.4 us (4 / 3 reached 258.3 there but cost the 64-request
+// mixed batch 2-4 us; 2 / 3 made it 266 us).
 template <typename E> struct SampledDepth;
 template <> struct SampledDepth<float> {
-  static constexpr int kPass1 = 8, kGreedy = 4;
+  static constexpr int kPass1 = 5, kGreedy = 3;
 };
 template <> struct SampledDepth<uint16_t> {
-  static constexpr int kPass1 = 3, kGreedy = 2;
+  static constexpr int kPass1 = 3, kGreedy = 3;
 };
 // Wave priorities inside the queue kernels: row streams run at kStreamPrio,
 // a sampled row's selection and draw at kSelectPrio.
