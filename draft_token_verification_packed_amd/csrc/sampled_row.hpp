@@ -1286,9 +1286,10 @@ __device__ int kth_block_code(SampledLds<NT>& L, const VmPlan& plan, int k, int 
   }
   // Every thread past the k-th code lowers the result itself. One atomic per
   // wave (wave_first_min) finishes top-k rows' selection sooner, but on the
-  // ragged fp32 batch (586 rows for 512 workgroups) the late greedy rows
-  // then stream beside that faster selection 3 us slower each and the
-  // launch took 86.3 instead of 83.9 us; the small batches gain 2 us.
+  // ragged fp32 batch (586 rows for 512 workgroups) the greedy rows handed
+  // out last then stream beside that faster selection several us slower and
+  // end the launch: 87.2 instead of 79.4 us per launch back to back (a
+  // 64-request batch gains 1.7 us).
   if (found < kTopBins) atomicMin(&L.bi[0], found);
   lds_barrier();
   const int b = L.bi[0];
