@@ -252,6 +252,11 @@ __device__ __forceinline__ void block_scan_incl_n(int& a, double& b, double& c, 
   b = bb + b;
   if (kTwo) c = bc + c;
 }
+template <int NT>
+__device__ __forceinline__ void block_scan_incl2(int& a, double& b, int* si, double* sd, int& ta, double& tb) {
+  double c = 0.0, tc = 0.0;
+  block_scan_incl_n<NT, false>(a, b, c, si, sd, ta, tb, tc);
+}
 
 // Order-preserving 16-bit code of a bfloat16 value (-0 mapped to +0), and back.
 __device__ __forceinline__ int bf16_code(float x) {
@@ -712,8 +717,8 @@ struct FullLocator {
       sm += lm[k];
     }
     int tc, ic = sc;
-    double tm, unused = 0.0, im = sm;
-    block_scan_incl_n<NT, false>(ic, im, unused, L.red_i, L.red_d, tc, tm, unused);
+    double tm, im = sm;
+    block_scan_incl2<NT>(ic, im, L.red_i, L.red_d, tc, tm);
     int ec = ic - sc;
     double em = im - sm;
 #pragma unroll
@@ -1445,8 +1450,8 @@ __device__ float mass_code_threshold(SampledLds<NT>& L, const VmPlan& plan, floa
   }
   if (tid == 0) L.bi[0] = kTopBins;
   int tc, ic = sc;
-  double tw, unused = 0.0, iw = sw;
-  block_scan_incl_n<NT, false>(ic, iw, unused, L.red_i, L.red_d, tc, tw, unused);
+  double tw, iw = sw;
+  block_scan_incl2<NT>(ic, iw, L.red_i, L.red_d, tc, tw);
   int rc = ic - sc;
   double rw = iw - sw;
   int found = kTopBins;
