@@ -380,8 +380,16 @@ struct CandLocator {
 
   __device__ double total_mass() const { return wtotal; }
 
-  // More than the weight of any element below the candidates (all < tau).
-  __device__ double beyond_weight() const { return weight(tau, m, T); }
+  // At least the weight of any element the bins do not hold: those below
+  // tau and, for bfloat16 rows (bins by code, kNB codes down from the
+  // maximum's), the candidates at kNB or more codes below the maximum's,
+  // which are no larger than the value of code mcode - kNB. A window that
+  // reaches zero or below spans far more than kNB codes.
+  __device__ double beyond_weight() const {
+    float v = tau;
+    if (kCode && mcode >= kNB) v = fmaxf(v, bf16_of_code(mcode - kNB));
+    return weight(v, m, T);
+  }
 
   // First bin b whose inclusive prefix satisfies pred; kNB if none.
   template <typename Pred>

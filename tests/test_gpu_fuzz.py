@@ -102,3 +102,28 @@ def test_sampled_run_twice_bit_identical(vsv, B, K):
         torch.cuda.synchronize()
     for k in ("accepted_len", "next_token", "out_offsets", "out_tokens", "row_token", "row_lse"):
         assert np.array_equal(host(outs[0][k]), host(outs[1][k])), k
+
+
+# Seeds of a wider random campaign (built as below) whose bfloat16 rows
+# filtered by top-p alone drew the wrong token: their candidates reached
+# far below the locator's bins (a window down to zero or below spans many
+# more codes than the bins hold), and the bound on the weight of the first
+# element outside the bins counted only the elements below tau.
+@pytest.mark.parametrize("seed", [20036, 20079, 20556, 21444, 22093, 22251, 22665])
+def test_fuzz_sampled_top_p_past_the_bins(vsv, seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 40))
+    Kmax = int(rng.integers(0, 6))
+    V = int(rng.choice(VOCABS[:5]))
+    dtype = int(rng.integers(0, 2))
+    shift = int(rng.integers(0, 2))
+    b = custom_sampled(rng, B, Kmax, V, dtype, _random_params(rng, V), seed=seed, offset=seed % 7, ld=V + 2,
+                       shift=shift, ties=bool(rng.random() < 0.3))
+    print("campaign seed=%d B=%d Kmax=%d V=%d dtype=%d shift=%d R=%d" %
+          (seed, B, Kmax, V, dtype, shift, int(b["offsets"][-1])), flush=True)
+    t = to_dev(b["store"])[:, b["shift"]:]
+    out = vsv.verify_sampled(t, to_dev(b["offsets"]), to_dev(b["owner"]), to_dev(b["drafts"]), to_dev(b["T"]),
+                             to_dev(b["TK"]), to_dev(b["TP"]), to_dev(b["MP"]), b["seed"], b["offset"], vocab=V)
+    import torch
+    torch.cuda.synchronize()
+    assert_same(out, oracle_custom(b))
