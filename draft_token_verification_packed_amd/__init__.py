@@ -167,7 +167,9 @@ def _vec(t, n, dtype, name):
 
 
 def _logits(t, vocab):
-    if not t.is_cuda or t.dim() != 2 or t.stride(1) != 1:
+    # the column stride only matters when a row holds more than one element
+    # (torch gives tensors without elements, or of one column, any strides)
+    if not t.is_cuda or t.dim() != 2 or (t.stride(1) != 1 and t.shape[1] > 1 and t.numel() > 0):
         raise ValueError("logits must be a 2-D CUDA tensor with unit column stride")
     v = t.shape[1] if vocab is None else int(vocab)
     if v > t.shape[1]:

@@ -139,6 +139,24 @@ def test_large_mixed_draft_confidence(vsv):
     np.testing.assert_allclose(host(conf), rc, rtol=1e-5, atol=0)
 
 
+def test_draft_confidence_without_rows_and_with_one_column(vsv):
+    """Draft logits with no rows (from numpy such a tensor has zero strides)
+    give empty outputs and no flag; a one-token vocabulary gives confidence
+    1 and the logit itself as the log-sum-exp."""
+    import torch
+    empty = to_dev(np.zeros((0, 5), dtype=np.float32))
+    conf, lse, flag = vsv.draft_confidence(empty)
+    torch.cuda.synchronize()
+    assert conf.numel() == 0 and lse.numel() == 0 and int(host(flag)[0]) == 0
+    x = np.array([[1.5], [-2.0], [0.25]], dtype=np.float32)
+    conf, lse, flag = vsv.draft_confidence(to_dev(x))
+    torch.cuda.synchronize()
+    rc, rl = oracle.draft_confidence(x, oracle.F32, 1)
+    np.testing.assert_allclose(host(conf), rc, rtol=1e-6, atol=0)
+    assert_lse_close(host(lse), rl)
+    assert int(host(flag)[0]) == 0
+
+
 @pytest.mark.parametrize("B,Kmax", [(300, 2), (600, 1)])
 def test_many_requests_in_longest_first_order(vsv, B, Kmax):
     """A batch with more rows than CUs and at most two rows per workgroup
