@@ -1536,7 +1536,12 @@ template <typename E, int NT>
 __device__ bool capture_row(const E* __restrict__ row, int V, float tau, const VmPlan& plan, SampledLds<NT>& L) {
   constexpr int N = Elem<E>::kVec;
   constexpr int NW = NT / kWave;
-  constexpr int kB = 8;        // entries per lane per batch
+  // entries per lane per batch: a bf16 row's picks (about 125 per wave on
+  // the large mixed batch) fill two slots per lane, and empty slots still
+  // cost their decode (2 took that batch from 260.4 to 257.7 us); fp32
+  // entries cover two vectors each and keep 8 (2 made the ragged fp32
+  // batch 4.5 us slower)
+  constexpr int kB = sizeof(E) == 2 ? 2 : 8;
   const int w = wave_id(), lane = lane_id();
   const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
   int head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(E));
